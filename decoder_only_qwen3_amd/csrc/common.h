@@ -1,0 +1,131 @@
+// Device-side helpers shared by the gfx950 kernels of libq3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 held as its bit pattern in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define Q3_HEAD_DIM 128
+#define Q3_MAX_BATCH 64
+
+#define Q3_DEV static __device__ __forceinline__
+
+Q3_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest, ties to even (NaN kept quiet).
+Q3_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+Q3_DEV uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Storage conversion helpers for the two activation/KV element types.
+template <typename T> Q3_DEV float ld_f(const T* p);
+template <> Q3_DEV float ld_f<float>(const float* p) { return *p; }
+template <> Q3_DEV float ld_f<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <typename T> Q3_DEV void st_f(T* p, float v);
+template <> Q3_DEV void st_f<float>(float* p, float v) { *p = v; }
+template <> Q3_DEV void st_f<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
+
+// Sum across the 64 lanes of a wavefront; every lane gets the total.
+Q3_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+Q3_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+Q3_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+Q3_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+Q3_DEV f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+Q3_DEV f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> packed fp16, round to nearest even.
+Q3_DEV uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 h = __builtin_convertvector((f32x2){lo, hi}, f16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Eight bf16 values -> eight fp16 values.  Every bf16 value inside fp16's
+// normal range is exact in fp16; conversion rounds toward zero, so a magnitude
+// beyond fp16's range saturates at 65504 instead of becoming infinite.
+Q3_DEV u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xffff0000u);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+Q3_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Sequences of one call.  Prefill: token t of the call belongs to sequence b
+// with cu[b] <= t < cu[b+1] and sits at position t - cu[b].  Decode: token b
+// is the single new token of sequence b, at position = that slot's length.
+struct SeqBatch {
+  int32_t n;
+  int32_t decode;
+  int32_t slot[Q3_MAX_BATCH];
+  int32_t cu[Q3_MAX_BATCH + 1];
+};
+
+// Per-slot KV placement and length, resident on the device.
+struct SeqState {
+  int64_t base;   // element offset of the slot's region in the KV arena
+  int32_t cap;    // token capacity (multiple of 64)
+  int32_t len;    // tokens currently cached
+};
+
+// KV arena addressing.  A slot's region holds, for each layer, the keys as
+// [kv_head][cap][128] followed by the values transposed as [kv_head][128][cap].
+struct KvGeom {
+  int32_t n_kv;
+  int32_t layer;
+};
+template <typename T>
+Q3_DEV T* kv_k(T* arena, const SeqState& s, KvGeom g, int head) {
+  return arena + s.base + ((int64_t)(g.layer * 2) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;
+}
+template <typename T>
+Q3_DEV T* kv_vt(T* arena, const SeqState& s, KvGeom g, int head) {
+  return arena + s.base + ((int64_t)(g.layer * 2 + 1) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;
+}
+
+Q3_DEV int seq_of_token(const SeqBatch& sb, int t) {
+  if (sb.decode) return t;
+  int lo = 0, hi = sb.n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (sb.cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Error bits raised by kernels (read back by q3_error_flags).
+#define Q3_ERRBIT_TOKEN 1u
+#define Q3_ERRBIT_NONFINITE 2u

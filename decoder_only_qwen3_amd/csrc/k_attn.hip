@@ -1,0 +1,488 @@
+// Causal grouped-query attention over the KV cache.
+//
+// Method source: "Dentro de un LLM: Inferencia en Python puro para Qwen3-0.6B
+// en MLX" -- Paso 5: scores q.k / sqrt(128); a query sees only keys at or
+// before its own position (the page masks the upper triangle; excluding those
+// keys is the same softmax); softmax over the visible keys weights the values;
+// query head h reads key/value head h / (n_q / n_kv).
+//
+// Cache layout (per slot and layer): keys [kv_head][cap][128] row-major,
+// values transposed [kv_head][128][cap].  With that layout both MFMA products
+// read 16-byte runs:
+//   S^T[key][row] = K[key][:] . Q[row][:]   A = K rows,    B = Q rows
+//   O^T[dim][row] = V^T[dim][keys] . P^T     A = V^T rows,  B = P from registers
+// The key order inside each 32-key chunk is permuted for the S^T product so
+// that lane group q (= lane/16) ends up holding the scores of keys 8q..8q+7,
+// which is exactly the eight-key run it must supply as the B operand of the
+// P.V product.  No shuffles or LDS round trips are needed for P.
+//
+// Precision: S = Q.K^T takes the bf16 queries and keys as they are.  The P.V
+// product runs on fp16 operands: the softmax weights are rounded to fp16
+// (relative error 2^-11, eight times finer than bf16) and the bf16 values are
+// converted to fp16 exactly.  The softmax denominator sums the rounded
+// weights, so the output is a properly normalised average of the values.
+#include "kernels.h"
+
+namespace q3k {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+Q3_DEV float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round eight softmax weights to fp16 in place (so the caller can sum the
+// rounded values) and pack them as an MFMA operand.
+Q3_DEV f16x8 pack_p(f32x4& a, f32x4& b) {
+  u32x4 u;
+  u[0] = pack_f16x2(a[0], a[1]);
+  u[1] = pack_f16x2(a[2], a[3]);
+  u[2] = pack_f16x2(b[0], b[1]);
+  u[3] = pack_f16x2(b[2], b[3]);
+  const f16x8 h = as_f16x8(u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (float)h[i];
+    b[i] = (float)h[4 + i];
+  }
+  return h;
+}
+
+// Zero the bf16 elements of an 8-key run whose key index is >= limit.
+Q3_DEV u32x4 mask_keys(u32x4 v, int key0, int limit) {
+  if (key0 + 8 <= limit) return v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t x = v[w];
+    if (key0 + 2 * w >= limit) x &= 0xffff0000u;
+    if (key0 + 2 * w + 1 >= limit) x &= 0x0000ffffu;
+    v[w] = x;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- prefill
+constexpr int KT = 64;          // keys per tile
+constexpr int LDSK = 128 + 8;   // key tile row stride (elements)
+constexpr int LDSV = KT + 8;    // value^T tile row stride
+
+struct TileTable {
+  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
+};
+
+// Block: one kv head and one query tile of `qt` tokens of one sequence; its
+// 128 query rows are the group's query heads x qt tokens (row r -> head
+// r / qt, token r % qt).  4 wavefronts x 32 rows.  K and V^T tiles of 64 keys
+// are double-buffered in LDS and shared by the 4 wavefronts.
+__global__ __launch_bounds__(256) void flash_prefill_kernel(
+    const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
+    const bf16_t* __restrict__ kv, int layer, int n_q, int n_kv, int qt, bf16_t* __restrict__ o,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * LDSK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * LDSV];  // fp16 bits
+
+  const int total = tt.tile_cu[sb.n];
+  const int tile = total - 1 - (int)blockIdx.x;  // late (long) tiles first
+  const int g = blockIdx.y;
+  int b = 0;
+  {
+    int lo = 0, hi = sb.n - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (tt.tile_cu[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int L = sb.cu[b + 1] - sb.cu[b];
+  const int q0 = (tile - tt.tile_cu[b]) * qt;
+  const SeqState s = st[sb.slot[b]];
+  const KvGeom geo{n_kv, layer};
+  const bf16_t* Kc = kv_k(kv, s, geo, g);
+  const bf16_t* Vt = kv_vt(kv, s, geo, g);
+  const int group = n_q / n_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int fr = lane & 15, fq = lane >> 4;
+
+  // Query fragments (B operand of S^T) for this wavefront's two 16-row blocks.
+  bf16x8 qf[2][4];
+  int qpos[2], qhead[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = wid * 32 + cb * 16 + fr;
+    const int hh = r / qt, tq = r - hh * qt;
+    qpos[cb] = q0 + tq;
+    qhead[cb] = g * group + hh;
+    const bool ok = qpos[cb] < L;
+    const bf16_t* qp = q + ((int64_t)(sb.cu[b] + (ok ? qpos[cb] : 0)) * n_q + qhead[cb]) * 128 + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = ld16(qp + ks * 32);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qf[cb][ks] = as_bf16x8(v);
+    }
+  }
+
+  const int kend = min(L, q0 + qt);
+  const int ntiles = (kend + KT - 1) / KT;
+
+  // Staging assignment: K tile 64 keys x 16 chunks; V^T tile 128 dims x 8 chunks.
+  u32x4 rk[4], rv[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kt * KT + (tid >> 4) + 16 * i;
+      rk[i] = ld16(Kc + (int64_t)key * 128 + (tid & 15) * 8);
+      const int dim = (tid >> 3) + 32 * i;
+      const int key0 = kt * KT + (tid & 7) * 8;
+      rv[i] = mask_keys(ld16(Vt + (int64_t)dim * s.cap + key0), key0, L);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sK[buf][((tid >> 4) + 16 * i) * LDSK + (tid & 15) * 8]) = rk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][((tid >> 3) + 32 * i) * LDSV + (tid & 7) * 8]) = bf16x8_to_f16x8(rv[i]);
+    }
+  };
+
+  f32x4 oacc[8][2];
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) oacc[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+
+    // S^T for the tile: sacc[c][sb][cb], keys kt*64 + c*32 + 8*fq + 4*sb + r.
+    f32x4 sacc[2][2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int krow = c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][krow * LDSK + ks * 32 + fq * 8]);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) sacc[c][sbk][cb] = mfma16(kf, qf[cb][ks], sacc[c][sbk][cb]);
+        }
+      }
+
+    const bool diag = kt * KT + KT - 1 > q0 || kt * KT + KT > L;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = sacc[c][sbk][cb][r] * scale_log2;
+            if (diag) {
+              const int key = kt * KT + c * 32 + 8 * fq + 4 * sbk + r;
+              if (key > qpos[cb] || key >= L) v = -INFINITY;
+            }
+            sacc[c][sbk][cb][r] = v;
+            mx = fmaxf(mx, v);
+          }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrun[cb], mx);
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2_f(mrun[cb] - mref);
+      mrun[cb] = mnew;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[c][sbk][cb][r] = exp2_f(sacc[c][sbk][cb][r] - mref);
+      lrun[cb] *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) oacc[d][cb] *= alpha;
+    }
+
+    // O^T += V^T . P^T  (fp16 operands)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f16x8 pf[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        pf[cb] = pack_p(sacc[c][0][cb], sacc[c][1][cb]);
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ls += sacc[c][0][cb][r] + sacc[c][1][cb][r];
+        lrun[cb] += ls;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const f16x8 vf = *reinterpret_cast<const f16x8*>(&sV[buf][(d * 16 + fr) * LDSV + c * 32 + fq * 8]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) oacc[d][cb] = mfma16_f16(vf, pf[cb], oacc[d][cb]);
+      }
+    }
+
+    if (kt + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Normalise and store: lane holds dims d*16 + fq*4 + r of row (cb, fr).
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    float l = lrun[cb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (qpos[cb] >= L) continue;
+    const float inv = 1.f / l;
+    bf16_t* op = o + ((int64_t)(sb.cu[b] + qpos[cb]) * n_q + qhead[cb]) * 128 + fq * 4;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      u32x2 w;
+      w[0] = pack_bf2(oacc[d][cb][0] * inv, oacc[d][cb][1] * inv);
+      w[1] = pack_bf2(oacc[d][cb][2] * inv, oacc[d][cb][3] * inv);
+      *reinterpret_cast<u32x2*>(op + d * 16) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode
+// Block (split j, kv head g, sequence b), one wavefront: the keys of split j
+// against the group's query heads (MFMA columns 0..group-1; other columns
+// zero).  Writes (max, sum, unnormalised output) partials; the combine kernel
+// merges splits in index order.  The number of splits is fixed per launch and
+// the split length follows the sequence's current length on the device, so a
+// captured graph stays valid as the cache grows.
+constexpr int PSTRIDE = 128 + 2;
+
+__global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restrict__ q, SeqBatch sb,
+                                                         const SeqState* __restrict__ st,
+                                                         const bf16_t* __restrict__ kv, int layer,
+                                                         int n_q, int n_kv, int splits,
+                                                         float* __restrict__ part, float scale_log2) {
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, fr = lane & 15, fq = lane >> 4;
+  const SeqState s = st[sb.slot[b]];
+  const int ctx = s.len + 1;
+  int chunk = (ctx + splits - 1) / splits;
+  chunk = (chunk + 31) & ~31;
+  const int k_begin = j * chunk;
+  const int k_end = min(ctx, k_begin + chunk);
+  const int group = n_q / n_kv;
+  if (k_begin >= k_end) {
+    if (fq == 0 && fr < group) {
+      float* pp = part + (((int64_t)b * n_q + g * group + fr) * splits + j) * PSTRIDE;
+      pp[0] = -INFINITY;
+      pp[1] = 0.f;
+    }
+    return;
+  }
+  const KvGeom geo{n_kv, layer};
+  const bf16_t* Kc = kv_k(kv, s, geo, g);
+  const bf16_t* Vt = kv_vt(kv, s, geo, g);
+
+  bf16x8 qf[4];
+  {
+    const bool ok = fr < group;
+    const bf16_t* qp = q + ((int64_t)b * n_q + g * group + (ok ? fr : 0)) * 128 + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = ld16(qp + ks * 32);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+  f32x4 oacc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  for (int c0 = k_begin; c0 < k_end; c0 += 32) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk) {
+      sacc[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      int key = c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
+      key = min(key, k_end - 1);
+      const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16(kp + ks * 32)), qf[ks], sacc[sbk]);
+    }
+    u32x4 vraw[8];
+    const int vkey0 = c0 + fq * 8;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      vraw[d] = mask_keys(ld16(Vt + (int64_t)(d * 16 + fr) * s.cap + vkey0), vkey0, k_end);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = c0 + 8 * fq + 4 * sbk + r;
+        float v = sacc[sbk][r] * scale_log2;
+        if (key >= k_end) v = -INFINITY;
+        sacc[sbk][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = exp2_f(mrun - mnew);
+    mrun = mnew;
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[sbk][r] = exp2_f(sacc[sbk][r] - mnew);
+    const f16x8 pf = pack_p(sacc[0], sacc[1]);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls += sacc[0][r] + sacc[1][r];
+    lrun = lrun * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(vraw[d])), pf, oacc[d] * alpha);
+  }
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  if (fr < group) {
+    float* pp = part + (((int64_t)b * n_q + g * group + fr) * splits + j) * PSTRIDE;
+    if (fq == 0) {
+      pp[0] = mrun;
+      pp[1] = lrun;
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pp[2 + d * 16 + fq * 4 + r] = oacc[d][r];
+  }
+}
+
+// One block of 128 threads per (sequence, query head): merge the splits in
+// index order (max-shifted weights 2^(m_j - M)), normalise, store bf16.
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part, int splits,
+                                                             bf16_t* __restrict__ o) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* p = part + (int64_t)bh * splits * PSTRIDE;
+  float M = -INFINITY;
+  for (int j = 0; j < splits; ++j) M = fmaxf(M, p[(int64_t)j * PSTRIDE]);
+  float L = 0.f, acc = 0.f;
+  for (int j = 0; j < splits; ++j) {
+    const float m = p[(int64_t)j * PSTRIDE];
+    if (m == -INFINITY) continue;
+    const float w = exp2_f(m - M);
+    L += p[(int64_t)j * PSTRIDE + 1] * w;
+    acc += p[(int64_t)j * PSTRIDE + 2 + d] * w;
+  }
+  o[(int64_t)bh * 128 + d] = f2bf(acc / L);
+}
+
+// ---------------------------------------------------------------- float32
+constexpr int F32_MAX_CTX = 8192;
+
+// Block (token t, query head h), 128 threads: plain softmax over the visible
+// keys, all in fp32.  Used for the float32 model.
+__global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__ q, SeqBatch sb,
+                                                       const SeqState* __restrict__ st,
+                                                       const float* __restrict__ kv, int layer, int n_q,
+                                                       int n_kv, float* __restrict__ o, float scale) {
+  __shared__ float qs[128];
+  __shared__ float sc[F32_MAX_CTX];
+  __shared__ float red[4];
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int b = seq_of_token(sb, t);
+  const SeqState s = st[sb.slot[b]];
+  const int pos = sb.decode ? s.len : t - sb.cu[b];
+  const int ctx = min(pos + 1, F32_MAX_CTX);
+  const int g = h / (n_q / n_kv);
+  const KvGeom geo{n_kv, layer};
+  const float* Kc = kv_k(kv, s, geo, g);
+  const float* Vt = kv_vt(kv, s, geo, g);
+  qs[tid] = q[((int64_t)t * n_q + h) * 128 + tid];
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = tid; j < ctx; j += 128) {
+    const float* kr = Kc + (int64_t)j * 128;
+    float dot = 0.f;
+    for (int d = 0; d < 128; ++d) dot = fmaf(qs[d], kr[d], dot);
+    sc[j] = dot * scale;
+    mx = fmaxf(mx, sc[j]);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j < ctx; j += 128) {
+    const float p = __expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) red[2 + (tid >> 6)] = sum;
+  __syncthreads();
+  sum = red[2] + red[3];
+  const float* vr = Vt + (int64_t)tid * s.cap;
+  float acc = 0.f;
+  for (int j = 0; j < ctx; ++j) acc = fmaf(sc[j], vr[j], acc);
+  o[((int64_t)t * n_q + h) * 128 + tid] = acc / sum;
+}
+}  // namespace
+
+hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
+                         const bf16_t* kv, int layer, int n_q, int n_kv, bf16_t* o, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int group = n_q / n_kv;
+  if (group < 1 || group > 8 || 128 % group != 0) return hipErrorInvalidValue;
+  const int qt = 128 / group;
+  TileTable tt;
+  tt.tile_cu[0] = 0;
+  for (int b = 0; b < sb.n; ++b) {
+    const int L = sb.cu[b + 1] - sb.cu[b];
+    tt.tile_cu[b + 1] = tt.tile_cu[b] + (L + qt - 1) / qt;
+  }
+  const int total = tt.tile_cu[sb.n];
+  if (total <= 0) return hipSuccess;
+  dim3 grid(total, n_kv);
+  const float scale_log2 = kLog2e / sqrtf(128.f);
+  flash_prefill_kernel<<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+  return hipGetLastError();
+}
+
+int decode_attn_splits(int B, int n_kv, int64_t max_ctx) {
+  const int64_t by_len = (max_ctx + 31) / 32;
+  int64_t want = (2048 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
+  if (want < 1) want = 1;
+  int64_t sp = by_len < want ? by_len : want;
+  return sp < 1 ? 1 : (int)sp;
+}
+
+hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, const bf16_t* kv,
+                       int layer, int n_q, int n_kv, int splits, float* part, bf16_t* o,
+                       hipStream_t s) {
+  if (sb.n <= 0) return hipSuccess;
+  const float scale_log2 = kLog2e / sqrtf(128.f);
+  dim3 grid(splits, n_kv, sb.n);
+  decode_attn_kernel<<<grid, 64, 0, s>>>(q, sb, st, kv, layer, n_q, n_kv, splits, part, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<<<sb.n * n_q, 128, 0, s>>>(part, splits, o);
+  return hipGetLastError();
+}
+
+hipError_t attn_f32(const float* q, int T, const SeqBatch& sb, const SeqState* st, const float* kv,
+                    int layer, int n_q, int n_kv, float* o, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid(T, n_q);
+  attn_f32_kernel<<<grid, 128, 0, s>>>(q, sb, st, kv, layer, n_q, n_kv, o, 1.f / sqrtf(128.f));
+  return hipGetLastError();
+}
+
+}  // namespace q3k

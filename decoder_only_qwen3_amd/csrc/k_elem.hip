@@ -1,0 +1,268 @@
+// Memory-bound element/row kernels: embedding gather, RMSNorm, QK-Norm + RoPE
+// + KV append, argmax and sequence bookkeeping.
+//
+// Method source: "Dentro de un LLM: Inferencia en Python puro para Qwen3-0.6B
+// en MLX" (reactapp.top) -- Paso 2 (embedding lookup), Paso 3 (RMSNorm),
+// Paso 4 (RoPE), Paso 5 (QK-Norm and the KV cache), Paso 8 (greedy pick),
+// Paso 9 (the generation loop's position bookkeeping).
+#include "kernels.h"
+
+namespace q3k {
+
+// ---------------------------------------------------------------- Paso 2
+// x[r][:] = E[ids[r]][:] widened to float32.  An out-of-range ID writes a zero
+// row and raises Q3_ERRBIT_TOKEN.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ E,
+                                                    int V, int H, float* __restrict__ x,
+                                                    uint32_t* err) {
+  const int r = blockIdx.x;
+  int id = ids[r];
+  const bool bad = id < 0 || id >= V;
+  if (bad) {
+    if (threadIdx.x == 0) atomicOr(err, Q3_ERRBIT_TOKEN);
+    id = 0;
+  }
+  const T* src = E + (int64_t)id * H;
+  float* dst = x + (int64_t)r * H;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) dst[c] = bad ? 0.f : ld_f<T>(src + c);
+}
+
+hipError_t embed(int dtype, const int32_t* ids, int n, const void* E, int V, int H, float* x,
+                 uint32_t* err, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == BF16)
+    embed_kernel<bf16_t><<<n, 256, 0, s>>>(ids, (const bf16_t*)E, V, H, x, err);
+  else
+    embed_kernel<float><<<n, 256, 0, s>>>(ids, (const float*)E, V, H, x, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Paso 3
+// One wavefront per row: out = x * rsqrt(mean(x^2) + eps) * w.  H % 256 == 0.
+template <typename Tout>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int rows, RowMap map,
+                                                      const float* __restrict__ w, int H, float eps,
+                                                      Tout* __restrict__ out) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = map.n >= 0 ? map.row[r] : r;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)src * H);
+  float ss = 0.f;
+  for (int c = lane; c < H / 4; c += 64) {
+    float4 v = xr[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  const float4* wr = reinterpret_cast<const float4*>(w);
+  Tout* o = out + (int64_t)r * H;
+  for (int c = lane; c < H / 4; c += 64) {
+    float4 v = xr[c], g = wr[c];
+    st_f<Tout>(o + 4 * c + 0, v.x * inv * g.x);
+    st_f<Tout>(o + 4 * c + 1, v.y * inv * g.y);
+    st_f<Tout>(o + 4 * c + 2, v.z * inv * g.z);
+    st_f<Tout>(o + 4 * c + 3, v.w * inv * g.w);
+  }
+}
+
+hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, const float* w,
+                   int H, float eps, void* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4);
+  if (out_dtype == BF16)
+    rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>(x, rows, map, w, H, eps, (bf16_t*)out);
+  else
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(x, rows, map, w, H, eps, (float*)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Pasos 4-5
+// One wavefront per (token, head unit); units are the n_q query heads, then
+// the n_kv key heads, then the n_kv value heads of the fused projection row.
+// Lane l owns dims l and l+64, which is exactly one RoPE pair.
+//   query/key: per-head RMSNorm (weights q_norm / k_norm, same eps), then the
+//              pair rotation by pos * theta^(-l/64) read from the cos/sin table;
+//              queries go to q_out [T][n_q][128], keys to the cache row `pos`.
+//   value:     stored unchanged into the transposed value block at column pos.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_append_kernel(
+    const float* __restrict__ qkv, int T_, SeqBatch sb, SeqState* __restrict__ st, T* __restrict__ kv,
+    int layer, int n_q, int n_kv, const float* __restrict__ qn, const float* __restrict__ kn, float eps,
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, T* __restrict__ q_out,
+    uint32_t* err) {
+  const int units = n_q + 2 * n_kv;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wv >= T_ * units) return;
+  const int t = wv / units, u = wv - t * units;
+  const int b = seq_of_token(sb, t);
+  const SeqState s = st[sb.slot[b]];
+  const int pos = sb.decode ? s.len : t - sb.cu[b];
+  if (pos < 0 || pos >= s.cap) {  // host validation makes this unreachable
+    if (lane == 0) atomicOr(err, 4u);
+    return;
+  }
+  const float* src = qkv + (int64_t)t * units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
+  float a = src[lane], c = src[lane + 64];
+  const KvGeom g{n_kv, layer};
+  if (u < n_q + n_kv) {
+    const float* w = u < n_q ? qn : kn;
+    const float ss = wave_sum(a * a + c * c);
+    const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
+    a = a * inv * w[lane];
+    c = c * inv * w[lane + 64];
+    const float cs = cos_t[(int64_t)pos * 64 + lane], sn = sin_t[(int64_t)pos * 64 + lane];
+    const float ra = a * cs - c * sn, rc = a * sn + c * cs;
+    T* dst;
+    if (u < n_q)
+      dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
+    else
+      dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
+    st_f<T>(dst + lane, ra);
+    st_f<T>(dst + lane + 64, rc);
+  } else {
+    T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
+    st_f<T>(dst + (int64_t)lane * s.cap + pos, a);
+    st_f<T>(dst + (int64_t)(lane + 64) * s.cap + pos, c);
+  }
+}
+
+hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
+                       void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
+                       float eps, const float* cos_t, const float* sin_t, void* q_out,
+                       uint32_t* err, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int64_t waves = (int64_t)T * (n_q + 2 * n_kv);
+  dim3 grid((unsigned)((waves + 3) / 4));
+  if (dtype == BF16)
+    rope_append_kernel<bf16_t><<<grid, 256, 0, s>>>(qkv, T, sb, st, (bf16_t*)kv, layer, n_q, n_kv, qn, kn,
+                                                    eps, cos_t, sin_t, (bf16_t*)q_out, err);
+  else
+    rope_append_kernel<float><<<grid, 256, 0, s>>>(qkv, T, sb, st, (float*)kv, layer, n_q, n_kv, qn, kn,
+                                                   eps, cos_t, sin_t, (float*)q_out, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Paso 8
+// Greedy pick: largest value, lowest index among equal maxima.
+Q3_DEV void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+// Block-wide (max, lowest index) over 256 threads; result valid in thread 0.
+Q3_DEV void block_argmax(float& bv, int& bi) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float ov = __shfl_xor(bv, o, 64);
+    int oi = __shfl_xor(bi, o, 64);
+    better(bv, bi, ov, oi);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < (int)(blockDim.x >> 6); ++k) better(bv, bi, sv[k], si[k]);
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_rows_kernel(const float* __restrict__ logits, int64_t ld,
+                                                          RowMap rows, int V, int32_t* next,
+                                                          uint32_t* err) {
+  const int r = blockIdx.x;
+  const int src = rows.n >= 0 ? rows.row[r] : r;
+  const float* p = logits + (int64_t)src * ld;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  bool finite = true;
+  for (int i = threadIdx.x; i < V; i += blockDim.x) {
+    float v = p[i];
+    finite &= __builtin_isfinite(v);
+    better(bv, bi, v, i);
+  }
+  if (!finite) atomicOr(err, Q3_ERRBIT_NONFINITE);
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) next[r] = bi == 0x7fffffff ? 0 : bi;
+}
+
+hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
+                       uint32_t* err, hipStream_t s) {
+  const int n = rows.n;
+  if (n <= 0) return hipSuccess;
+  argmax_rows_kernel<<<n, 256, 0, s>>>(logits, ld, rows, V, next, err);
+  return hipGetLastError();
+}
+
+// Pasos 8-9: reduce the lm_head kernel's per-block partials, then move the
+// sequences forward (decode: one more cached token; prefill: the prompt).
+__global__ __launch_bounds__(256) void argmax_finish_kernel(const float* __restrict__ pval,
+                                                            const int32_t* __restrict__ pidx,
+                                                            int nblocks, int M, int32_t* next,
+                                                            SeqBatch sb, SeqState* st, uint32_t* err) {
+  const int m = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  bool finite = true;
+  for (int j = threadIdx.x; j < nblocks; j += blockDim.x) {
+    float v = pval[(int64_t)j * M + m];
+    int i = pidx[(int64_t)j * M + m];
+    finite &= __builtin_isfinite(v) || i < 0;
+    if (i >= 0) better(bv, bi, v, i);
+  }
+  if (!finite) atomicOr(err, Q3_ERRBIT_NONFINITE);
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) {
+    next[m] = bi == 0x7fffffff ? 0 : bi;
+    if (m < sb.n) {
+      SeqState* s = st + sb.slot[m];
+      s->len = sb.decode ? s->len + 1 : sb.cu[m + 1] - sb.cu[m];
+    }
+  }
+}
+
+hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
+                         const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  argmax_finish_kernel<<<M, 256, 0, s>>>(pval, pidx, nblocks, M, next, sb, st, err);
+  return hipGetLastError();
+}
+
+__global__ void seq_advance_kernel(SeqBatch sb, SeqState* st) {
+  const int b = threadIdx.x;
+  if (b < sb.n) {
+    SeqState* s = st + sb.slot[b];
+    s->len = sb.decode ? s->len + 1 : sb.cu[b + 1] - sb.cu[b];
+  }
+}
+
+hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s) {
+  seq_advance_kernel<<<1, 64, 0, s>>>(sb, st);
+  return hipGetLastError();
+}
+
+__global__ void widen_kernel(const bf16_t* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf2f(src[i]);
+}
+
+hipError_t widen_bf16(const bf16_t* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  widen_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace q3k

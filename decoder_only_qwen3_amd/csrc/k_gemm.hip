@@ -1,0 +1,151 @@
+// bf16 MFMA GEMM for the prefill projections and the SwiGLU MLP.
+//
+//   C[M,N] = A[M,K] . W[N,K]^T,  A = activations (row-major, K contiguous),
+//   W = a weight matrix stored (out_features, in_features) as the page's
+//   listings apply it (x @ W^T).  fp32 accumulation on v_mfma_f32_16x16x32_bf16.
+//
+// Method source: "Dentro de un LLM: Inferencia en Python puro para Qwen3-0.6B
+// en MLX" -- Paso 5 (q/k/v and o projections), Paso 6 (SwiGLU: gate, up,
+// silu(gate) * up, down), Paso 7 (residual adds).
+//
+// Tiling: 128x128 block tile, K step 64, 256 threads = 4 wavefronts in a 2x2
+// grid, each wavefront owning a 64x64 sub-tile (4x4 MFMA tiles of 16x16).
+// Global -> register prefetch of the next K step overlaps the MFMAs of the
+// current one; tiles are staged through LDS with 16-byte row padding.
+#include "kernels.h"
+
+namespace q3k {
+
+namespace {
+constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+
+Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int M,
+                                                           const bf16_t* __restrict__ W, int N, int K,
+                                                           void* __restrict__ out, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][BN * LDK];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+
+  u32x4 ra[4], rw[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 32 * i;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      ra[i] = (bm0 + r < M) ? ld16(A + (int64_t)(bm0 + r) * K + k0 + lcol) : z;
+      rw[i] = (bn0 + r < N) ? ld16(W + (int64_t)(bn0 + r) * K + k0 + lcol) : z;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sA[buf][(lrow + 32 * i) * LDK + lcol]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sW[buf][(lrow + 32 * i) * LDK + lcol]) = rw[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[4], bw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + i * 16 + fr) * LDK + ks * 32 + fk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bw[j] = *reinterpret_cast<const bf16x8*>(&sW[buf][(wn * 64 + j * 16 + fr) * LDK + ks * 32 + fk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // C layout of a 16x16 MFMA tile: lane l holds rows (l/16)*4 + r, column l%16.
+  const int rbase = bm0 + wm * 64 + (lane >> 4) * 4;
+  const int cbase = bn0 + wn * 64 + (lane & 15);
+  if constexpr (EPI == EPI_SWIGLU) {
+    // Packed rows: every 32 rows of W are 16 gate rows then the matching 16 up
+    // rows, so tile j=2p is gate and j=2p+1 is up for the same output column.
+    bf16_t* o = reinterpret_cast<bf16_t*>(out);
+    const int ocol0 = (bn0 + wn * 64) / 2 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int col = ocol0 + p * 16;
+          if (row < M && 2 * col < N) {
+            const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
+            o[(int64_t)row * ldo + col] = f2bf(silu_f(g) * u);
+          }
+        }
+  } else {
+    float* o = reinterpret_cast<float*>(out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + i * 16 + r;
+          const int col = cbase + j * 16;
+          if (row < M && col < N) {
+            float* p = o + (int64_t)row * ldo + col;
+            if constexpr (EPI == EPI_RESADD)
+              *p += acc[i][j][r];
+            else
+              *p = acc[i][j][r];
+          }
+        }
+  }
+}
+}  // namespace
+
+hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
+                     int64_t ldo, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (K % BK != 0 || N % 16 != 0) return hipErrorInvalidValue;
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  switch (epi) {
+    case EPI_STORE:
+    case EPI_ARGMAX:
+      gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    case EPI_RESADD:
+      gemm_bf16_kernel<EPI_RESADD><<<grid, 256, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    case EPI_SWIGLU:
+      if (N % 64 != 0) return hipErrorInvalidValue;
+      gemm_bf16_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q3k

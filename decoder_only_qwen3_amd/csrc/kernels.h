@@ -1,0 +1,84 @@
+// Host-side launchers for the libq3 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace q3k {
+
+enum Dtype { F32 = 0, BF16 = 1 };
+
+// Epilogues of the projection kernels.
+enum Epi {
+  EPI_STORE = 0,    // out[m][n] = acc                       (float out)
+  EPI_RESADD = 1,   // out[m][n] += acc                      (float residual stream)
+  EPI_SWIGLU = 2,   // rows packed [gate 16 | up 16]...; out[m][j] = silu(g)*u (act dtype)
+  EPI_ARGMAX = 3,   // out[m][n] = acc (float logits) + per-block (max, index) partials
+};
+
+// Rows selected from a row-major matrix (n < 0: rows 0..count-1 in order).
+struct RowMap {
+  int32_t n;
+  int32_t row[Q3_MAX_BATCH];
+};
+
+// ---------------------------------------------------------------- k_elem.hip
+hipError_t embed(int dtype, const int32_t* ids, int n, const void* E, int V, int H, float* x,
+                 uint32_t* err, hipStream_t s);
+hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, const float* w,
+                   int H, float eps, void* out, hipStream_t s);
+hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
+                       void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
+                       float eps, const float* cos_t, const float* sin_t, void* q_out,
+                       uint32_t* err, hipStream_t s);
+hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
+                       uint32_t* err, hipStream_t s);
+// Reduce per-block (max, index) partials of EPI_ARGMAX into next[m], then
+// advance the lengths of the sequences of `sb` (decode: +1; prefill: = length).
+hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
+                         const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s);
+hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s);
+hipError_t widen_bf16(const bf16_t* src, float* dst, int64_t n, hipStream_t s);
+hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- k_gemm.hip
+// C[M,N] = A[M,K] . W[N,K]^T with bf16 operands on MFMA; K % 64 == 0.
+hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
+                     int64_t ldo, hipStream_t s);
+
+// ---------------------------------------------------------------- k_skinny.hip
+struct SkinnyPlan {
+  int nst;     // 32-wide K steps per wavefront (4 or 8)
+  int ksplit;  // blocks sharing one row range, each over K/ksplit
+};
+SkinnyPlan skinny_plan(int epi, int M, int N, int K);
+size_t skinny_partials_floats(int M, int N, int ksplit);
+// M <= 64 rows of X (bf16) times W[N,K]^T (bf16).  `partials` holds
+// ksplit*M*N floats when ksplit > 1; `counters` N/16/rb zeroed words.
+hipError_t skinny_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, void* out,
+                       int64_t ldo, float* partials, uint32_t* counters, float* amax_val,
+                       int32_t* amax_idx, SkinnyPlan plan, hipStream_t s);
+int skinny_argmax_blocks(int N, SkinnyPlan plan);
+// float32 weights and activations (the float32 model); any M.
+hipError_t gemv_f32(int epi, const float* X, int M, const float* W, int N, int K, void* out,
+                    int64_t ldo, hipStream_t s);
+
+// ---------------------------------------------------------------- k_attn.hip
+hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
+                         const bf16_t* kv, int layer, int n_q, int n_kv, bf16_t* o,
+                         hipStream_t s);
+int decode_attn_splits(int B, int n_kv, int64_t max_ctx);
+hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, const bf16_t* kv,
+                       int layer, int n_q, int n_kv, int splits, float* part, bf16_t* o,
+                       hipStream_t s);
+hipError_t attn_f32(const float* q, int T, const SeqBatch& sb, const SeqState* st,
+                    const float* kv, int layer, int n_q, int n_kv, float* o, hipStream_t s);
+
+}  // namespace q3k
+
+#include <string>
+namespace q3rt {
+// Thread-local message returned by q3_last_error().
+void set_last_error(const std::string& msg);
+}  // namespace q3rt

@@ -1,0 +1,241 @@
+// Single-kernel entry points (include/q3_ops.h): the kernels of the forward
+// pass on explicit buffers, for parity tests and kernel benchmarks.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/q3_ops.h"
+#include "kernels.h"
+
+using namespace q3k;
+
+namespace {
+q3_status op_fail(q3_status st, const std::string& m) {
+  q3rt::set_last_error(m);
+  return st;
+}
+q3_status op_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return Q3_OK;
+  return op_fail(Q3_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+#define OP_TRY(expr)                                  \
+  do {                                                \
+    q3_status s_ = op_hip((expr), #expr);             \
+    if (s_ != Q3_OK) return s_;                       \
+  } while (0)
+
+size_t al(size_t v) { return (v + 255) / 256 * 256; }
+
+struct SkinnyWs {
+  size_t counters, err, amax_val, amax_idx, partials, total;
+};
+SkinnyWs skinny_ws(int epi, int M, int N, int K) {
+  SkinnyWs w;
+  SkinnyPlan p = skinny_plan(epi, M, N, K);
+  const size_t groups = (size_t)N / 16;
+  w.counters = 0;
+  w.err = al(groups * 4);
+  w.amax_val = w.err + al(16);
+  w.amax_idx = w.amax_val + al(groups * M * 4);
+  w.partials = w.amax_idx + al(groups * M * 4);
+  w.total = w.partials + al(skinny_partials_floats(M, N, p.ksplit) * 4 + 4);
+  return w;
+}
+
+// Device tables for the arena-based ops: SeqState[n] then an error word.
+q3_status upload_states(int n, const int64_t* base, const int32_t* cap, const int32_t* len, void* d_ws,
+                        hipStream_t s) {
+  std::vector<SeqState> st(n);
+  for (int b = 0; b < n; ++b) {
+    if (cap[b] <= 0 || cap[b] % 64 != 0) return op_fail(Q3_E_ARG, "capacities must be positive multiples of 64");
+    if (len[b] < 0 || len[b] > cap[b]) return op_fail(Q3_E_ARG, "length outside capacity");
+    st[b] = SeqState{base[b], cap[b], len[b]};
+  }
+  OP_TRY(hipStreamSynchronize(s));
+  OP_TRY(hipMemcpy(d_ws, st.data(), n * sizeof(SeqState), hipMemcpyHostToDevice));
+  return Q3_OK;
+}
+
+q3_status make_batch(int n, const int32_t* cu, int decode, SeqBatch* sb) {
+  if (n < 1 || n > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "n_seqs must be in [1, 64]");
+  std::memset(sb, 0, sizeof(*sb));
+  sb->n = n;
+  sb->decode = decode;
+  for (int b = 0; b < n; ++b) sb->slot[b] = b;
+  if (decode) {
+    for (int b = 0; b <= n; ++b) sb->cu[b] = b;
+  } else {
+    if (!cu || cu[0] != 0) return op_fail(Q3_E_ARG, "cu_seqlens must start at 0");
+    for (int b = 0; b <= n; ++b) sb->cu[b] = cu[b];
+    for (int b = 0; b < n; ++b)
+      if (cu[b + 1] <= cu[b]) return op_fail(Q3_E_ARG, "empty sequence");
+  }
+  return Q3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+q3_status q3op_embed(int32_t dtype, const int32_t* d_ids, int32_t n, const void* d_table, int32_t vocab,
+                     int32_t dim, float* d_out, uint32_t* d_err, void* stream) {
+  if (n < 0 || !d_ids || !d_table || !d_out || !d_err) return op_fail(Q3_E_ARG, "bad argument");
+  OP_TRY(embed(dtype, d_ids, n, d_table, vocab, dim, d_out, d_err, (hipStream_t)stream));
+  return Q3_OK;
+}
+
+q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const float* d_w, int32_t dim,
+                       float eps, void* d_out, void* stream) {
+  if (rows < 0 || dim <= 0 || dim % 256 != 0 || !d_x || !d_w || !d_out) return op_fail(Q3_E_ARG, "bad argument");
+  RowMap all;
+  all.n = -1;
+  OP_TRY(rmsnorm(out_dtype, d_x, rows, all, d_w, dim, eps, d_out, (hipStream_t)stream));
+  return Q3_OK;
+}
+
+size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K) {
+  if (kernel == Q3OP_SKINNY) return skinny_ws(epi, M, N, K).total;
+  return 0;
+}
+
+q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
+                      int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
+                      void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (!d_x || !d_w || !d_out || M < 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
+  if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
+  if (epi == EPI_ARGMAX && (!d_next || M > Q3_MAX_BATCH)) return op_fail(Q3_E_ARG, "logits epilogue needs d_next and M <= 64");
+  RowMap rows;
+  rows.n = M;
+  for (int i = 0; i < M && i < Q3_MAX_BATCH; ++i) rows.row[i] = i;
+  uint32_t* no_err = nullptr;
+  if (kernel == Q3OP_GEMM) {
+    OP_TRY(gemm_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, d_out, ldo, s));
+    if (epi == EPI_ARGMAX) {
+      if (!d_ws || ws_bytes < 4) return op_fail(Q3_E_ARG, "logits epilogue needs 4 bytes of workspace");
+      no_err = (uint32_t*)d_ws;
+      OP_TRY(argmax_rows((const float*)d_out, ldo, rows, N, d_next, no_err, s));
+    }
+    return Q3_OK;
+  }
+  if (kernel == Q3OP_GEMV_F32) {
+    OP_TRY(gemv_f32(epi, (const float*)d_x, M, (const float*)d_w, N, K, d_out, ldo, s));
+    if (epi == EPI_ARGMAX) {
+      if (!d_ws || ws_bytes < 4) return op_fail(Q3_E_ARG, "logits epilogue needs 4 bytes of workspace");
+      OP_TRY(argmax_rows((const float*)d_out, ldo, rows, N, d_next, (uint32_t*)d_ws, s));
+    }
+    return Q3_OK;
+  }
+  if (kernel == Q3OP_SKINNY) {
+    if (M > Q3_MAX_BATCH) return op_fail(Q3_E_UNSUPPORTED, "the weight-streaming kernel takes M <= 64");
+    SkinnyWs w = skinny_ws(epi, M, N, K);
+    if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace too small");
+    char* ws = (char*)d_ws;
+    SkinnyPlan p = skinny_plan(epi, M, N, K);
+    OP_TRY(fill_u32((uint32_t*)(ws + w.counters), 0u, N / 16, s));
+    OP_TRY(skinny_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, d_out, ldo, (float*)(ws + w.partials),
+                       (uint32_t*)(ws + w.counters), (float*)(ws + w.amax_val), (int32_t*)(ws + w.amax_idx), p, s));
+    if (epi == EPI_ARGMAX) {
+      SeqBatch none;
+      std::memset(&none, 0, sizeof(none));
+      OP_TRY(argmax_finish((const float*)(ws + w.amax_val), (const int32_t*)(ws + w.amax_idx),
+                           skinny_argmax_blocks(N, p), M, d_next, none, nullptr, (uint32_t*)(ws + w.err), s));
+    }
+    return Q3_OK;
+  }
+  return op_fail(Q3_E_ARG, "unknown kernel");
+}
+
+size_t q3op_rope_workspace_bytes(int32_t n_seqs, int32_t max_pos) {
+  return al(n_seqs * sizeof(SeqState)) + al(16) + 2 * al((size_t)max_pos * 64 * 4);
+}
+
+q3_status q3op_rope_append(int32_t dtype, const float* d_qkv, int32_t n, const int32_t* h_cu, int32_t decode,
+                           const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len, void* d_kv,
+                           int32_t n_q, int32_t n_kv, const float* d_qn, const float* d_kn, float eps,
+                           double theta, int32_t max_pos, void* d_q_out, void* d_ws, size_t ws_bytes,
+                           void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  SeqBatch sb;
+  q3_status st = make_batch(n, h_cu, decode, &sb);
+  if (st != Q3_OK) return st;
+  if (!d_qkv || !d_kv || !d_qn || !d_kn || !d_q_out || !h_base || !h_cap || !h_len || max_pos <= 0)
+    return op_fail(Q3_E_ARG, "bad argument");
+  if (!d_ws || ws_bytes < q3op_rope_workspace_bytes(n, max_pos)) return op_fail(Q3_E_ARG, "workspace too small");
+  for (int b = 0; b < n; ++b) {
+    const int last = decode ? h_len[b] : (sb.cu[b + 1] - sb.cu[b] - 1);
+    if (last >= h_cap[b] || last >= max_pos) return op_fail(Q3_E_CAPACITY, "position beyond capacity");
+  }
+  char* ws = (char*)d_ws;
+  st = upload_states(n, h_base, h_cap, h_len, ws, s);
+  if (st != Q3_OK) return st;
+  uint32_t* err = (uint32_t*)(ws + al(n * sizeof(SeqState)));
+  float* cos_t = (float*)(ws + al(n * sizeof(SeqState)) + al(16));
+  float* sin_t = (float*)((char*)cos_t + al((size_t)max_pos * 64 * 4));
+  std::vector<float> cs((size_t)max_pos * 64), sn((size_t)max_pos * 64);
+  for (int p = 0; p < max_pos; ++p)
+    for (int i = 0; i < 64; ++i) {
+      const double a = (double)p * std::pow(theta, -(double)i / 64.0);
+      cs[(size_t)p * 64 + i] = (float)std::cos(a);
+      sn[(size_t)p * 64 + i] = (float)std::sin(a);
+    }
+  OP_TRY(hipMemcpy(cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+  OP_TRY(hipMemcpy(sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+  OP_TRY(fill_u32(err, 0u, 1, s));
+  const int T = sb.cu[n];
+  OP_TRY(rope_append(dtype, d_qkv, T, sb, (SeqState*)ws, d_kv, 0, n_q, n_kv, d_qn, d_kn, eps, cos_t, sin_t, d_q_out,
+                     err, s));
+  return Q3_OK;
+}
+
+size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t n_q, int32_t splits) {
+  size_t b = al(n_seqs * sizeof(SeqState));
+  if (kernel == Q3OP_ATTN_DECODE) b += al((size_t)n_seqs * n_q * (splits > 0 ? splits : 2048) * 130 * 4);
+  return b;
+}
+
+q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32_t* h_cu, int32_t decode,
+                         const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len, const void* d_kv,
+                         int32_t n_q, int32_t n_kv, int32_t splits, void* d_out, void* d_ws, size_t ws_bytes,
+                         void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  SeqBatch sb;
+  q3_status st = make_batch(n, h_cu, decode, &sb);
+  if (st != Q3_OK) return st;
+  if (!d_q || !d_kv || !d_out || !h_base || !h_cap || !h_len) return op_fail(Q3_E_ARG, "bad argument");
+  if (n_kv <= 0 || n_q % n_kv != 0 || n_q / n_kv > 8) return op_fail(Q3_E_UNSUPPORTED, "head grouping");
+  if (kernel == Q3OP_ATTN_FLASH && decode) return op_fail(Q3_E_ARG, "flash kernel is the prefill kernel");
+  if (kernel == Q3OP_ATTN_DECODE && !decode) return op_fail(Q3_E_ARG, "decode kernel needs decode = 1");
+  for (int b = 0; b < n; ++b) {
+    const int ctx = decode ? h_len[b] + 1 : sb.cu[b + 1] - sb.cu[b];
+    if (ctx > h_cap[b]) return op_fail(Q3_E_CAPACITY, "context beyond capacity");
+  }
+  if (kernel == Q3OP_ATTN_DECODE && splits <= 0) {
+    int64_t mc = 1;
+    for (int b = 0; b < n; ++b) mc = std::max<int64_t>(mc, h_cap[b]);
+    splits = decode_attn_splits(n, n_kv, mc);
+  }
+  if (!d_ws || ws_bytes < q3op_attention_workspace_bytes(kernel, n, n_q, splits))
+    return op_fail(Q3_E_ARG, "workspace too small");
+  char* ws = (char*)d_ws;
+  st = upload_states(n, h_base, h_cap, h_len, ws, s);
+  if (st != Q3_OK) return st;
+  const SeqState* sst = (const SeqState*)ws;
+  const int T = sb.cu[n];
+  if (kernel == Q3OP_ATTN_FLASH) {
+    OP_TRY(flash_prefill((const bf16_t*)d_q, T, sb, sst, (const bf16_t*)d_kv, 0, n_q, n_kv, (bf16_t*)d_out, s));
+  } else if (kernel == Q3OP_ATTN_DECODE) {
+    float* part = (float*)(ws + al(n * sizeof(SeqState)));
+    OP_TRY(decode_attn((const bf16_t*)d_q, sb, sst, (const bf16_t*)d_kv, 0, n_q, n_kv, splits, part,
+                       (bf16_t*)d_out, s));
+  } else if (kernel == Q3OP_ATTN_F32) {
+    OP_TRY(attn_f32((const float*)d_q, T, sb, sst, (const float*)d_kv, 0, n_q, n_kv, (float*)d_out, s));
+  } else {
+    return op_fail(Q3_E_ARG, "unknown kernel");
+  }
+  return Q3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,738 @@
+// libq3 host runtime: the C ABI of include/q3.h -- validation, memory layout,
+// weight packing, KV arena, the prefill and decode launch sequences and the
+// decode-step HIP graphs.
+//
+// The launch sequence follows "Dentro de un LLM: Inferencia en Python puro
+// para Qwen3-0.6B en MLX": Paso 2 (embedding), Paso 7 (pre-norm block with
+// two residual adds, repeated per layer), Paso 8 (final norm, tied lm_head,
+// greedy pick), Paso 9 (prefill once, then one token per step with the KV
+// cache; the position of a new token is the number already cached).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/q3.h"
+#include "kernels.h"
+
+using namespace q3k;
+
+namespace {
+
+thread_local std::string g_err;
+
+q3_status fail(q3_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(Q3_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));         \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct LayerW {
+  size_t qkv, o, gu, d;               // packed projection weights (model dtype)
+  size_t in_norm, post_norm, qn, kn;  // float32
+};
+
+struct WeightLayout {
+  size_t embed = 0, final_norm = 0, cos_t = 0, sin_t = 0, total = 0;
+  std::vector<LayerW> layers;
+};
+
+struct WsLayout {
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, partials, counters, attn_part, state,
+      err, total;
+  int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
+  int64_t n_counters;
+  int amax_blocks;
+};
+
+struct HostSlot {
+  bool allocated = false;
+  int64_t base = 0;  // element offset
+  int64_t cap = 0;
+  int64_t len = 0;
+};
+
+bool valid_config(const q3_config* c, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return false; };
+  if (!c) return bad("config is NULL");
+  if (c->n_layers < 0) return bad("n_layers < 0");
+  if (c->head_dim != 128) return bad("head_dim must be 128");
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads != 0)
+    return bad("n_q_heads must be a positive multiple of n_kv_heads");
+  if (c->n_q_heads / c->n_kv_heads > 8) return bad("query heads per kv head must be <= 8");
+  if (c->hidden <= 0 || c->hidden % 512 != 0) return bad("hidden must be a positive multiple of 512");
+  if (c->ffn <= 0 || c->ffn % 512 != 0) return bad("ffn must be a positive multiple of 512");
+  if ((c->n_q_heads * 128) % 512 != 0) return bad("n_q_heads*128 must be a multiple of 512");
+  if (c->vocab <= 0 || c->vocab % 16 != 0) return bad("vocab must be a positive multiple of 16");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0)) return bad("rms_eps and rope_theta must be > 0");
+  if (c->dtype != Q3_F32 && c->dtype != Q3_BF16) return bad("dtype must be Q3_F32 or Q3_BF16");
+  if (c->max_slots <= 0) return bad("max_slots must be > 0");
+  if (c->max_positions <= 0 || c->max_positions > (1 << 24)) return bad("max_positions out of range");
+  if (c->dtype == Q3_F32 && c->max_positions > 8192) return bad("the float32 model supports at most 8192 positions");
+  if (c->max_prefill_tokens <= 0 || c->max_prefill_tokens > (1 << 24)) return bad("max_prefill_tokens out of range");
+  if (c->kv_tokens <= 0) return bad("kv_tokens must be > 0");
+  return true;
+}
+
+int esz(const q3_config& c) { return c.dtype == Q3_BF16 ? 2 : 4; }
+int qkv_rows(const q3_config& c) { return (c.n_q_heads + 2 * c.n_kv_heads) * 128; }
+
+WeightLayout weight_layout(const q3_config& c) {
+  WeightLayout L;
+  const size_t e = esz(c), H = c.hidden, Q = (size_t)c.n_q_heads * 128, I = c.ffn;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.embed = take((size_t)c.vocab * H * e);
+  for (int i = 0; i < c.n_layers; ++i) {
+    LayerW w;
+    w.qkv = take((size_t)qkv_rows(c) * H * e);
+    w.o = take(H * Q * e);
+    w.gu = take(2 * I * H * e);
+    w.d = take(H * I * e);
+    w.in_norm = take(H * 4);
+    w.post_norm = take(H * 4);
+    w.qn = take(128 * 4);
+    w.kn = take(128 * 4);
+    L.layers.push_back(w);
+  }
+  L.final_norm = take(H * 4);
+  L.cos_t = take((size_t)c.max_positions * 64 * 4);
+  L.sin_t = take((size_t)c.max_positions * 64 * 4);
+  L.total = off;
+  return L;
+}
+
+int max_attn_splits_rows(const q3_config& c) {
+  int best = 0;
+  for (int B = 1; B <= Q3_MAX_BATCH; ++B)
+    best = std::max(best, B * decode_attn_splits(B, c.n_kv_heads, c.max_positions));
+  return best;
+}
+
+WsLayout ws_layout(const q3_config& c) {
+  WsLayout W;
+  const size_t e = esz(c), H = c.hidden, Q = (size_t)c.n_q_heads * 128, I = c.ffn;
+  const int64_t R = std::max<int64_t>(c.max_prefill_tokens, Q3_MAX_BATCH);
+  W.rows = R;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  W.x = take(R * H * 4);
+  W.h = take(R * H * e);
+  W.qkv = take((size_t)R * qkv_rows(c) * 4);
+  W.q = take(R * Q * e);
+  W.o = take(R * Q * e);
+  W.m = take(R * I * e);
+  W.logits = take((size_t)Q3_MAX_BATCH * c.vocab * 4);
+  W.amax_blocks = c.vocab / 16;
+  W.amax_val = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
+  W.amax_idx = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
+  size_t part = 0;
+  int64_t counters = 0;
+  const int shapes[5][3] = {{EPI_STORE, qkv_rows(c), c.hidden},
+                            {EPI_RESADD, c.hidden, (int)Q},
+                            {EPI_SWIGLU, 2 * c.ffn, c.hidden},
+                            {EPI_RESADD, c.hidden, c.ffn},
+                            {EPI_ARGMAX, c.vocab, c.hidden}};
+  for (auto& s : shapes) {
+    SkinnyPlan p = skinny_plan(s[0], Q3_MAX_BATCH, s[1], s[2]);
+    part = std::max(part, skinny_partials_floats(Q3_MAX_BATCH, s[1], p.ksplit));
+    counters = std::max<int64_t>(counters, s[1] / 16);
+  }
+  W.n_counters = counters;
+  W.partials = take(part * 4 + 4);
+  W.counters = take(counters * 4);
+  W.attn_part = take((size_t)max_attn_splits_rows(c) * c.n_q_heads * 130 * 4);
+  W.state = take((size_t)c.max_slots * sizeof(SeqState));
+  W.err = take(16);
+  W.total = off;
+  return W;
+}
+
+// One decode-step graph per (batch, slots, pointers, stream).
+struct GraphKey {
+  std::vector<int32_t> slots;
+  const void *tokens, *logits, *next, *stream;
+  bool operator<(const GraphKey& o) const {
+    if (slots != o.slots) return slots < o.slots;
+    if (tokens != o.tokens) return tokens < o.tokens;
+    if (logits != o.logits) return logits < o.logits;
+    if (next != o.next) return next < o.next;
+    return stream < o.stream;
+  }
+};
+
+}  // namespace
+
+namespace q3rt {
+void set_last_error(const std::string& msg) { g_err = msg; }
+}  // namespace q3rt
+
+struct q3_model {
+  q3_config cfg;
+  WeightLayout wl;
+  WsLayout wsl;
+  char* w = nullptr;
+  char* kv = nullptr;
+  char* ws = nullptr;
+  size_t kv_bytes = 0;
+  bool bound = false, loaded = false;
+  std::vector<HostSlot> slots;
+  int64_t kv_used = 0;  // elements
+  bool use_graph = true;
+  std::map<GraphKey, hipGraphExec_t> graphs;
+
+  template <typename T = void>
+  T* W(size_t off) const { return reinterpret_cast<T*>(w + off); }
+  template <typename T = void>
+  T* WS(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  SeqState* state() const { return WS<SeqState>(wsl.state); }
+  uint32_t* err() const { return WS<uint32_t>(wsl.err); }
+
+  void drop_graphs() {
+    for (auto& kvp : graphs) hipGraphExecDestroy(kvp.second);
+    graphs.clear();
+  }
+};
+
+namespace {
+
+bool ready(const q3_model* m, q3_status* st) {
+  if (!m) { *st = fail(Q3_E_ARG, "model is NULL"); return false; }
+  if (!m->bound) { *st = fail(Q3_E_STATE, "q3_bind_memory has not been called"); return false; }
+  if (!m->loaded) { *st = fail(Q3_E_STATE, "q3_load_weights has not completed"); return false; }
+  return true;
+}
+
+q3_status upload_state(q3_model* m, int32_t slot, hipStream_t s) {
+  const HostSlot& h = m->slots[slot];
+  SeqState v{h.base, (int32_t)h.cap, (int32_t)h.len};
+  HIP_TRY(hipMemcpyAsync(m->state() + slot, &v, sizeof(v), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return Q3_OK;
+}
+
+// ------------------------------------------------------------- launch sequences
+q3_status check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(Q3_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return Q3_OK;
+}
+#define LAUNCH(expr)                                   \
+  do {                                                 \
+    q3_status st_ = check((expr), #expr);              \
+    if (st_ != Q3_OK) return st_;                      \
+  } while (0)
+
+// The transformer blocks of Paso 7 over `T` rows already embedded in x.
+q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hipStream_t s) {
+  const q3_config& c = m->cfg;
+  const WsLayout& L = m->wsl;
+  const int H = c.hidden, Q = c.n_q_heads * 128, I = c.ffn, NQKV = qkv_rows(c);
+  float* x = m->WS<float>(L.x);
+  void* h = m->WS(L.h);
+  float* qkv = m->WS<float>(L.qkv);
+  void* qb = m->WS(L.q);
+  void* ob = m->WS(L.o);
+  void* mb = m->WS(L.m);
+  float* part = m->WS<float>(L.partials);
+  uint32_t* cnt = m->WS<uint32_t>(L.counters);
+  const float* cos_t = m->W<float>(m->wl.cos_t);
+  const float* sin_t = m->W<float>(m->wl.sin_t);
+  RowMap all;
+  all.n = -1;
+  const bool bf = c.dtype == Q3_BF16;
+  int splits = 1;
+  if (decode && bf) {
+    int64_t maxcap = 1;
+    for (int b = 0; b < sb.n; ++b) maxcap = std::max(maxcap, m->slots[sb.slot[b]].cap);
+    splits = decode_attn_splits(sb.n, c.n_kv_heads, std::min<int64_t>(maxcap, c.max_positions));
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& lw = m->wl.layers[l];
+    // Paso 3 + Paso 5: normalised input, fused q/k/v projection.
+    LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
+    if (!bf) {
+      LAUNCH(gemv_f32(EPI_STORE, (const float*)h, T, m->W<float>(lw.qkv), NQKV, H, qkv, NQKV, s));
+    } else if (decode) {
+      LAUNCH(skinny_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, part, cnt,
+                         nullptr, nullptr, skinny_plan(EPI_STORE, T, NQKV, H), s));
+    } else {
+      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, s));
+    }
+    // QK-Norm, RoPE, cache append (Pasos 4-5).
+    LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
+                       m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s));
+    // Attention (Paso 5).
+    if (!bf) {
+      LAUNCH(attn_f32((const float*)qb, T, sb, m->state(), (const float*)m->kv, l, c.n_q_heads, c.n_kv_heads,
+                      (float*)ob, s));
+    } else if (decode) {
+      LAUNCH(decode_attn((const bf16_t*)qb, sb, m->state(), (const bf16_t*)m->kv, l, c.n_q_heads, c.n_kv_heads,
+                         splits, m->WS<float>(L.attn_part), (bf16_t*)ob, s));
+    } else {
+      LAUNCH(flash_prefill((const bf16_t*)qb, T, sb, m->state(), (const bf16_t*)m->kv, l, c.n_q_heads,
+                           c.n_kv_heads, (bf16_t*)ob, s));
+    }
+    // Output projection + residual (Paso 5 end, Paso 7).
+    if (!bf) {
+      LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
+    } else if (decode) {
+      LAUNCH(skinny_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, part, cnt, nullptr,
+                         nullptr, skinny_plan(EPI_RESADD, T, H, Q), s));
+    } else {
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
+    }
+    // SwiGLU MLP + residual (Paso 6, Paso 7).
+    LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.post_norm), H, c.rms_eps, h, s));
+    if (!bf) {
+      LAUNCH(gemv_f32(EPI_SWIGLU, (const float*)h, T, m->W<float>(lw.gu), 2 * I, H, mb, I, s));
+      LAUNCH(gemv_f32(EPI_RESADD, (const float*)mb, T, m->W<float>(lw.d), H, I, x, H, s));
+    } else if (decode) {
+      LAUNCH(skinny_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, part, cnt,
+                         nullptr, nullptr, skinny_plan(EPI_SWIGLU, T, 2 * I, H), s));
+      LAUNCH(skinny_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, part, cnt, nullptr,
+                         nullptr, skinny_plan(EPI_RESADD, T, H, I), s));
+    } else {
+      LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
+    }
+  }
+  return Q3_OK;
+}
+
+// Final norm + tied lm_head + greedy pick on `rows` rows of x (Paso 8), then
+// the length update of Paso 9.
+q3_status enqueue_head(q3_model* m, const RowMap& rows, int nrows, const SeqBatch& sb, float* d_logits,
+                       int32_t* d_next, hipStream_t s) {
+  const q3_config& c = m->cfg;
+  const WsLayout& L = m->wsl;
+  float* x = m->WS<float>(L.x);
+  void* h = m->WS(L.h);
+  float* logits = d_logits ? d_logits : m->WS<float>(L.logits);
+  LAUNCH(rmsnorm(c.dtype, x, nrows, rows, m->W<float>(m->wl.final_norm), c.hidden, c.rms_eps, h, s));
+  if (c.dtype == Q3_BF16) {
+    SkinnyPlan p = skinny_plan(EPI_ARGMAX, nrows, c.vocab, c.hidden);
+    LAUNCH(skinny_bf16(EPI_ARGMAX, (const bf16_t*)h, nrows, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, logits,
+                       c.vocab, m->WS<float>(L.partials), m->WS<uint32_t>(L.counters), m->WS<float>(L.amax_val),
+                       m->WS<int32_t>(L.amax_idx), p, s));
+    LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), skinny_argmax_blocks(c.vocab, p),
+                         nrows, d_next, sb, m->state(), m->err(), s));
+  } else {
+    LAUNCH(gemv_f32(EPI_STORE, (const float*)h, nrows, m->W<float>(m->wl.embed), c.vocab, c.hidden, logits,
+                    c.vocab, s));
+    RowMap ident;
+    ident.n = nrows;
+    for (int i = 0; i < nrows; ++i) ident.row[i] = i;
+    LAUNCH(argmax_rows(logits, c.vocab, ident, c.vocab, d_next, m->err(), s));
+    LAUNCH(seq_advance(sb, m->state(), s));
+  }
+  return Q3_OK;
+}
+
+q3_status enqueue_decode(q3_model* m, const SeqBatch& sb, const int32_t* d_tokens, float* d_logits,
+                         int32_t* d_next, hipStream_t s) {
+  const q3_config& c = m->cfg;
+  const int B = sb.n;
+  LAUNCH(embed(c.dtype, d_tokens, B, m->W(m->wl.embed), c.vocab, c.hidden, m->WS<float>(m->wsl.x), m->err(), s));
+  q3_status st = enqueue_layers(m, B, sb, true, s);
+  if (st != Q3_OK) return st;
+  RowMap all;
+  all.n = -1;
+  return enqueue_head(m, all, B, sb, d_logits, d_next, s);
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* q3_last_error(void) { return g_err.c_str(); }
+
+size_t q3_weights_bytes(const q3_config* cfg) {
+  if (!valid_config(cfg, nullptr)) return 0;
+  return weight_layout(*cfg).total;
+}
+
+size_t q3_kv_bytes(const q3_config* cfg) {
+  if (!valid_config(cfg, nullptr)) return 0;
+  const int64_t per_tok = (int64_t)cfg->n_layers * 2 * cfg->n_kv_heads * 128 * esz(*cfg);
+  return align_up((size_t)cfg->kv_tokens * per_tok);
+}
+
+size_t q3_workspace_bytes(const q3_config* cfg) {
+  if (!valid_config(cfg, nullptr)) return 0;
+  return ws_layout(*cfg).total;
+}
+
+q3_status q3_create(const q3_config* cfg, q3_model** out) {
+  std::string why;
+  if (!out) return fail(Q3_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!valid_config(cfg, &why)) return fail(Q3_E_UNSUPPORTED, "config: " + why);
+  q3_model* m = new q3_model();
+  m->cfg = *cfg;
+  m->wl = weight_layout(*cfg);
+  m->wsl = ws_layout(*cfg);
+  m->slots.resize(cfg->max_slots);
+  *out = m;
+  g_err.clear();
+  return Q3_OK;
+}
+
+void q3_destroy(q3_model* m) {
+  if (!m) return;
+  m->drop_graphs();
+  delete m;
+}
+
+q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, void* d_kv, size_t kv_bytes,
+                         void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!d_weights || !d_kv || !d_workspace) return fail(Q3_E_ARG, "NULL device region");
+  if (((uintptr_t)d_weights | (uintptr_t)d_kv | (uintptr_t)d_workspace) % kAlign)
+    return fail(Q3_E_ARG, "device regions must be 256-byte aligned");
+  if (weights_bytes < m->wl.total) return fail(Q3_E_ARG, "weights region too small");
+  if (kv_bytes < q3_kv_bytes(&m->cfg)) return fail(Q3_E_ARG, "KV region too small");
+  if (workspace_bytes < m->wsl.total) return fail(Q3_E_ARG, "workspace region too small");
+  hipStream_t s = (hipStream_t)stream;
+  m->drop_graphs();
+  m->w = (char*)d_weights;
+  m->kv = (char*)d_kv;
+  m->kv_bytes = kv_bytes;
+  m->ws = (char*)d_workspace;
+  m->loaded = false;
+  m->kv_used = 0;
+  for (auto& sl : m->slots) sl = HostSlot();
+  // RoPE table: angle(p, i) = p * theta^(-i/64), evaluated in float64 (Paso 4).
+  const q3_config& c = m->cfg;
+  std::vector<float> cs((size_t)c.max_positions * 64), sn((size_t)c.max_positions * 64);
+  for (int64_t p = 0; p < c.max_positions; ++p)
+    for (int i = 0; i < 64; ++i) {
+      const double a = (double)p * std::pow(c.rope_theta, -(double)i / 64.0);
+      cs[p * 64 + i] = (float)std::cos(a);
+      sn[p * 64 + i] = (float)std::sin(a);
+    }
+  HIP_TRY(hipMemcpyAsync(m->W(m->wl.cos_t), cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(m->W(m->wl.sin_t), sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s));
+  std::vector<SeqState> zero(c.max_slots, SeqState{0, 0, 0});
+  HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
+  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.counters), 0u, m->wsl.n_counters, s));
+  HIP_TRY(fill_u32(m->err(), 0u, 4, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  m->bound = true;
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_load_weights(q3_model* m, const q3_tensor* t, int32_t n, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  if (!t || n <= 0) return fail(Q3_E_ARG, "no tensors");
+  const q3_config& c = m->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t H = c.hidden, Q = (int64_t)c.n_q_heads * 128, KVW = (int64_t)c.n_kv_heads * 128, I = c.ffn;
+  const size_t e = esz(c);
+  m->loaded = false;
+  m->drop_graphs();
+  std::map<std::string, int> seen;
+  // Validate everything before the first copy.
+  struct Job { int idx; std::string kind; int layer; };
+  std::vector<Job> jobs;
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name || !t[i].data) return fail(Q3_E_ARG, "tensor with NULL name or data");
+    const std::string name = t[i].name;
+    if (seen.count(name)) return fail(Q3_E_ARG, "duplicate tensor " + name);
+    seen[name] = i;
+    if (t[i].dtype != c.dtype) return fail(Q3_E_ARG, name + ": dtype differs from the model's");
+    int64_t r = -1, k = -1;
+    std::string kind;
+    int layer = -1;
+    if (name == "model.embed_tokens.weight") { kind = "embed"; r = c.vocab; k = H; }
+    else if (name == "model.norm.weight") { kind = "final_norm"; r = H; }
+    else {
+      int li = -1;
+      char rest[128] = {0};
+      if (std::sscanf(name.c_str(), "model.layers.%d.%127s", &li, rest) != 2 || li < 0 || li >= c.n_layers)
+        return fail(Q3_E_ARG, "unknown tensor " + name);
+      layer = li;
+      const std::string tail = rest;
+      if (tail == "self_attn.q_proj.weight") { kind = "q"; r = Q; k = H; }
+      else if (tail == "self_attn.k_proj.weight") { kind = "k"; r = KVW; k = H; }
+      else if (tail == "self_attn.v_proj.weight") { kind = "v"; r = KVW; k = H; }
+      else if (tail == "self_attn.o_proj.weight") { kind = "o"; r = H; k = Q; }
+      else if (tail == "self_attn.q_norm.weight") { kind = "qn"; r = 128; }
+      else if (tail == "self_attn.k_norm.weight") { kind = "kn"; r = 128; }
+      else if (tail == "input_layernorm.weight") { kind = "in"; r = H; }
+      else if (tail == "post_attention_layernorm.weight") { kind = "post"; r = H; }
+      else if (tail == "mlp.gate_proj.weight") { kind = "gate"; r = I; k = H; }
+      else if (tail == "mlp.up_proj.weight") { kind = "up"; r = I; k = H; }
+      else if (tail == "mlp.down_proj.weight") { kind = "down"; r = H; k = I; }
+      else return fail(Q3_E_ARG, "unknown tensor " + name);
+    }
+    const bool ok = (k < 0) ? (t[i].ndim == 1 && t[i].shape[0] == r)
+                            : (t[i].ndim == 2 && t[i].shape[0] == r && t[i].shape[1] == k);
+    if (!ok) return fail(Q3_E_ARG, name + ": wrong shape");
+    jobs.push_back({i, kind, layer});
+  }
+  const size_t expect = 2 + (size_t)c.n_layers * 11;
+  if (jobs.size() != expect) return fail(Q3_E_ARG, "expected " + std::to_string(expect) + " tensors");
+  for (const Job& j : jobs) {
+    const q3_tensor& tt = t[j.idx];
+    const char* src = (const char*)tt.data;
+    auto copy = [&](size_t dst_off, size_t bytes) {
+      return hipMemcpyAsync(m->W(dst_off), src, bytes, hipMemcpyDefault, s);
+    };
+    auto norm = [&](size_t dst_off, int64_t len) {
+      if (c.dtype == Q3_BF16) return widen_bf16((const bf16_t*)src, m->W<float>(dst_off), len, s);
+      return hipMemcpyAsync(m->W(dst_off), src, len * 4, hipMemcpyDefault, s);
+    };
+    hipError_t err = hipSuccess;
+    if (j.kind == "embed") err = copy(m->wl.embed, (size_t)c.vocab * H * e);
+    else if (j.kind == "final_norm") err = norm(m->wl.final_norm, H);
+    else {
+      const LayerW& lw = m->wl.layers[j.layer];
+      if (j.kind == "q") err = copy(lw.qkv, Q * H * e);
+      else if (j.kind == "k") err = copy(lw.qkv + Q * H * e, KVW * H * e);
+      else if (j.kind == "v") err = copy(lw.qkv + (Q + KVW) * H * e, KVW * H * e);
+      else if (j.kind == "o") err = copy(lw.o, H * Q * e);
+      else if (j.kind == "down") err = copy(lw.d, H * I * e);
+      else if (j.kind == "gate" || j.kind == "up") {
+        // runs of 16 rows: [gate 16 | up 16] [gate 16 | up 16] ...
+        const size_t run = 16 * H * e;
+        const size_t dst = lw.gu + (j.kind == "up" ? run : 0);
+        err = hipMemcpy2DAsync(m->W(dst), 2 * run, src, run, run, I / 16, hipMemcpyDefault, s);
+      }
+      else if (j.kind == "qn") err = norm(lw.qn, 128);
+      else if (j.kind == "kn") err = norm(lw.kn, 128);
+      else if (j.kind == "in") err = norm(lw.in_norm, H);
+      else if (j.kind == "post") err = norm(lw.post_norm, H);
+    }
+    if (err != hipSuccess) return fail(Q3_E_HIP, std::string("weight copy: ") + hipGetErrorString(err));
+  }
+  HIP_TRY(hipStreamSynchronize(s));
+  m->loaded = true;
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_seq_alloc(q3_model* m, int32_t slot, int64_t capacity, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  if (slot < 0 || slot >= m->cfg.max_slots) return fail(Q3_E_ARG, "slot out of range");
+  if (m->slots[slot].allocated) return fail(Q3_E_STATE, "slot already allocated");
+  if (capacity <= 0) return fail(Q3_E_ARG, "capacity must be > 0");
+  const int64_t cap = (capacity + 63) / 64 * 64;
+  if (cap > (int64_t)1 << 30) return fail(Q3_E_UNSUPPORTED, "capacity too large");
+  const int64_t per_tok = (int64_t)m->cfg.n_layers * 2 * m->cfg.n_kv_heads * 128;
+  const int64_t need = cap * per_tok;
+  const int64_t total = (int64_t)(m->kv_bytes / esz(m->cfg));
+  if (m->kv_used + need > total) return fail(Q3_E_CAPACITY, "KV arena full");
+  HostSlot& h = m->slots[slot];
+  h.allocated = true;
+  h.base = m->kv_used;
+  h.cap = cap;
+  h.len = 0;
+  m->kv_used += need;
+  m->drop_graphs();
+  q3_status st = upload_state(m, slot, (hipStream_t)stream);
+  if (st != Q3_OK) return st;
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_seq_reset(q3_model* m, int32_t n, const int32_t* slots, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  if (n < 0 || (n > 0 && !slots)) return fail(Q3_E_ARG, "bad slot list");
+  for (int i = 0; i < n; ++i)
+    if (slots[i] < 0 || slots[i] >= m->cfg.max_slots) return fail(Q3_E_ARG, "slot out of range");
+  for (int i = 0; i < n; ++i) {
+    m->slots[slots[i]].len = 0;
+    q3_status st = upload_state(m, slots[i], (hipStream_t)stream);
+    if (st != Q3_OK) return st;
+  }
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_kv_reset(q3_model* m, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  m->drop_graphs();
+  m->kv_used = 0;
+  for (int i = 0; i < m->cfg.max_slots; ++i) {
+    m->slots[i] = HostSlot();
+  }
+  std::vector<SeqState> zero(m->cfg.max_slots, SeqState{0, 0, 0});
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_seq_length(const q3_model* m, int32_t slot, int64_t* out) {
+  if (!m || !out) return fail(Q3_E_ARG, "NULL argument");
+  if (slot < 0 || slot >= m->cfg.max_slots) return fail(Q3_E_ARG, "slot out of range");
+  *out = m->slots[slot].len;
+  return Q3_OK;
+}
+
+q3_status q3_set_option(q3_model* m, int32_t option, int64_t value) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (option == Q3_OPT_DECODE_GRAPH) {
+    m->use_graph = value != 0;
+    if (!m->use_graph) m->drop_graphs();
+    return Q3_OK;
+  }
+  return fail(Q3_E_ARG, "unknown option");
+}
+
+q3_status q3_error_flags(q3_model* m, uint32_t* out, void* stream) {
+  if (!m || !out) return fail(Q3_E_ARG, "NULL argument");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipMemcpy(out, m->err(), 4, hipMemcpyDeviceToHost));
+  HIP_TRY(fill_u32(m->err(), 0u, 1, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return Q3_OK;
+}
+
+static q3_status check_slots(q3_model* m, int32_t n, const int32_t* slots) {
+  if (n < 1 || n > Q3_MAX_BATCH) return fail(Q3_E_ARG, "n_seqs must be in [1, 64]");
+  if (!slots) return fail(Q3_E_ARG, "slots is NULL");
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= m->cfg.max_slots) return fail(Q3_E_ARG, "slot out of range");
+    if (!m->slots[slots[i]].allocated) return fail(Q3_E_STATE, "slot not allocated");
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i]) return fail(Q3_E_ARG, "a slot appears twice");
+  }
+  return Q3_OK;
+}
+
+q3_status q3_prefill(q3_model* m, int32_t n, const int32_t* h_slots, const int32_t* h_cu,
+                     const int32_t* d_tokens, float* d_logits, int32_t* d_next, uint32_t flags,
+                     void* stream) {
+  q3_status st;
+  if (!ready(m, &st)) return st;
+  if ((st = check_slots(m, n, h_slots)) != Q3_OK) return st;
+  if (!h_cu || !d_tokens || !d_next) return fail(Q3_E_ARG, "NULL cu_seqlens, tokens or next");
+  const bool all = (flags & Q3_PREFILL_ALL_LOGITS) != 0;
+  if (flags & ~Q3_PREFILL_ALL_LOGITS) return fail(Q3_E_ARG, "unknown flag");
+  if (all && !d_logits) return fail(Q3_E_ARG, "Q3_PREFILL_ALL_LOGITS needs d_logits");
+  if (h_cu[0] != 0) return fail(Q3_E_ARG, "cu_seqlens[0] must be 0");
+  for (int b = 0; b < n; ++b) {
+    const int64_t L = (int64_t)h_cu[b + 1] - h_cu[b];
+    if (L < 1) return fail(Q3_E_ARG, "every sequence needs at least one token");
+    const HostSlot& hs = m->slots[h_slots[b]];
+    if (hs.len != 0) return fail(Q3_E_STATE, "prefill needs an empty slot");
+    if (L > hs.cap) return fail(Q3_E_CAPACITY, "KV cache full: prompt longer than the slot");
+    if (L > m->cfg.max_positions) return fail(Q3_E_CAPACITY, "prompt longer than max_positions");
+  }
+  const int64_t T = h_cu[n];
+  if (T > m->cfg.max_prefill_tokens) return fail(Q3_E_CAPACITY, "more tokens than max_prefill_tokens");
+  const q3_config& c = m->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  SeqBatch sb;
+  std::memset(&sb, 0, sizeof(sb));
+  sb.n = n;
+  sb.decode = 0;
+  for (int b = 0; b < n; ++b) sb.slot[b] = h_slots[b];
+  for (int b = 0; b <= n; ++b) sb.cu[b] = h_cu[b];
+
+  LAUNCH(embed(c.dtype, d_tokens, (int)T, m->W(m->wl.embed), c.vocab, c.hidden, m->WS<float>(m->wsl.x), m->err(), s));
+  st = enqueue_layers(m, (int)T, sb, false, s);
+  if (st != Q3_OK) return st;
+  RowMap last;
+  last.n = n;
+  for (int b = 0; b < n; ++b) last.row[b] = h_cu[b + 1] - 1;
+  if (!all) {
+    st = enqueue_head(m, last, n, sb, d_logits, d_next, s);
+    if (st != Q3_OK) return st;
+  } else {
+    // Every position's logits (Paso 8 as printed computes all rows).
+    RowMap every;
+    every.n = -1;
+    void* h = m->WS(m->wsl.h);
+    LAUNCH(rmsnorm(c.dtype, m->WS<float>(m->wsl.x), (int)T, every, m->W<float>(m->wl.final_norm), c.hidden,
+                   c.rms_eps, h, s));
+    if (c.dtype == Q3_BF16)
+      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, (int)T, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, d_logits,
+                       c.vocab, s));
+    else
+      LAUNCH(gemv_f32(EPI_STORE, (const float*)h, (int)T, m->W<float>(m->wl.embed), c.vocab, c.hidden, d_logits,
+                      c.vocab, s));
+    LAUNCH(argmax_rows(d_logits, c.vocab, last, c.vocab, d_next, m->err(), s));
+    LAUNCH(seq_advance(sb, m->state(), s));
+  }
+  for (int b = 0; b < n; ++b) m->slots[h_slots[b]].len = h_cu[b + 1] - h_cu[b];
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_decode_step(q3_model* m, int32_t n, const int32_t* h_slots, const int32_t* d_tokens,
+                         float* d_logits, int32_t* d_next, void* stream) {
+  q3_status st;
+  if (!ready(m, &st)) return st;
+  if ((st = check_slots(m, n, h_slots)) != Q3_OK) return st;
+  if (!d_tokens || !d_next) return fail(Q3_E_ARG, "NULL tokens or next");
+  for (int b = 0; b < n; ++b) {
+    const HostSlot& hs = m->slots[h_slots[b]];
+    if (hs.len + 1 > hs.cap) return fail(Q3_E_CAPACITY, "KV cache full");
+    if (hs.len + 1 > m->cfg.max_positions) return fail(Q3_E_CAPACITY, "sequence reached max_positions");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  SeqBatch sb;
+  std::memset(&sb, 0, sizeof(sb));
+  sb.n = n;
+  sb.decode = 1;
+  for (int b = 0; b < n; ++b) {
+    sb.slot[b] = h_slots[b];
+    sb.cu[b] = b;
+  }
+  sb.cu[n] = n;
+
+  if (m->use_graph && s != nullptr) {
+    GraphKey key{std::vector<int32_t>(h_slots, h_slots + n), d_tokens, d_logits, d_next, stream};
+    auto it = m->graphs.find(key);
+    if (it == m->graphs.end()) {
+      if (m->graphs.size() >= 64) m->drop_graphs();  // bound the cache of recorded steps
+      HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+      st = enqueue_decode(m, sb, d_tokens, d_logits, d_next, s);
+      hipGraph_t g = nullptr;
+      hipError_t ec = hipStreamEndCapture(s, &g);
+      if (st != Q3_OK) {
+        if (g) hipGraphDestroy(g);
+        return st;
+      }
+      if (ec != hipSuccess) return fail(Q3_E_HIP, std::string("graph capture: ") + hipGetErrorString(ec));
+      hipGraphExec_t ge = nullptr;
+      hipError_t ei = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+      hipGraphDestroy(g);
+      if (ei != hipSuccess) return fail(Q3_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(ei));
+      it = m->graphs.emplace(key, ge).first;
+    }
+    HIP_TRY(hipGraphLaunch(it->second, s));
+  } else {
+    st = enqueue_decode(m, sb, d_tokens, d_logits, d_next, s);
+    if (st != Q3_OK) return st;
+  }
+  for (int b = 0; b < n; ++b) m->slots[h_slots[b]].len += 1;
+  g_err.clear();
+  return Q3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+/*
+ * q3_ops.h -- single-kernel entry points of libq3, for parity tests and
+ * kernel benchmarks.  Each runs one step of the forward pass of "Dentro de un
+ * LLM: Inferencia en Python puro para Qwen3-0.6B en MLX" on explicit device
+ * buffers, with the same kernels q3_prefill / q3_decode_step use.
+ *
+ * Conventions are those of q3.h: d_* pointers are device memory, the others
+ * host memory; `stream` is a hipStream_t as void*; status codes and
+ * q3_last_error() report failures.  No call allocates device memory: kernels
+ * that need scratch take `d_ws` of at least the size the matching
+ * *_workspace_bytes call returns.  Unlike the model calls, these synchronise
+ * the stream after host-to-device copies of small tables (test use only).
+ *
+ * bf16 data is passed as its 16-bit patterns.
+ */
+#ifndef Q3_OPS_H
+#define Q3_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "q3.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Paso 2: d_out[r][:] = table[ids[r]][:] as float32 (table dtype = dtype).
+ * An ID outside [0, vocab) gives a zero row and sets bit 1 of *d_err. */
+q3_status q3op_embed(int32_t dtype, const int32_t* d_ids, int32_t n, const void* d_table, int32_t vocab,
+                     int32_t dim, float* d_out, uint32_t* d_err, void* stream);
+
+/* Paso 3: d_out[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * w, rows of `dim`
+ * (a multiple of 256) float32 values; output float32 or bf16 (out_dtype). */
+q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const float* d_w, int32_t dim,
+                       float eps, void* d_out, void* stream);
+
+/* Projection kernels: out = X[M,K] . W[N,K]^T with epilogue `epi`:
+ *   0 store float32 out[M][ldo]; 1 add into float32 out[M][ldo];
+ *   2 SwiGLU: W rows packed in runs of 16 gate rows then 16 up rows,
+ *     out[m][j] = silu(gate_j) * up_j written in X's dtype (ldo >= N/2);
+ *   3 logits: store float32 out[M][ldo] and d_next[m] = argmax (lowest index
+ *     on ties).
+ * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0);
+ * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
+ * kernel 2 = float32 GEMV (float32 model).  bf16 kernels take bf16 X and W. */
+#define Q3OP_GEMM 0
+#define Q3OP_SKINNY 1
+#define Q3OP_GEMV_F32 2
+size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K);
+q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
+                      int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
+                      void* stream);
+
+/* A one-layer KV arena for the attention ops: sequence b owns the elements
+ * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):
+ * keys [n_kv][cap][128] then values transposed [n_kv][128][cap]; h_cap[b] is
+ * a multiple of 64.  h_len[b] = tokens already cached before the call.
+ *
+ * Pasos 4-5: per-head RMSNorm (q_norm / k_norm) then rotate-half RoPE at each
+ * token's position, queries to d_q_out [T][n_q][128], keys and values into the
+ * arena.  Rows of d_qkv [T][(n_q + 2 n_kv)*128] float32 hold q, k, v heads.
+ * decode = 0: tokens h_cu[b]..h_cu[b+1] of sequence b sit at positions 0..;
+ * decode = 1: token b sits at position h_len[b]. */
+size_t q3op_rope_workspace_bytes(int32_t n_seqs, int32_t max_pos);
+q3_status q3op_rope_append(int32_t dtype, const float* d_qkv, int32_t n_seqs, const int32_t* h_cu,
+                           int32_t decode, const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len,
+                           void* d_kv, int32_t n_q, int32_t n_kv, const float* d_qn, const float* d_kn,
+                           float eps, double theta, int32_t max_pos, void* d_q_out, void* d_ws,
+                           size_t ws_bytes, void* stream);
+
+/* Paso 5 attention over the arena above, output [T][n_q][128] in dtype.
+ * kernel 0 = bf16 flash prefill (decode must be 0: query t of sequence b at
+ * position t - h_cu[b], keys 0..L_b-1 of that sequence);
+ * kernel 1 = bf16 split-K decode (decode must be 1: query b at position
+ * h_len[b], keys 0..h_len[b]); `splits` <= 0 picks the library's choice;
+ * kernel 2 = float32 (either mode). */
+#define Q3OP_ATTN_FLASH 0
+#define Q3OP_ATTN_DECODE 1
+#define Q3OP_ATTN_F32 2
+size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t n_q, int32_t splits);
+q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n_seqs, const int32_t* h_cu, int32_t decode,
+                         const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len, const void* d_kv,
+                         int32_t n_q, int32_t n_kv, int32_t splits, void* d_out, void* d_ws, size_t ws_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q3_OPS_H */

@@ -1,0 +1,61 @@
+"""Shared helpers for the GPU parity tests (HIP path vs the CPU oracle)."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import q3synth
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max |gpu - ref| / RMS(ref): the logits error measure of the parity bar."""
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(np.asarray(gpu, dtype=np.float64) - ref)) / rms)
+
+
+def margin_ok(ref_logits: np.ndarray, gpu_token: int, tol_abs: float) -> bool:
+    """True when the GPU's token is the oracle's argmax, or within tol_abs of it (a near-tie)."""
+    top = int(np.argmax(ref_logits))
+    if gpu_token == top:
+        return True
+    return float(ref_logits[top] - ref_logits[gpu_token]) <= tol_abs
+
+
+@functools.lru_cache(maxsize=4)
+def weights_for(dims: q3synth.ModelDims, seed: int):
+    return q3synth.make_weights(dims, seed)
+
+
+# ---------------------------------------------------------------- device marshalling
+def dev_bf16(a: np.ndarray):
+    """bf16-valued float32 array -> torch int16 tensor of its bit patterns on cuda:0."""
+    import torch
+    bits = q3synth.bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).to("cuda:0")
+
+
+def host_bf16(t) -> np.ndarray:
+    """torch int16 tensor of bf16 bit patterns -> float32 numpy array."""
+    bits = t.cpu().numpy().view(np.uint16).astype(np.uint32) << 16
+    return bits.view(np.float32)
+
+
+def dev_f32(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def rand_bf16(rng, shape, scale=1.0) -> np.ndarray:
+    return q3synth.round_to_bf16((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def ops():
+    from decoder_only_qwen3_amd import _lib
+    return _lib, _lib.load()
+
+
+def call(status):
+    from decoder_only_qwen3_amd import _lib
+    _lib.check(status)

@@ -1,0 +1,356 @@
+"""Kernel-level parity: each libq3 kernel (through include/q3_ops.h) against
+the matching oracle function on seeded random inputs, at sizes that span
+several tiles and a ragged tail."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import q3synth
+from gpu_helpers import call, dev_bf16, dev_f32, host_bf16, ops, rand_bf16
+from oracle import attention_rows, rms_norm, rope_cos_sin, rope_rotate, silu, to_bf16
+
+pytestmark = pytest.mark.gpu
+
+EPI_STORE, EPI_RESADD, EPI_SWIGLU, EPI_ARGMAX = 0, 1, 2, 3
+GEMM, SKINNY, GEMV_F32 = 0, 1, 2
+BF16, F32 = 1, 0
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _ws(nbytes):
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda:0")
+
+
+# ---------------------------------------------------------------- Paso 2 / Paso 3
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_embed_gather_and_bad_id(dtype):
+    mod, lib = ops()
+    rng = np.random.default_rng(1)
+    V, H = 1000, 256
+    table = rand_bf16(rng, (V, H)) if dtype == BF16 else rng.standard_normal((V, H)).astype(np.float32)
+    ids = np.array([0, 999, 5, 5, 1000, -1, 17], dtype=np.int32)
+    dt = dev_bf16(table) if dtype == BF16 else dev_f32(table)
+    di = torch.from_numpy(ids).to("cuda:0")
+    out = torch.empty((len(ids), H), dtype=torch.float32, device="cuda:0")
+    err = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    call(lib.q3op_embed(dtype, di.data_ptr(), len(ids), dt.data_ptr(), V, H, out.data_ptr(), err.data_ptr(), None))
+    _sync()
+    got = out.cpu().numpy()
+    for r, t in enumerate(ids):
+        expect = table[t] if 0 <= t < V else np.zeros(H, np.float32)
+        np.testing.assert_array_equal(got[r], expect)
+    assert int(err[0].item()) & 1
+
+
+@pytest.mark.parametrize("rows", [1, 5, 67])
+@pytest.mark.parametrize("out_dtype", [F32, BF16])
+def test_rmsnorm(rows, out_dtype):
+    mod, lib = ops()
+    rng = np.random.default_rng(rows)
+    H = 1024
+    x = (rng.standard_normal((rows, H)) * rng.uniform(0.01, 20, (rows, 1))).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    out = torch.empty((rows, H), dtype=torch.float32 if out_dtype == F32 else torch.int16, device="cuda:0")
+    dx, dw = dev_f32(x), dev_f32(w)   # keep the device copies alive until the kernel ran
+    call(lib.q3op_rmsnorm(out_dtype, dx.data_ptr(), rows, dw.data_ptr(), H, 1e-6, out.data_ptr(), None))
+    _sync()
+    ref = rms_norm(x.astype(np.float64), w.astype(np.float64), 1e-6)
+    if out_dtype == F32:
+        np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=2e-6, atol=1e-6)
+    else:
+        got = host_bf16(out)
+        # same rounding point as the oracle's contract; fp32 vs fp64 may flip a tie by 1 ulp
+        np.testing.assert_allclose(got, to_bf16(ref), rtol=2 ** -7, atol=1e-30)
+        assert np.mean(got == to_bf16(ref)) > 0.99
+
+
+# ---------------------------------------------------------------- projections
+def _pack_gate_up(g, u):
+    I = g.shape[0]
+    out = np.empty((2 * I, g.shape[1]), dtype=g.dtype)
+    for r in range(I // 16):
+        out[32 * r:32 * r + 16] = g[16 * r:16 * r + 16]
+        out[32 * r + 16:32 * r + 32] = u[16 * r:16 * r + 16]
+    return out
+
+
+def _linear(kernel, epi, X, W, out_init=None, ldo=None, want_next=False):
+    mod, lib = ops()
+    M, K = X.shape
+    N = W.shape[0]
+    bf = kernel in (GEMM, SKINNY)
+    dx = dev_bf16(X) if bf else dev_f32(X)
+    dw = dev_bf16(W) if bf else dev_f32(W)
+    if epi == EPI_SWIGLU:
+        ldo = ldo or N // 2
+        out = torch.zeros((M, ldo), dtype=torch.int16 if bf else torch.float32, device="cuda:0")
+    else:
+        ldo = ldo or N
+        out = dev_f32(out_init) if out_init is not None else torch.zeros((M, ldo), dtype=torch.float32, device="cuda:0")
+    nxt = torch.full((max(M, 1),), -7, dtype=torch.int32, device="cuda:0")
+    ws = _ws(lib.q3op_linear_workspace_bytes(kernel, epi, M, N, K))
+    call(lib.q3op_linear(kernel, epi, dx.data_ptr(), M, dw.data_ptr(), N, K, out.data_ptr(), ldo,
+                         nxt.data_ptr() if want_next else None, ws.data_ptr(), ws.numel(), None))
+    _sync()
+    got = host_bf16(out) if (epi == EPI_SWIGLU and bf) else out.cpu().numpy()
+    return got, nxt.cpu().numpy()
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
+
+
+@pytest.mark.parametrize("kernel,M", [(GEMM, 1), (GEMM, 5), (GEMM, 130), (GEMM, 257),
+                                      (SKINNY, 1), (SKINNY, 3), (SKINNY, 16), (SKINNY, 17), (SKINNY, 64)])
+@pytest.mark.parametrize("N,K", [(4096, 1024), (1024, 2048), (1024, 3072)])
+def test_linear_store_and_residual(kernel, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    X = rand_bf16(rng, (M, K))
+    W = rand_bf16(rng, (N, K), 0.02)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    got, _ = _linear(kernel, EPI_STORE, X, W)
+    assert _rel(got, ref) < 2e-5
+    base = rng.standard_normal((M, N)).astype(np.float32)
+    got, _ = _linear(kernel, EPI_RESADD, X, W, out_init=base)
+    assert _rel(got - base, ref) < 2e-5
+
+
+@pytest.mark.parametrize("kernel,M", [(GEMM, 3), (GEMM, 200), (SKINNY, 1), (SKINNY, 40), (GEMV_F32, 6)])
+def test_linear_swiglu(kernel, M):
+    rng = np.random.default_rng(M)
+    I, H = 3072, 1024
+    bf = kernel != GEMV_F32
+    mk = (lambda s, sc=1.0: rand_bf16(rng, s, sc)) if bf else (lambda s, sc=1.0: (rng.standard_normal(s) * sc).astype(np.float32))
+    X = mk((M, H))
+    G, U = mk((I, H), 0.05), mk((I, H), 0.05)
+    got, _ = _linear(kernel, EPI_SWIGLU, X, _pack_gate_up(G, U))
+    g = X.astype(np.float64) @ G.astype(np.float64).T
+    u = X.astype(np.float64) @ U.astype(np.float64).T
+    ref = silu(g) * u
+    if bf:
+        # one bf16 rounding of the product: at most one ulp (2^-7 relative) apart
+        np.testing.assert_allclose(got, to_bf16(ref), rtol=2 ** -7, atol=1e-6)
+        assert np.mean(got == to_bf16(ref)) > 0.99
+    else:
+        assert _rel(got, ref) < 1e-5
+
+
+@pytest.mark.parametrize("M", [1, 2, 9])
+def test_gemv_f32_store_and_residual(M):
+    rng = np.random.default_rng(100 + M)
+    X = rng.standard_normal((M, 1024)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((2048, 1024))).astype(np.float32)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    got, _ = _linear(GEMV_F32, EPI_STORE, X, W)
+    assert _rel(got, ref) < 1e-5
+    base = rng.standard_normal((M, 2048)).astype(np.float32)
+    got, _ = _linear(GEMV_F32, EPI_RESADD, X, W, out_init=base)
+    assert _rel(got - base, ref) < 1e-5
+
+
+@pytest.mark.parametrize("kernel,M", [(SKINNY, 1), (SKINNY, 7), (SKINNY, 64), (GEMM, 3), (GEMV_F32, 2)])
+def test_logits_and_argmax(kernel, M):
+    rng = np.random.default_rng(300 + M)
+    V, H = 8192, 1024
+    bf = kernel != GEMV_F32
+    X = rand_bf16(rng, (M, H)) if bf else rng.standard_normal((M, H)).astype(np.float32)
+    E = rand_bf16(rng, (V, H), 0.02) if bf else (0.02 * rng.standard_normal((V, H))).astype(np.float32)
+    # plant exact ties: row 4100 duplicates row 4000, row 100 gets the winner's values too
+    ref = X.astype(np.float64) @ E.astype(np.float64).T
+    win = int(np.argmax(ref[0]))
+    E[4100] = E[win]
+    E[win + 1 if win + 1 < V else 0] = E[win]
+    ref = X.astype(np.float64) @ E.astype(np.float64).T
+    got, nxt = _linear(kernel, EPI_ARGMAX, X, E, want_next=True)
+    assert _rel(got, ref) < 2e-5
+    for m in range(M):
+        # argmax of the kernel's own logits with lowest-index ties
+        assert nxt[m] == int(np.argmax(got[m]))
+        top = int(np.argmax(ref[m]))
+        assert ref[m][top] - ref[m][nxt[m]] <= 1e-5 * np.sqrt(np.mean(ref[m] ** 2))
+
+
+# ---------------------------------------------------------------- Pasos 4-5: QK-Norm, RoPE, cache append
+def _arena(lens_cap, n_kv, esz):
+    bases, off = [], 0
+    for cap in lens_cap:
+        bases.append(off)
+        off += 2 * n_kv * cap * 128
+    return bases, off
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+@pytest.mark.parametrize("decode", [0, 1])
+def test_rope_append(dtype, decode):
+    mod, lib = ops()
+    rng = np.random.default_rng(5 + decode)
+    n_q, n_kv = 16, 8
+    if decode:
+        lens = [1, 1, 1]
+        cu = [0, 1, 2, 3]
+        prior = [0, 70, 4000]
+    else:
+        lens = [3, 64, 130]
+        cu = list(np.concatenate([[0], np.cumsum(lens)]))
+        prior = [0, 0, 0]
+    caps = [4096, 128, 4096]
+    T = cu[-1]
+    units = n_q + 2 * n_kv
+    qkv = rng.standard_normal((T, units * 128)).astype(np.float32)
+    qn = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    kn = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    if dtype == BF16:
+        qn, kn = q3synth.round_to_bf16(qn), q3synth.round_to_bf16(kn)
+    bases, total = _arena(caps, n_kv, 2 if dtype == BF16 else 4)
+    kv = torch.zeros(total, dtype=torch.int16 if dtype == BF16 else torch.float32, device="cuda:0")
+    qout = torch.zeros((T, n_q, 128), dtype=torch.int16 if dtype == BF16 else torch.float32, device="cuda:0")
+    max_pos = 4100
+    ws = _ws(lib.q3op_rope_workspace_bytes(len(lens), max_pos))
+    dqkv, dqn, dkn = dev_f32(qkv), dev_f32(qn), dev_f32(kn)
+    call(lib.q3op_rope_append(dtype, dqkv.data_ptr(), len(lens), mod.i32_array(cu), decode,
+                              mod.i64_array(bases), mod.i32_array(caps), mod.i32_array(prior), kv.data_ptr(),
+                              n_q, n_kv, dqn.data_ptr(), dkn.data_ptr(), 1e-6, 1e6, max_pos,
+                              qout.data_ptr(), ws.data_ptr(), ws.numel(), None))
+    _sync()
+    rnd = to_bf16 if dtype == BF16 else (lambda a: a)
+    read = host_bf16 if dtype == BF16 else (lambda t: t.cpu().numpy())
+    q_got = read(qout).reshape(T, n_q, 128)
+    kv_got = read(kv)
+    tol = dict(rtol=2 ** -7, atol=1e-6) if dtype == BF16 else dict(rtol=1e-5, atol=1e-6)
+    for b in range(len(lens)):
+        rows = slice(cu[b], cu[b + 1])
+        pos = (np.arange(lens[b]) if not decode else np.array([prior[b]]))
+        x = qkv[rows].astype(np.float64).reshape(-1, units, 128)
+        c, s = rope_cos_sin(pos, 128, 1e6)
+        q_ref = rnd(rope_rotate(rms_norm(x[:, :n_q], qn, 1e-6), c, s))
+        k_ref = rnd(rope_rotate(rms_norm(x[:, n_q:n_q + n_kv], kn, 1e-6), c, s))
+        v_ref = rnd(x[:, n_q + n_kv:])
+        np.testing.assert_allclose(q_got[rows], q_ref, **tol)
+        cap = caps[b]
+        region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
+        K = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        for i, p in enumerate(pos):
+            np.testing.assert_allclose(K[:, p, :], k_ref[i], **tol)
+            np.testing.assert_array_equal(Vt[:, :, p], v_ref[i].astype(np.float32))
+
+
+# ---------------------------------------------------------------- Paso 5: attention
+def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0):
+    mod, lib = ops()
+    rng = np.random.default_rng(seed)
+    decode = kernel == 1 or (kernel == 2 and prior is not None)
+    bf = kernel != 2
+    mk = (lambda s: rand_bf16(rng, s)) if bf else (lambda s: rng.standard_normal(s).astype(np.float32))
+    n = len(lens)
+    if decode:
+        ctx = [p + 1 for p in prior]
+        cu = list(range(n + 1))
+        q = mk((n, n_q, 128))
+    else:
+        ctx = list(lens)
+        prior = [0] * n
+        cu = list(np.concatenate([[0], np.cumsum(lens)]))
+        q = mk((cu[-1], n_q, 128))
+    bases, total = _arena(caps, n_kv, 2 if bf else 4)
+    arena = np.full(total, np.nan if not bf else 0, dtype=np.float32)
+    if bf:
+        arena = np.zeros(total, np.float32)
+        # fill the unused cache area with NaN bit patterns later via torch (garbage must not leak)
+    Ks, Vs = [], []
+    for b in range(n):
+        K = mk((ctx[b], n_kv, 128))
+        V = mk((ctx[b], n_kv, 128))
+        Ks.append(K)
+        Vs.append(V)
+        cap = caps[b]
+        region = np.zeros(2 * n_kv * cap * 128, np.float32)
+        Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        Kc[:, :ctx[b], :] = K.transpose(1, 0, 2)
+        Vt[:, :, :ctx[b]] = V.transpose(1, 2, 0)
+        arena[bases[b]:bases[b] + region.size] = region
+    if bf:
+        bits = q3synth.bf16_bits(arena)
+        # poison every cache slot beyond each sequence's context with NaN
+        for b in range(n):
+            cap = caps[b]
+            reg = bits[bases[b]:bases[b] + 2 * n_kv * cap * 128]
+            Kc = reg[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+            Vt = reg[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+            Kc[:, ctx[b]:, :] = 0x7FC0
+            Vt[:, :, ctx[b]:] = 0x7FC0
+        dkv = torch.from_numpy(bits.view(np.int16)).to("cuda:0")
+        dq = dev_bf16(q)
+        out = torch.zeros((q.shape[0], n_q, 128), dtype=torch.int16, device="cuda:0")
+    else:
+        dkv = dev_f32(arena)
+        dq = dev_f32(q)
+        out = torch.zeros((q.shape[0], n_q, 128), dtype=torch.float32, device="cuda:0")
+    ws = _ws(lib.q3op_attention_workspace_bytes(kernel, n, n_q, splits))
+    call(lib.q3op_attention(kernel, dq.data_ptr(), n, mod.i32_array(cu), 1 if decode else 0,
+                            mod.i64_array(bases), mod.i32_array(caps), mod.i32_array(prior), dkv.data_ptr(),
+                            n_q, n_kv, splits, out.data_ptr(), ws.data_ptr(), ws.numel(), None))
+    _sync()
+    got = host_bf16(out) if bf else out.cpu().numpy()
+    worst = 0.0
+    refs = []
+    for b in range(n):
+        if decode:
+            qb = q[b:b + 1].astype(np.float64)
+            ref = attention_rows(qb, Ks[b].astype(np.float64), Vs[b].astype(np.float64),
+                                 np.array([prior[b]]), np.arange(ctx[b]))
+            g = got[b:b + 1]
+        else:
+            qb = q[cu[b]:cu[b + 1]].astype(np.float64)
+            pos = np.arange(lens[b])
+            ref = attention_rows(qb, Ks[b].astype(np.float64), Vs[b].astype(np.float64), pos, pos)
+            g = got[cu[b]:cu[b + 1]]
+        assert np.all(np.isfinite(g)), f"seq {b}: non-finite output"
+        # Error in units of the allowed bound.  bf16 output: half an ulp of the
+        # stored value (2^-8 relative) plus 2e-3 of the row RMS for the fp16
+        # softmax weights; float32: 1e-5 of the row RMS.
+        rms = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+        bound = (2.0 ** -8 * np.abs(ref) + 2e-3 * rms) if bf else 1e-5 * rms
+        worst = max(worst, float(np.max(np.abs(g - ref) / bound)))
+    return worst
+
+
+@pytest.mark.parametrize("lens", [[1], [5], [64], [65], [130, 1, 63, 200], [513]])
+def test_flash_prefill_attention(lens):
+    caps = [((L + 63) // 64) * 64 for L in lens]
+    worst = _attention_case(0, lens, None, caps, seed=len(lens) + lens[0])
+    assert worst < 1.0, worst
+
+
+def test_flash_prefill_gqa_groups():
+    for n_q, n_kv in [(8, 8), (16, 2), (8, 1)]:
+        worst = _attention_case(0, [70, 9], None, [128, 64], n_q=n_q, n_kv=n_kv, seed=n_kv)
+        assert worst < 1.0, (n_q, n_kv, worst)
+
+
+@pytest.mark.parametrize("prior", [[0], [1], [31], [32], [255, 0, 8319], [32799]])
+def test_decode_attention(prior):
+    caps = [((p + 1 + 63) // 64) * 64 for p in prior]
+    worst = _attention_case(1, [1] * len(prior), prior, caps, seed=prior[0] + 3)
+    assert worst < 1.0, worst
+
+
+def test_decode_attention_split_counts():
+    for splits in (1, 3, 64):
+        worst = _attention_case(1, [1, 1], [700, 40], [768, 64], seed=splits, splits=splits)
+        assert worst < 1.0, (splits, worst)
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_attention_f32(mode):
+    if mode == "prefill":
+        worst = _attention_case(2, [1, 37, 70], None, [64, 64, 128], seed=9)
+    else:
+        worst = _attention_case(2, [1, 1], [0, 300], [64, 320], seed=10)
+    assert worst < 1.0, worst
