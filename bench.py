@@ -1,0 +1,226 @@
+"""Benchmark: prefill + greedy decode of the Qwen3-0.6B-shaped decoder on one MI355X.
+
+One step = one pass of the whole path over one request of the workload:
+reset the slot, prefill the 512-token prompt (embedding, 28 blocks, final norm,
+tied lm_head, argmax), then 256 greedy decode steps, each feeding the previous
+step's device-side token back in and writing logits.  Weights are seeded random
+bf16 (the page's checkpoint is not used); inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line.  `value` is decode tokens/s; prefill tokens/s, the
+whole-step decode HBM fraction, the dominant kernel's roofline and the CPU
+oracle's rate ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="q06b_bf16_p512_d256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    return ap.parse_args()
+
+
+def decode_bytes_per_step(d, ctx):
+    """Algorithmic HBM bytes of one batch-1 decode step at context `ctx` (new token included)."""
+    L, H, Q, KV, I, V = d.n_layers, d.hidden, d.n_q_heads * 128, d.n_kv_heads * 128, d.ffn, d.vocab
+    e = 2 if d.dtype == "bf16" else 4
+    weights = (L * (H * (Q + 2 * KV) + Q * H + 2 * I * H + I * H) + V * H) * e
+    norms = (L * (2 * H + 256) + H) * 4
+    kv_read = ctx * L * 2 * KV * e
+    kv_write = L * 2 * KV * e
+    logits = V * 4
+    return weights + norms + kv_read + kv_write + logits
+
+
+def prefill_flops(d, lens):
+    L, H, Q, KV, I, V = d.n_layers, d.hidden, d.n_q_heads * 128, d.n_kv_heads * 128, d.ffn, d.vocab
+    per_tok = 2 * L * (H * (Q + 2 * KV) + Q * H + 3 * I * H)
+    attn = sum(4 * d.n_q_heads * 128 * L * n * (n + 1) // 2 for n in lens)
+    head = 2 * V * H * len(lens)
+    return per_tok * sum(lens) + attn + head
+
+
+def cpu_baseline(d, w, prompt, seconds_budget=20.0):
+    """Time the CPU oracle (float64 numpy) on a bounded sample: a short prefill, then decode steps."""
+    from oracle import OracleModel
+    cores = len(os.sched_getaffinity(0))
+    m = OracleModel(d, w)
+    n_prompt = 16
+    cache = m.new_cache(n_prompt + 64)
+    t0 = time.perf_counter()
+    lg = m.forward(prompt[:n_prompt], cache)[0]   # also converts the weights to float64 once
+    t1 = time.perf_counter()
+    tok = int(np.argmax(lg))
+    steps, t_dec = 0, 0.0
+    while steps < 64 and (steps < 2 or t_dec < seconds_budget):
+        s0 = time.perf_counter()
+        tok = int(np.argmax(m.forward([tok], cache)[0]))
+        t_dec += time.perf_counter() - s0
+        steps += 1
+    return {"value": steps / t_dec, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle, {d.n_layers} layers: {n_prompt}-token prefill "
+                      f"({t1 - t0:.1f} s incl. one-time float64 weight conversion) then {steps} "
+                      f"greedy decode steps timed ({t_dec:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import q3synth
+    from decoder_only_qwen3_amd import Q3Model, _lib
+
+    wl = q3synth.WORKLOADS[args.workload]
+    d = wl.dims
+    lens = [int(x) for x in wl.prompt_lengths()]
+    steps_dec = wl.decode_steps
+    B = wl.n_seqs
+    t_gen = time.perf_counter()
+    w = q3synth.make_weights(d, wl.seed)
+    prompts = [q3synth.make_tokens(L, d.vocab, wl.seed + 1 + i).tolist() for i, L in enumerate(lens)]
+    t_gen = time.perf_counter() - t_gen
+
+    cap = max(lens) + steps_dec
+    m = Q3Model(d, max_slots=B, max_positions=cap, max_prefill_tokens=sum(lens), kv_tokens=B * ((cap + 63) // 64 * 64))
+    m.load_weights(w)
+    if args.no_graphs:
+        m.set_graphs(False)
+    slots = list(range(B))
+    for s in slots:
+        m.seq_alloc(s, cap)
+    dev = m.device
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    with torch.cuda.stream(m.stream):
+        d_prompt = torch.from_numpy(np.concatenate([np.asarray(p, np.int32) for p in prompts])).to(dev)
+        d_tok = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+        d_logits = torch.empty((B, d.vocab), dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step():
+        m.seq_reset(slots)
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(m.stream)
+        m.prefill_raw(slots, cu, d_prompt, d_logits, d_tok[0])
+        e1.record(m.stream)
+        for i in range(steps_dec):
+            m.decode_raw(slots, d_tok[i % 2], d_logits, d_tok[(i + 1) % 2])
+        e2.record(m.stream)
+        return e0, e1, e2
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    if m.error_flags() != 0:
+        raise RuntimeError("device error flags raised during warmup")
+    marks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        marks.append(one_step())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in marks]
+    dec_ms = [b.elapsed_time(c) for _, b, c in marks]
+    prefill_tok_s = sum(lens) * args.steps / (sum(pre_ms) / 1e3)
+    decode_tok_s = B * steps_dec * args.steps / (sum(dec_ms) / 1e3)
+
+    # Whole-step decode HBM fraction (batch-1 byte count, averaged over the contexts).
+    if B == 1:
+        byts = np.mean([decode_bytes_per_step(d, lens[0] + 1 + i) for i in range(steps_dec)])
+        dec_step_s = (sum(dec_ms) / 1e3) / (args.steps * steps_dec)
+        decode_hbm = {"bytes_per_step": float(byts), "achieved_GBs": byts / dec_step_s / 1e9,
+                      "frac": byts / dec_step_s / 1e9 / HBM_PEAK_GBS}
+    else:
+        decode_hbm = None
+    pf = prefill_flops(d, lens)
+    prefill_mfma = {"flops": pf, "achieved_TFLOPs": pf / (np.mean(pre_ms) / 1e3) / 1e12,
+                    "frac": pf / (np.mean(pre_ms) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    # Dominant kernel: the tied lm_head weight stream (one launch per decode step,
+    # 151936 x 1024 bf16 = 311 MB), timed with HIP events on the model's stream
+    # over repeated launches of the same kernel on the model's own embedding table.
+    lib = _lib.load()
+    M = B
+    N, K = d.vocab, d.hidden
+    with torch.cuda.stream(m.stream):
+        x = torch.zeros((M, K), dtype=torch.int16, device=dev)
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        nxt = torch.empty(M, dtype=torch.int32, device=dev)
+        wsb = lib.q3op_linear_workspace_bytes(1, 3, M, N, K)
+        ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)
+    embed_ptr = m.bufs[0].data_ptr()  # the embedding table sits at offset 0 of the weight region
+    # d_next = NULL: only the lm_head kernel itself (logits + per-block partials) is launched
+    for _ in range(3):
+        _lib.check(lib.q3op_linear(1, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
+                                   ws.data_ptr(), ws.numel(), m.sh))
+    k0, k1 = ev(), ev()
+    k0.record(m.stream)
+    for _ in range(args.kernel_reps):
+        _lib.check(lib.q3op_linear(1, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
+                                   ws.data_ptr(), ws.numel(), m.sh))
+    k1.record(m.stream)
+    torch.cuda.synchronize()
+    per_launch_ms = k0.elapsed_time(k1) / args.kernel_reps
+    alg_bytes = N * K * 2 + M * K * 2 + M * N * 4 + (N // 16) * M * 8
+    achieved = alg_bytes / (per_launch_ms / 1e3) / 1e9
+
+    line = {
+        "metric": "decode tok/s + prefill tok/s (1 GPU) and % of HBM / bf16-MFMA roofline",
+        "value": round(decode_tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if d.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,0.02) weights (norms 1+N(0,0.1)), uniform random token IDs",
+        "config": {"workload": wl.name, "n_layers": d.n_layers, "n_seqs": B, "prompt_tokens": lens if B <= 4 else sum(lens),
+                   "decode_steps": steps_dec, "graphs": not args.no_graphs},
+        "prefill_tok_s": round(prefill_tok_s, 1),
+        "decode_tok_s": round(decode_tok_s, 2),
+        "prefill_ms": round(float(np.mean(pre_ms)), 3),
+        "decode_ms_per_token_step": round(float(np.mean(dec_ms)) / steps_dec, 4),
+        "decode_hbm": decode_hbm,
+        "prefill_mfma": prefill_mfma,
+        "roofline": {"bound": "hbm", "kernel": "skinny_kernel<EPI_ARGMAX> (lm_head + argmax partials, M=%d)" % M,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "per_launch_us": round(per_launch_ms * 1e3, 2), "alg_bytes": alg_bytes},
+        "host_setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d, w, prompts[0])
+    m.close()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

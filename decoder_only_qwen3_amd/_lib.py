@@ -22,7 +22,7 @@ EXPORTS = [
     "q3_bind_memory", "q3_load_weights", "q3_seq_alloc", "q3_seq_reset", "q3_kv_reset",
     "q3_seq_length", "q3_prefill", "q3_decode_step", "q3_set_option", "q3_error_flags",
     "q3_last_error",
-    "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear",
+    "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear", "q3op_norm_linear",
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
     "q3op_attention",
 ]
@@ -87,6 +87,7 @@ def load() -> C.CDLL:
         "q3op_rmsnorm": (I32, [I32, VP, I32, VP, I32, C.c_float, VP, VP]),
         "q3op_linear_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "q3op_linear": (I32, [I32, I32, VP, I32, VP, I32, I32, VP, I64, VP, VP, SZ, VP]),
+        "q3op_norm_linear": (I32, [I32, VP, I32, VP, C.c_float, VP, I32, I32, VP, I64, VP, VP, SZ, VP]),
         "q3op_rope_workspace_bytes": (SZ, [I32, I32]),
         "q3op_rope_append": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP,
                                    C.c_float, C.c_double, I32, VP, VP, SZ, VP]),

@@ -262,6 +262,12 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
 // captured graph stays valid as the cache grows.
 constexpr int PSTRIDE = 128 + 2;
 
+// Split length used for a context of `ctx` keys over `splits` splits.
+Q3_DEV int split_chunk_len(int ctx, int splits) {
+  const int chunk = (ctx + splits - 1) / splits;
+  return (chunk + 31) & ~31;
+}
+
 __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restrict__ q, SeqBatch sb,
                                                          const SeqState* __restrict__ st,
                                                          const bf16_t* __restrict__ kv, int layer,
@@ -271,8 +277,7 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restric
   const int lane = threadIdx.x, fr = lane & 15, fq = lane >> 4;
   const SeqState s = st[sb.slot[b]];
   const int ctx = s.len + 1;
-  int chunk = (ctx + splits - 1) / splits;
-  chunk = (chunk + 31) & ~31;
+  const int chunk = split_chunk_len(ctx, splits);
   const int k_begin = j * chunk;
   const int k_end = min(ctx, k_begin + chunk);
   const int group = n_q / n_kv;
@@ -364,19 +369,35 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restric
   }
 }
 
-// One block of 128 threads per (sequence, query head): merge the splits in
-// index order (max-shifted weights 2^(m_j - M)), normalise, store bf16.
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part, int splits,
-                                                             bf16_t* __restrict__ o) {
+// One block of 128 threads per (sequence, query head): merge the non-empty
+// splits in index order (max-shifted weights 2^(m_j - M)), normalise, store.
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part, SeqBatch sb,
+                                                             const SeqState* __restrict__ st, int n_q,
+                                                             int splits, bf16_t* __restrict__ o) {
+  __shared__ float wgt[1024];
+  __shared__ float red[2];
   const int bh = blockIdx.x, d = threadIdx.x;
+  const int b = bh / n_q;
+  const int ctx = st[sb.slot[b]].len + 1;
+  const int chunk = split_chunk_len(ctx, splits);
+  const int nact = min(min(splits, (ctx + chunk - 1) / chunk), 1024);
   const float* p = part + (int64_t)bh * splits * PSTRIDE;
-  float M = -INFINITY;
-  for (int j = 0; j < splits; ++j) M = fmaxf(M, p[(int64_t)j * PSTRIDE]);
-  float L = 0.f, acc = 0.f;
-  for (int j = 0; j < splits; ++j) {
+  // Split maxima loaded in parallel, then the global max and the weights.
+  float mx = -INFINITY;
+  for (int j = d; j < nact; j += 128) {
     const float m = p[(int64_t)j * PSTRIDE];
-    if (m == -INFINITY) continue;
-    const float w = exp2_f(m - M);
+    wgt[j] = m;
+    mx = fmaxf(mx, m);
+  }
+  mx = wave_max(mx);
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  for (int j = d; j < nact; j += 128) wgt[j] = exp2_f(wgt[j] - M);
+  __syncthreads();
+  float L = 0.f, acc = 0.f;
+  for (int j = 0; j < nact; ++j) {
+    const float w = wgt[j];
     L += p[(int64_t)j * PSTRIDE + 1] * w;
     acc += p[(int64_t)j * PSTRIDE + 2 + d] * w;
   }
@@ -457,7 +478,7 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
 }
 
 int decode_attn_splits(int B, int n_kv, int64_t max_ctx) {
-  const int64_t by_len = (max_ctx + 31) / 32;
+  const int64_t by_len = (max_ctx + 63) / 64;
   int64_t want = (2048 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   if (want < 1) want = 1;
   int64_t sp = by_len < want ? by_len : want;
@@ -473,7 +494,7 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
   decode_attn_kernel<<<grid, 64, 0, s>>>(q, sb, st, kv, layer, n_q, n_kv, splits, part, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<<<sb.n * n_q, 128, 0, s>>>(part, splits, o);
+  decode_combine_kernel<<<sb.n * n_q, 128, 0, s>>>(part, sb, st, n_q, splits, o);
   return hipGetLastError();
 }
 

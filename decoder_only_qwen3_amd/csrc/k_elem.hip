@@ -151,10 +151,10 @@ Q3_DEV void better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
 }
 
-// Block-wide (max, lowest index) over 256 threads; result valid in thread 0.
+// Block-wide (max, lowest index) over up to 1024 threads; result valid in thread 0.
 Q3_DEV void block_argmax(float& bv, int& bi) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+  __shared__ float sv[16];
+  __shared__ int si[16];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     float ov = __shfl_xor(bv, o, 64);
@@ -198,17 +198,33 @@ hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int 
 
 // Pasos 8-9: reduce the lm_head kernel's per-block partials, then move the
 // sequences forward (decode: one more cached token; prefill: the prompt).
-__global__ __launch_bounds__(256) void argmax_finish_kernel(const float* __restrict__ pval,
-                                                            const int32_t* __restrict__ pidx,
-                                                            int nblocks, int M, int32_t* next,
-                                                            SeqBatch sb, SeqState* st, uint32_t* err) {
+__global__ __launch_bounds__(1024) void argmax_finish_kernel(const float* __restrict__ pval,
+                                                             const int32_t* __restrict__ pidx,
+                                                             int nblocks, int M, int32_t* next,
+                                                             SeqBatch sb, SeqState* st, uint32_t* err) {
   const int m = blockIdx.x;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   bool finite = true;
-  for (int j = threadIdx.x; j < nblocks; j += blockDim.x) {
-    float v = pval[(int64_t)j * M + m];
-    int i = pidx[(int64_t)j * M + m];
+  int j = threadIdx.x;
+  // four independent loads in flight per thread
+  for (; j + 3 * (int)blockDim.x < nblocks; j += 4 * blockDim.x) {
+    float v[4];
+    int ix[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = pval[(int64_t)(j + u * blockDim.x) * M + m];
+      ix[u] = pidx[(int64_t)(j + u * blockDim.x) * M + m];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      finite &= __builtin_isfinite(v[u]) || ix[u] < 0;
+      if (ix[u] >= 0) better(bv, bi, v[u], ix[u]);
+    }
+  }
+  for (; j < nblocks; j += blockDim.x) {
+    const float v = pval[(int64_t)j * M + m];
+    const int i = pidx[(int64_t)j * M + m];
     finite &= __builtin_isfinite(v) || i < 0;
     if (i >= 0) better(bv, bi, v, i);
   }
@@ -226,7 +242,7 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const float* __restr
 hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
                          const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  argmax_finish_kernel<<<M, 256, 0, s>>>(pval, pidx, nblocks, M, next, sb, st, err);
+  argmax_finish_kernel<<<M, 1024, 0, s>>>(pval, pidx, nblocks, M, next, sb, st, err);
   return hipGetLastError();
 }
 
@@ -240,6 +256,16 @@ __global__ void seq_advance_kernel(SeqBatch sb, SeqState* st) {
 
 hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s) {
   seq_advance_kernel<<<1, 64, 0, s>>>(sb, st);
+  return hipGetLastError();
+}
+
+__global__ void seq_set_len_kernel(SeqBatch sb, SeqState* st, int32_t len) {
+  const int b = threadIdx.x;
+  if (b < sb.n) st[sb.slot[b]].len = len;
+}
+
+hipError_t seq_set_len(const SeqBatch& sb, SeqState* st, int32_t len, hipStream_t s) {
+  seq_set_len_kernel<<<1, 64, 0, s>>>(sb, st, len);
   return hipGetLastError();
 }
 

@@ -5,19 +5,23 @@
 // no LDS staging); the few activation rows come from L2.
 //
 // Method source: "Dentro de un LLM: Inferencia en Python puro para Qwen3-0.6B
-// en MLX" -- Paso 5 (projections), Paso 6 (SwiGLU), Paso 7 (residuals),
-// Paso 8 (lm_head and the greedy pick).
+// en MLX" -- Paso 3 (RMSNorm, fused here as a prologue), Paso 5 (projections),
+// Paso 6 (SwiGLU), Paso 7 (residuals), Paso 8 (lm_head and the greedy pick).
 //
-// Decomposition: a block of 4 wavefronts owns RG groups of 16 weight rows and
-// a K range of 4*NST*32 columns; wavefront w takes NST consecutive 32-wide K
-// steps of that range.  MFMA operand mapping (v_mfma_f32_16x16x32_bf16):
+// Decomposition: a block owns RG groups of 16 weight rows (RG = 2 for SwiGLU:
+// a gate group and its up group) over the whole K range; its W wavefronts each
+// take NST consecutive 32-wide K steps (K = W * NST * 32).  Blocks never talk
+// to each other, so no device-scope fence is needed.  MFMA operand mapping
+// (v_mfma_f32_16x16x32_bf16):
 //   A = activations: lane l supplies X[mt*16 + l%16][k .. k+7]
 //   B = W^T:         lane l supplies W[row0 + l%16][k .. k+7]
 //   with k = kstep*32 + (l/16)*8, so each weight row is read as 64 contiguous
-//   bytes per load instruction.  The four wavefronts' partial sums are added
-//   in LDS in a fixed order.  When K needs several blocks (ksplit > 1) each
-//   block writes its partial to a workspace and the last block to finish a row
-//   range adds all partials in split order, so results are deterministic.
+//   bytes per load instruction.  The wavefronts' partial sums are added in
+//   LDS in wavefront order, so results do not depend on scheduling.
+//
+// NORM = true: X is not given; the prologue computes it from the float32
+// residual rows x and the norm weight g as bf16(x * rsqrt(mean(x^2)+eps) * g),
+// the same rounding point as the standalone RMSNorm kernel (decode, M <= 8).
 #include "kernels.h"
 
 namespace q3k {
@@ -25,19 +29,21 @@ namespace q3k {
 namespace {
 Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
-template <int EPI, int MT, int NST>
-__global__ __launch_bounds__(256) void skinny_kernel(const bf16_t* __restrict__ X, int M,
-                                                     const bf16_t* __restrict__ W, int N, int K,
-                                                     void* __restrict__ out, int64_t ldo,
-                                                     float* __restrict__ partials,
-                                                     uint32_t* __restrict__ counters,
-                                                     float* __restrict__ amax_val,
-                                                     int32_t* __restrict__ amax_idx, int ksplit) {
+constexpr int kMaxWaves = 16;
+constexpr int kNormMaxM = 8;
+
+template <int EPI, int MT, int NST, bool NORM>
+__global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ Xin, int M,
+                                                      const bf16_t* __restrict__ W, int N, int K,
+                                                      const float* __restrict__ gnorm, float eps,
+                                                      void* __restrict__ out, int64_t ldo,
+                                                      float* __restrict__ amax_val,
+                                                      int32_t* __restrict__ amax_idx) {
   constexpr int RG = (EPI == EPI_SWIGLU) ? 2 : 1;
-  constexpr int KW = NST * 32;  // K columns per wavefront
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int kidx = blockIdx.y;
-  const int k0 = kidx * (4 * KW) + wid * KW + (lane >> 4) * 8;
+  const int k0 = wid * (NST * 32) + (lane >> 4) * 8;
   const int row0 = blockIdx.x * RG * 16;
 
   // Weight fragments first: they are the HBM stream.
@@ -46,8 +52,41 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16_t* __restrict__ 
   for (int g = 0; g < RG; ++g) {
     const bf16_t* wp = W + (int64_t)(row0 + g * 16 + (lane & 15)) * K + k0;
 #pragma unroll
-    for (int s = 0; s < NST; ++s) wf[g][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + s * 32));
+    for (int s = 0; s < NST; ++s)
+      wf[g][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + s * 32));
   }
+
+  float* red = smem;                                  // [nw][RG][MT][256]
+  float* inv = smem + nw * RG * MT * 256;             // [kNormMaxM] (NORM only)
+  if constexpr (NORM) {
+    // Sums of squares of the M residual rows, reduced over the block.
+    const float* x = reinterpret_cast<const float*>(Xin);
+    float ss[kNormMaxM];
+#pragma unroll
+    for (int m = 0; m < kNormMaxM; ++m) ss[m] = 0.f;
+    for (int k = threadIdx.x * 4; k < K; k += blockDim.x * 4) {
+#pragma unroll
+      for (int m = 0; m < kNormMaxM; ++m) {
+        if (m < M) {
+          const float4 v = *reinterpret_cast<const float4*>(x + (int64_t)m * K + k);
+          ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kNormMaxM; ++m) {
+      const float t = wave_sum(ss[m]);
+      if (lane == 0) red[wid * kNormMaxM + m] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < kNormMaxM) {
+      float t = 0.f;
+      for (int w = 0; w < nw; ++w) t += red[w * kNormMaxM + threadIdx.x];
+      inv[threadIdx.x] = rsqrtf(t / (float)K + eps);
+    }
+    __syncthreads();
+  }
+
   f32x4 acc[RG][MT];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
@@ -56,83 +95,65 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16_t* __restrict__ 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + (lane & 15);
-    const bf16_t* xp = X + (int64_t)(m < M ? m : 0) * K + k0;
+    const bool live = m < M;
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
-      u32x4 xv = ld16(xp + s * 32);
-      if (m >= M) xv = u32x4{0u, 0u, 0u, 0u};
+      u32x4 xv = {0u, 0u, 0u, 0u};
+      if constexpr (NORM) {
+        if (live) {
+          const float* xp = reinterpret_cast<const float*>(Xin) + (int64_t)m * K + k0 + s * 32;
+          const float4 a = *reinterpret_cast<const float4*>(xp);
+          const float4 b = *reinterpret_cast<const float4*>(xp + 4);
+          const float4 ga = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32);
+          const float4 gb = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32 + 4);
+          const float r = inv[m];
+          xv[0] = pack_bf2(a.x * r * ga.x, a.y * r * ga.y);
+          xv[1] = pack_bf2(a.z * r * ga.z, a.w * r * ga.w);
+          xv[2] = pack_bf2(b.x * r * gb.x, b.y * r * gb.y);
+          xv[3] = pack_bf2(b.z * r * gb.z, b.w * r * gb.w);
+        }
+      } else {
+        const bf16_t* xp = reinterpret_cast<const bf16_t*>(Xin) + (int64_t)(live ? m : 0) * K + k0;
+        xv = ld16(xp + s * 32);
+        if (!live) xv = u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
       for (int g = 0; g < RG; ++g) acc[g][mt] = mfma16(as_bf16x8(xv), as_bf16x8(wf[g][s]), acc[g][mt]);
     }
   }
+  if constexpr (NORM) __syncthreads();  // red[] doubled as the norm scratch
 
-  // Cross-wavefront reduction.  red[w][g][mt][lane*4 + r].
-  __shared__ __attribute__((aligned(16))) float red[4][RG][MT][256];
+  // Cross-wavefront reduction: red[w][g][mt][lane*4 + r].
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<f32x4*>(&red[wid][g][mt][lane * 4]) = acc[g][mt];
+      *reinterpret_cast<f32x4*>(&red[((wid * RG + g) * MT + mt) * 256 + lane * 4]) = acc[g][mt];
   __syncthreads();
 
   // Entry e = (mt, lane', r) of the C fragment: m = mt*16 + (lane'/16)*4 + r,
-  // n = row0 + g*16 + lane'%16.
+  // n = row0 + g*16 + lane'%16.  Summed over wavefronts in order into red[0].
   constexpr int NE = MT * 256;
-  __shared__ float vals[RG][MT * 256];
-  for (int e = threadIdx.x; e < NE; e += 256) {
+  for (int e = threadIdx.x; e < NE; e += blockDim.x) {
     const int mt = e >> 8, le = e & 255;
+    if (mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3) >= M) continue;  // padding rows of the MFMA tile
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-      vals[g][e] = red[0][g][mt][le] + red[1][g][mt][le] + red[2][g][mt][le] + red[3][g][mt][le];
-  }
-
-  if (ksplit > 1) {
-    // Publish this split's partial, then let the last block of the row range finish.
-    for (int e = threadIdx.x; e < NE; e += 256) {
-      const int mt = e >> 8, le = e & 255;
-      const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
-      const int nl = (le >> 2) & 15;
-      if (m < M) {
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-          partials[((int64_t)kidx * M + m) * N + row0 + g * 16 + nl] = vals[g][e];
-      }
+    for (int g = 0; g < RG; ++g) {
+      float sum = 0.f;
+      for (int w = 0; w < nw; ++w) sum += red[((w * RG + g) * MT + mt) * 256 + le];
+      red[(g * MT + mt) * 256 + le] = sum;  // slot of wavefront 0, already read by this thread
     }
-    __threadfence();
-    __syncthreads();
-    __shared__ uint32_t ticket;
-    if (threadIdx.x == 0) ticket = atomicAdd(&counters[blockIdx.x], 1u);
-    __syncthreads();
-    if (ticket != (uint32_t)(ksplit - 1)) return;
-    __threadfence();
-    for (int e = threadIdx.x; e < NE; e += 256) {
-      const int mt = e >> 8, le = e & 255;
-      const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
-      const int nl = (le >> 2) & 15;
-      if (m < M) {
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-          float sum = 0.f;
-          for (int k = 0; k < ksplit; ++k)
-            sum += __builtin_nontemporal_load(&partials[((int64_t)k * M + m) * N + row0 + g * 16 + nl]);
-          vals[g][e] = sum;
-        }
-      }
-    }
-    if (threadIdx.x == 0) counters[blockIdx.x] = 0u;
-    __syncthreads();
   }
+  __syncthreads();
 
-  // Epilogue.
   if constexpr (EPI == EPI_ARGMAX) {
     // logits out, then per-row (max, lowest index) over this block's 16 rows
-    __syncthreads();
     float* o = reinterpret_cast<float*>(out);
-    for (int e = threadIdx.x; e < NE; e += 256) {
+    for (int e = threadIdx.x; e < NE; e += blockDim.x) {
       const int mt = e >> 8, le = e & 255;
       const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
       const int nl = (le >> 2) & 15;
-      if (m < M) o[(int64_t)m * ldo + row0 + nl] = vals[0][e];
+      if (m < M) o[(int64_t)m * ldo + row0 + nl] = red[mt * 256 + le];
     }
     if (threadIdx.x < M) {
       const int m = threadIdx.x, mt = m >> 4, mr = m & 15;
@@ -140,7 +161,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16_t* __restrict__ 
       int bi = -1;
       for (int nl = 0; nl < 16; ++nl) {
         const int le = ((((mr >> 2) << 4) + nl) << 2) + (mr & 3);
-        const float v = vals[0][mt * 256 + le];
+        const float v = red[mt * 256 + le];
         if (bi < 0 || v > bv) { bv = v; bi = row0 + nl; }
         if (!__builtin_isfinite(v)) { bv = v; bi = row0 + nl; break; }
       }
@@ -148,86 +169,96 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16_t* __restrict__ 
       amax_idx[(int64_t)blockIdx.x * M + m] = bi;
     }
   } else {
-    for (int e = threadIdx.x; e < NE; e += 256) {
+    for (int e = threadIdx.x; e < NE; e += blockDim.x) {
       const int mt = e >> 8, le = e & 255;
       const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
       const int nl = (le >> 2) & 15;
       if (m >= M) continue;
+      const float v0 = red[mt * 256 + le];
       if constexpr (EPI == EPI_SWIGLU) {
+        const float v1 = red[(MT + mt) * 256 + le];
         bf16_t* o = reinterpret_cast<bf16_t*>(out);
-        o[(int64_t)m * ldo + (row0 >> 1) + nl] = f2bf(silu_f(vals[0][e]) * vals[1][e]);
+        o[(int64_t)m * ldo + (row0 >> 1) + nl] = f2bf(silu_f(v0) * v1);
       } else if constexpr (EPI == EPI_RESADD) {
         float* o = reinterpret_cast<float*>(out);
-        o[(int64_t)m * ldo + row0 + nl] += vals[0][e];
+        o[(int64_t)m * ldo + row0 + nl] += v0;
       } else {
         float* o = reinterpret_cast<float*>(out);
-        o[(int64_t)m * ldo + row0 + nl] = vals[0][e];
+        o[(int64_t)m * ldo + row0 + nl] = v0;
       }
     }
   }
 }
 
-template <int EPI, int NST>
-hipError_t launch_mt(int MT, dim3 grid, const bf16_t* X, int M, const bf16_t* W, int N, int K, void* out,
-                     int64_t ldo, float* partials, uint32_t* counters, float* av, int32_t* ai,
-                     int ksplit, hipStream_t s) {
+template <int EPI, int NST, bool NORM>
+hipError_t launch_mt(int MT, dim3 grid, dim3 block, size_t lds, const void* X, int M, const bf16_t* W, int N,
+                     int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
+                     hipStream_t s) {
+#define Q3_SK(mt) skinny_kernel<EPI, mt, NST, NORM><<<grid, block, lds, s>>>(X, M, W, N, K, g, eps, out, ldo, av, ai)
   switch (MT) {
-    case 1: skinny_kernel<EPI, 1, NST><<<grid, 256, 0, s>>>(X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit); break;
-    case 2: skinny_kernel<EPI, 2, NST><<<grid, 256, 0, s>>>(X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit); break;
-    case 3: skinny_kernel<EPI, 3, NST><<<grid, 256, 0, s>>>(X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit); break;
-    default: skinny_kernel<EPI, 4, NST><<<grid, 256, 0, s>>>(X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit); break;
+    case 1: Q3_SK(1); break;
+    case 2: Q3_SK(2); break;
+    case 3: Q3_SK(3); break;
+    default: Q3_SK(4); break;
   }
+#undef Q3_SK
   return hipGetLastError();
 }
 
+template <int EPI, bool NORM>
+hipError_t launch_nst(const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const bf16_t* W, int N,
+                      int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
+                      hipStream_t s) {
+  const int rg = (EPI == EPI_SWIGLU) ? 2 : 1;
+  const size_t lds = (size_t)p.waves * rg * MT * 256 * 4 + kNormMaxM * 4;
+  dim3 block(64 * p.waves);
+  if (p.nst == 8) return launch_mt<EPI, 8, NORM>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
+  return launch_mt<EPI, 4, NORM>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
+}
+
 template <int EPI>
-hipError_t launch_nst(int nst, int MT, dim3 grid, const bf16_t* X, int M, const bf16_t* W, int N, int K,
-                      void* out, int64_t ldo, float* partials, uint32_t* counters, float* av,
-                      int32_t* ai, int ksplit, hipStream_t s) {
-  if (nst == 8)
-    return launch_mt<EPI, 8>(MT, grid, X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit, s);
-  return launch_mt<EPI, 4>(MT, grid, X, M, W, N, K, out, ldo, partials, counters, av, ai, ksplit, s);
+hipError_t launch_norm(bool norm, const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const bf16_t* W,
+                       int N, int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
+                       hipStream_t s) {
+  if (norm) return launch_nst<EPI, true>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
+  return launch_nst<EPI, false>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
 }
 }  // namespace
 
-// Choose how many 32-wide K steps each wavefront takes: 8 when the matrix has
-// enough 16-row groups to fill the GPU with one block per group, else 4 so
-// that more blocks share the rows.
+// Wavefronts per block and K steps per wavefront: 32-wide K steps in runs of
+// 4 (more wavefronts, more loads in flight per CU) unless that needs more than
+// 16 wavefronts or more than 48 KiB of LDS for the reduction.
 SkinnyPlan skinny_plan(int epi, int M, int N, int K) {
-  (void)M;
+  (void)N;
   const int rg = (epi == EPI_SWIGLU) ? 2 : 1;
-  const int groups = N / (16 * rg);
-  SkinnyPlan p;
-  p.nst = (K % 1024 == 0 && groups >= 512) ? 8 : 4;
-  p.ksplit = K / (4 * 32 * p.nst);
+  const int MT = (M + 15) / 16;
+  SkinnyPlan p{4, K / 128};
+  if (p.waves > kMaxWaves || p.waves * rg * MT > 48) p = SkinnyPlan{8, K / 256};
   return p;
 }
 
-size_t skinny_partials_floats(int M, int N, int ksplit) {
-  return ksplit > 1 ? (size_t)ksplit * M * N : 0;
-}
+bool skinny_norm_ok(int M) { return M <= kNormMaxM; }
 
-int skinny_argmax_blocks(int N, SkinnyPlan plan) {
-  (void)plan;
-  return N / 16;
-}
+int skinny_argmax_blocks(int N) { return N / 16; }
 
-hipError_t skinny_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, void* out,
-                       int64_t ldo, float* partials, uint32_t* counters, float* amax_val,
-                       int32_t* amax_idx, SkinnyPlan plan, hipStream_t s) {
+hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
+                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (M > 64) return hipErrorInvalidValue;
-  const int nst = plan.nst;
+  const bool norm = gnorm != nullptr;
+  if (norm && M > kNormMaxM) return hipErrorInvalidValue;
+  const SkinnyPlan p = skinny_plan(epi, M, N, K);
   const int rg = (epi == EPI_SWIGLU) ? 2 : 1;
-  if (N % (16 * rg) != 0 || K % (4 * 32 * nst) != 0 || plan.ksplit * 4 * 32 * nst != K)
-    return hipErrorInvalidValue;
   const int MT = (M + 15) / 16;
-  dim3 grid(N / (16 * rg), plan.ksplit);
+  if (N % (16 * rg) != 0 || p.waves * p.nst * 32 != K || p.waves > kMaxWaves || p.waves * rg * MT > 48 ||
+      (norm && K % 4 != 0))
+    return hipErrorInvalidValue;
+  dim3 grid(N / (16 * rg));
   switch (epi) {
-    case EPI_STORE: return launch_nst<EPI_STORE>(nst, MT, grid, X, M, W, N, K, out, ldo, partials, counters, amax_val, amax_idx, plan.ksplit, s);
-    case EPI_RESADD: return launch_nst<EPI_RESADD>(nst, MT, grid, X, M, W, N, K, out, ldo, partials, counters, amax_val, amax_idx, plan.ksplit, s);
-    case EPI_SWIGLU: return launch_nst<EPI_SWIGLU>(nst, MT, grid, X, M, W, N, K, out, ldo, partials, counters, amax_val, amax_idx, plan.ksplit, s);
-    case EPI_ARGMAX: return launch_nst<EPI_ARGMAX>(nst, MT, grid, X, M, W, N, K, out, ldo, partials, counters, amax_val, amax_idx, plan.ksplit, s);
+    case EPI_STORE: return launch_norm<EPI_STORE>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
+    case EPI_RESADD: return launch_norm<EPI_RESADD>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
+    case EPI_SWIGLU: return launch_norm<EPI_SWIGLU>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
+    case EPI_ARGMAX: return launch_norm<EPI_ARGMAX>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
   }
   return hipErrorInvalidValue;
 }

@@ -39,6 +39,7 @@ hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int 
 hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
                          const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s);
 hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s);
+hipError_t seq_set_len(const SeqBatch& sb, SeqState* st, int32_t len, hipStream_t s);
 hipError_t widen_bf16(const bf16_t* src, float* dst, int64_t n, hipStream_t s);
 hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 
@@ -49,17 +50,18 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
 
 // ---------------------------------------------------------------- k_skinny.hip
 struct SkinnyPlan {
-  int nst;     // 32-wide K steps per wavefront (4 or 8)
-  int ksplit;  // blocks sharing one row range, each over K/ksplit
+  int nst;    // 32-wide K steps per wavefront (4 or 8)
+  int waves;  // wavefronts per block; K = waves * nst * 32
 };
 SkinnyPlan skinny_plan(int epi, int M, int N, int K);
-size_t skinny_partials_floats(int M, int N, int ksplit);
-// M <= 64 rows of X (bf16) times W[N,K]^T (bf16).  `partials` holds
-// ksplit*M*N floats when ksplit > 1; `counters` N/16/rb zeroed words.
-hipError_t skinny_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, void* out,
-                       int64_t ldo, float* partials, uint32_t* counters, float* amax_val,
-                       int32_t* amax_idx, SkinnyPlan plan, hipStream_t s);
-int skinny_argmax_blocks(int N, SkinnyPlan plan);
+bool skinny_norm_ok(int M);
+int skinny_argmax_blocks(int N);
+// M <= 64 rows times W[N,K]^T (bf16).  gnorm == nullptr: X is bf16 [M][K].
+// gnorm != nullptr (M <= 8): X is the float32 residual [M][K] and the kernel
+// applies RMSNorm with weight gnorm and eps first.  EPI_ARGMAX also writes
+// per-block (max, index) partials, N/16 blocks x M.
+hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
+                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s);
 // float32 weights and activations (the float32 model); any M.
 hipError_t gemv_f32(int epi, const float* X, int M, const float* W, int N, int K, void* out,
                     int64_t ldo, hipStream_t s);

@@ -30,18 +30,15 @@ q3_status op_hip(hipError_t e, const char* what) {
 size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
 struct SkinnyWs {
-  size_t counters, err, amax_val, amax_idx, partials, total;
+  size_t err, amax_val, amax_idx, total;
 };
-SkinnyWs skinny_ws(int epi, int M, int N, int K) {
+SkinnyWs skinny_ws(int M, int N) {
   SkinnyWs w;
-  SkinnyPlan p = skinny_plan(epi, M, N, K);
   const size_t groups = (size_t)N / 16;
-  w.counters = 0;
-  w.err = al(groups * 4);
-  w.amax_val = w.err + al(16);
+  w.err = 0;
+  w.amax_val = al(16);
   w.amax_idx = w.amax_val + al(groups * M * 4);
-  w.partials = w.amax_idx + al(groups * M * 4);
-  w.total = w.partials + al(skinny_partials_floats(M, N, p.ksplit) * 4 + 4);
+  w.total = w.amax_idx + al(groups * M * 4);
   return w;
 }
 
@@ -56,6 +53,22 @@ q3_status upload_states(int n, const int64_t* base, const int32_t* cap, const in
   }
   OP_TRY(hipStreamSynchronize(s));
   OP_TRY(hipMemcpy(d_ws, st.data(), n * sizeof(SeqState), hipMemcpyHostToDevice));
+  return Q3_OK;
+}
+
+q3_status skinny_op(int epi, const void* X, int M, const float* gnorm, float eps, const void* W, int N, int K,
+                    void* out, int64_t ldo, int32_t* next, void* d_ws, size_t ws_bytes, hipStream_t s) {
+  SkinnyWs w = skinny_ws(M, N);
+  if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace too small");
+  char* ws = (char*)d_ws;
+  OP_TRY(skinny_bf16(epi, X, M, (const bf16_t*)W, N, K, gnorm, eps, out, ldo, (float*)(ws + w.amax_val),
+                     (int32_t*)(ws + w.amax_idx), s));
+  if (epi == EPI_ARGMAX && next) {
+    SeqBatch none;
+    std::memset(&none, 0, sizeof(none));
+    OP_TRY(argmax_finish((const float*)(ws + w.amax_val), (const int32_t*)(ws + w.amax_idx), skinny_argmax_blocks(N),
+                         M, next, none, nullptr, (uint32_t*)(ws + w.err), s));
+  }
   return Q3_OK;
 }
 
@@ -96,8 +109,10 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
 }
 
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K) {
-  if (kernel == Q3OP_SKINNY) return skinny_ws(epi, M, N, K).total;
-  return 0;
+  (void)epi;
+  (void)K;
+  if (kernel == Q3OP_SKINNY) return skinny_ws(M, N).total;
+  return 256;
 }
 
 q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
@@ -106,7 +121,8 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   hipStream_t s = (hipStream_t)stream;
   if (!d_x || !d_w || !d_out || M < 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
   if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
-  if (epi == EPI_ARGMAX && (!d_next || M > Q3_MAX_BATCH)) return op_fail(Q3_E_ARG, "logits epilogue needs d_next and M <= 64");
+  if (epi == EPI_ARGMAX && M > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "logits epilogue needs M <= 64");
+  if (epi == EPI_ARGMAX && !d_next && kernel != Q3OP_SKINNY) return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
   RowMap rows;
   rows.n = M;
   for (int i = 0; i < M && i < Q3_MAX_BATCH; ++i) rows.row[i] = i;
@@ -130,22 +146,19 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   }
   if (kernel == Q3OP_SKINNY) {
     if (M > Q3_MAX_BATCH) return op_fail(Q3_E_UNSUPPORTED, "the weight-streaming kernel takes M <= 64");
-    SkinnyWs w = skinny_ws(epi, M, N, K);
-    if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace too small");
-    char* ws = (char*)d_ws;
-    SkinnyPlan p = skinny_plan(epi, M, N, K);
-    OP_TRY(fill_u32((uint32_t*)(ws + w.counters), 0u, N / 16, s));
-    OP_TRY(skinny_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, d_out, ldo, (float*)(ws + w.partials),
-                       (uint32_t*)(ws + w.counters), (float*)(ws + w.amax_val), (int32_t*)(ws + w.amax_idx), p, s));
-    if (epi == EPI_ARGMAX) {
-      SeqBatch none;
-      std::memset(&none, 0, sizeof(none));
-      OP_TRY(argmax_finish((const float*)(ws + w.amax_val), (const int32_t*)(ws + w.amax_idx),
-                           skinny_argmax_blocks(N, p), M, d_next, none, nullptr, (uint32_t*)(ws + w.err), s));
-    }
-    return Q3_OK;
+    return skinny_op(epi, d_x, M, nullptr, 0.f, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, s);
   }
   return op_fail(Q3_E_ARG, "unknown kernel");
+}
+
+q3_status q3op_norm_linear(int32_t epi, const float* d_x, int32_t M, const float* d_gnorm, float eps,
+                           const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo, int32_t* d_next,
+                           void* d_ws, size_t ws_bytes, void* stream) {
+  if (!d_x || !d_gnorm || !d_w || !d_out || M <= 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
+  if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
+  if (epi == EPI_ARGMAX && !d_next) return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
+  if (!skinny_norm_ok(M)) return op_fail(Q3_E_UNSUPPORTED, "the fused RMSNorm prologue takes M <= 8");
+  return skinny_op(epi, d_x, M, d_gnorm, eps, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, (hipStream_t)stream);
 }
 
 size_t q3op_rope_workspace_bytes(int32_t n_seqs, int32_t max_pos) {

@@ -51,10 +51,8 @@ struct WeightLayout {
 };
 
 struct WsLayout {
-  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, partials, counters, attn_part, state,
-      err, total;
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, state, err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
-  int64_t n_counters;
   int amax_blocks;
 };
 
@@ -139,21 +137,6 @@ WsLayout ws_layout(const q3_config& c) {
   W.amax_blocks = c.vocab / 16;
   W.amax_val = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
   W.amax_idx = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
-  size_t part = 0;
-  int64_t counters = 0;
-  const int shapes[5][3] = {{EPI_STORE, qkv_rows(c), c.hidden},
-                            {EPI_RESADD, c.hidden, (int)Q},
-                            {EPI_SWIGLU, 2 * c.ffn, c.hidden},
-                            {EPI_RESADD, c.hidden, c.ffn},
-                            {EPI_ARGMAX, c.vocab, c.hidden}};
-  for (auto& s : shapes) {
-    SkinnyPlan p = skinny_plan(s[0], Q3_MAX_BATCH, s[1], s[2]);
-    part = std::max(part, skinny_partials_floats(Q3_MAX_BATCH, s[1], p.ksplit));
-    counters = std::max<int64_t>(counters, s[1] / 16);
-  }
-  W.n_counters = counters;
-  W.partials = take(part * 4 + 4);
-  W.counters = take(counters * 4);
   W.attn_part = take((size_t)max_attn_splits_rows(c) * c.n_q_heads * 130 * 4);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
@@ -246,8 +229,6 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   void* qb = m->WS(L.q);
   void* ob = m->WS(L.o);
   void* mb = m->WS(L.m);
-  float* part = m->WS<float>(L.partials);
-  uint32_t* cnt = m->WS<uint32_t>(L.counters);
   const float* cos_t = m->W<float>(m->wl.cos_t);
   const float* sin_t = m->W<float>(m->wl.sin_t);
   RowMap all;
@@ -261,13 +242,15 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   }
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
-    // Paso 3 + Paso 5: normalised input, fused q/k/v projection.
-    LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
+    // Paso 3 + Paso 5: normalised input, fused q/k/v projection.  Decode with
+    // few rows folds the RMSNorm into the projection kernel's prologue.
+    const bool fuse_norm = bf && decode && skinny_norm_ok(T);
+    if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
     if (!bf) {
       LAUNCH(gemv_f32(EPI_STORE, (const float*)h, T, m->W<float>(lw.qkv), NQKV, H, qkv, NQKV, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, part, cnt,
-                         nullptr, nullptr, skinny_plan(EPI_STORE, T, NQKV, H), s));
+      LAUNCH(skinny_bf16(EPI_STORE, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.qkv), NQKV, H,
+                         fuse_norm ? m->W<float>(lw.in_norm) : nullptr, c.rms_eps, qkv, NQKV, nullptr, nullptr, s));
     } else {
       LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, s));
     }
@@ -289,21 +272,19 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     if (!bf) {
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, part, cnt, nullptr,
-                         nullptr, skinny_plan(EPI_RESADD, T, H, Q), s));
+      LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s));
     } else {
       LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
     }
     // SwiGLU MLP + residual (Paso 6, Paso 7).
-    LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.post_norm), H, c.rms_eps, h, s));
+    if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.post_norm), H, c.rms_eps, h, s));
     if (!bf) {
       LAUNCH(gemv_f32(EPI_SWIGLU, (const float*)h, T, m->W<float>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)mb, T, m->W<float>(lw.d), H, I, x, H, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, part, cnt,
-                         nullptr, nullptr, skinny_plan(EPI_SWIGLU, T, 2 * I, H), s));
-      LAUNCH(skinny_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, part, cnt, nullptr,
-                         nullptr, skinny_plan(EPI_RESADD, T, H, I), s));
+      LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.gu), 2 * I, H,
+                         fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps, mb, I, nullptr, nullptr, s));
+      LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s));
     } else {
       LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
@@ -321,13 +302,16 @@ q3_status enqueue_head(q3_model* m, const RowMap& rows, int nrows, const SeqBatc
   float* x = m->WS<float>(L.x);
   void* h = m->WS(L.h);
   float* logits = d_logits ? d_logits : m->WS<float>(L.logits);
-  LAUNCH(rmsnorm(c.dtype, x, nrows, rows, m->W<float>(m->wl.final_norm), c.hidden, c.rms_eps, h, s));
+  // The lm_head has ~9500 blocks; a per-block RMSNorm prologue would repeat the
+  // norm in each of them, so the final norm stays a separate kernel.
+  const bool fuse_norm = false;
+  if (!fuse_norm)
+    LAUNCH(rmsnorm(c.dtype, x, nrows, rows, m->W<float>(m->wl.final_norm), c.hidden, c.rms_eps, h, s));
   if (c.dtype == Q3_BF16) {
-    SkinnyPlan p = skinny_plan(EPI_ARGMAX, nrows, c.vocab, c.hidden);
-    LAUNCH(skinny_bf16(EPI_ARGMAX, (const bf16_t*)h, nrows, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, logits,
-                       c.vocab, m->WS<float>(L.partials), m->WS<uint32_t>(L.counters), m->WS<float>(L.amax_val),
-                       m->WS<int32_t>(L.amax_idx), p, s));
-    LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), skinny_argmax_blocks(c.vocab, p),
+    LAUNCH(skinny_bf16(EPI_ARGMAX, fuse_norm ? (const void*)x : h, nrows, m->W<bf16_t>(m->wl.embed), c.vocab,
+                       c.hidden, fuse_norm ? m->W<float>(m->wl.final_norm) : nullptr, c.rms_eps, logits, c.vocab,
+                       m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
+    LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), skinny_argmax_blocks(c.vocab),
                          nrows, d_next, sb, m->state(), m->err(), s));
   } else {
     LAUNCH(gemv_f32(EPI_STORE, (const float*)h, nrows, m->W<float>(m->wl.embed), c.vocab, c.hidden, logits,
@@ -428,7 +412,6 @@ q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, voi
   HIP_TRY(hipMemcpyAsync(m->W(m->wl.sin_t), sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s));
   std::vector<SeqState> zero(c.max_slots, SeqState{0, 0, 0});
   HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
-  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.counters), 0u, m->wsl.n_counters, s));
   HIP_TRY(fill_u32(m->err(), 0u, 4, s));
   HIP_TRY(hipStreamSynchronize(s));
   m->bound = true;
@@ -558,11 +541,15 @@ q3_status q3_seq_reset(q3_model* m, int32_t n, const int32_t* slots, void* strea
   if (n < 0 || (n > 0 && !slots)) return fail(Q3_E_ARG, "bad slot list");
   for (int i = 0; i < n; ++i)
     if (slots[i] < 0 || slots[i] >= m->cfg.max_slots) return fail(Q3_E_ARG, "slot out of range");
-  for (int i = 0; i < n; ++i) {
-    m->slots[slots[i]].len = 0;
-    q3_status st = upload_state(m, slots[i], (hipStream_t)stream);
-    if (st != Q3_OK) return st;
+  // Queued on the stream (no host synchronisation), in batches of Q3_MAX_BATCH.
+  for (int i0 = 0; i0 < n; i0 += Q3_MAX_BATCH) {
+    SeqBatch sb;
+    std::memset(&sb, 0, sizeof(sb));
+    sb.n = std::min(n - i0, Q3_MAX_BATCH);
+    for (int b = 0; b < sb.n; ++b) sb.slot[b] = slots[i0 + b];
+    HIP_TRY(seq_set_len(sb, m->state(), 0, (hipStream_t)stream));
   }
+  for (int i = 0; i < n; ++i) m->slots[slots[i]].len = 0;
   g_err.clear();
   return Q3_OK;
 }

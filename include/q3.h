@@ -122,7 +122,8 @@ q3_status q3_load_weights(q3_model* m, const q3_tensor* tensors, int32_t n, void
 /* Give slot `slot` a KV region of `capacity_tokens` (rounded up to 64) from
  * the arena, and empty it.  A slot can be allocated once per arena reset. */
 q3_status q3_seq_alloc(q3_model* m, int32_t slot, int64_t capacity_tokens, void* stream);
-/* Empty the given slots (length 0), keeping their regions. */
+/* Empty the given slots (length 0), keeping their regions.  Queued on
+ * `stream` without synchronising it. */
 q3_status q3_seq_reset(q3_model* m, int32_t n, const int32_t* slots, void* stream);
 /* Free every slot region (the whole arena becomes available again). */
 q3_status q3_kv_reset(q3_model* m, void* stream);

@@ -40,7 +40,8 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  *   2 SwiGLU: W rows packed in runs of 16 gate rows then 16 up rows,
  *     out[m][j] = silu(gate_j) * up_j written in X's dtype (ldo >= N/2);
  *   3 logits: store float32 out[M][ldo] and d_next[m] = argmax (lowest index
- *     on ties).
+ *     on ties).  With kernel 1 and d_next == NULL only the logits and the
+ *     kernel's per-block (max, index) partials are produced (one launch).
  * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0);
  * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
  * kernel 2 = float32 GEMV (float32 model).  bf16 kernels take bf16 X and W. */
@@ -51,6 +52,14 @@ size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32
 q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
                       int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
                       void* stream);
+
+/* Pasos 3 + 5: the weight-streaming kernel with RMSNorm fused into its
+ * prologue (decode with M <= 8): X = bf16(x * rsqrt(mean(x^2) + eps) * g)
+ * from float32 rows d_x [M][K] and float32 weight d_gnorm [K], then epilogue
+ * `epi` as in q3op_linear.  Workspace: q3op_linear_workspace_bytes(1, ...). */
+q3_status q3op_norm_linear(int32_t epi, const float* d_x, int32_t M, const float* d_gnorm, float eps,
+                           const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo, int32_t* d_next,
+                           void* d_ws, size_t ws_bytes, void* stream);
 
 /* A one-layer KV arena for the attention ops: sequence b owns the elements
  * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):

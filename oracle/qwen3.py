@@ -223,7 +223,7 @@ class OracleModel:
 
     # -- Paso 5 + Paso 7 ------------------------------------------------------
     def attention(self, h: np.ndarray, layer: int, cache: KVCache,
-                  positions: np.ndarray) -> np.ndarray:
+                  positions: np.ndarray, keep: Optional[np.ndarray] = None) -> np.ndarray:
         d = self.d
         p = f"model.layers.{layer}.self_attn"
         T = h.shape[0]
@@ -243,16 +243,25 @@ class OracleModel:
         cache.v[layer][s0:s1] = v
         k_all = cache.k[layer][:s1]
         v_all = cache.v[layer][:s1]
+        if keep is not None:
+            q, positions, T = q[keep], positions[keep], len(keep)
         o = attention_rows(q, k_all, v_all, positions, np.arange(s1, dtype=np.int64))
         o = self.rnd(o.reshape(T, d.n_q_heads * d.head_dim))
         return o @ self.W(f"{p}.o_proj.weight").T
 
     def block(self, x: np.ndarray, layer: int, cache: KVCache,
-              positions: np.ndarray) -> np.ndarray:
+              positions: np.ndarray, keep: Optional[np.ndarray] = None) -> np.ndarray:
+        """Paso 7.  `keep`: indices of the rows whose output is wanted; every
+        row's key and value still enter the cache, and the kept rows' values
+        are exactly those of the full computation (rows do not mix outside
+        attention, and attention reads only the cache)."""
         d = self.d
         p = f"model.layers.{layer}"
         h = self.rnd(rms_norm(x, self.W(f"{p}.input_layernorm.weight"), d.rms_eps))
-        x = x + self.attention(h, layer, cache, positions)
+        a = self.attention(h, layer, cache, positions, keep)
+        if keep is not None:
+            x = x[keep]
+        x = x + a
         h = self.rnd(rms_norm(x, self.W(f"{p}.post_attention_layernorm.weight"), d.rms_eps))
         x = x + swiglu(h, self.W(f"{p}.mlp.gate_proj.weight"), self.W(f"{p}.mlp.up_proj.weight"),
                        self.W(f"{p}.mlp.down_proj.weight"), self.rnd)
@@ -275,12 +284,16 @@ class OracleModel:
         pos0 = cache.length
         positions = pos0 + np.arange(ids.size, dtype=np.int64)
         E = self.W("model.embed_tokens.weight")
+        rows = np.asarray([ids.size - 1] if logit_rows is None else list(logit_rows), dtype=np.int64)
         x = E[ids]
         for layer in range(d.n_layers):
-            x = self.block(x, layer, cache, positions)
+            # The last block only needs the rows whose logits are returned.
+            keep = rows if layer == d.n_layers - 1 else None
+            x = self.block(x, layer, cache, positions, keep)
         cache.length = pos0 + ids.size
-        rows = [ids.size - 1] if logit_rows is None else list(logit_rows)
-        hf = self.rnd(rms_norm(x[rows], self.W("model.norm.weight"), d.rms_eps))
+        if d.n_layers == 0:
+            x = x[rows]
+        hf = self.rnd(rms_norm(x, self.W("model.norm.weight"), d.rms_eps))
         return hf @ E.T
 
     # -- Paso 9: generation loops ---------------------------------------------

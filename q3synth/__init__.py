@@ -132,10 +132,15 @@ def tensor_specs(d: ModelDims) -> List[Tuple[str, Tuple[int, ...], str]]:
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """float32 -> nearest bf16 value (ties to even), returned as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    a = np.array(a, dtype=np.float32, copy=True, order="C")
+    if not np.all(np.isfinite(a)):
+        raise ValueError("round_to_bf16 expects finite values")
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)       # finite floats stay below 2^32 here
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -147,23 +152,34 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
-def make_weights(d: ModelDims, seed: int = 0) -> Dict[str, np.ndarray]:
-    """Seeded random-init weights, float32 arrays (bf16 values for bf16 models)."""
+def _draw(spec, ss, bf16: bool) -> np.ndarray:
+    name, shape, kind = spec
+    rng = np.random.Generator(np.random.PCG64(ss))
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if kind == "linear":
+        a *= np.float32(0.02)
+    else:
+        a *= np.float32(0.1)
+        a += np.float32(1.0)
+    return round_to_bf16(a) if bf16 else a
+
+
+def make_weights(d: ModelDims, seed: int = 0, threads: int = 1) -> Dict[str, np.ndarray]:
+    """Seeded random-init weights, float32 arrays (bf16 values for bf16 models).
+
+    Each tensor has its own child seed, so drawing them on several threads gives
+    the same arrays as drawing them one after another.
+    """
     specs = tensor_specs(d)
     children = np.random.SeedSequence(seed).spawn(len(specs))
-    out: Dict[str, np.ndarray] = {}
-    for (name, shape, kind), ss in zip(specs, children):
-        rng = np.random.Generator(np.random.PCG64(ss))
-        a = rng.standard_normal(shape, dtype=np.float32)
-        if kind == "linear":
-            a *= np.float32(0.02)
-        else:
-            a *= np.float32(0.1)
-            a += np.float32(1.0)
-        if d.dtype == "bf16":
-            a = round_to_bf16(a)
-        out[name] = a
-    return out
+    bf = d.dtype == "bf16"
+    if threads > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            arrays = list(ex.map(lambda a: _draw(a[0], a[1], bf), zip(specs, children)))
+    else:
+        arrays = [_draw(sp, ss, bf) for sp, ss in zip(specs, children)]
+    return {sp[0]: a for sp, a in zip(specs, arrays)}
 
 
 def make_tokens(n: int, vocab: int, seed: int) -> np.ndarray:

@@ -354,3 +354,46 @@ def test_attention_f32(mode):
     else:
         worst = _attention_case(2, [1, 1], [0, 300], [64, 320], seed=10)
     assert worst < 1.0, worst
+
+
+@pytest.mark.parametrize("epi,M,N", [(EPI_STORE, 1, 4096), (EPI_SWIGLU, 3, 6144), (EPI_ARGMAX, 1, 8192),
+                                     (EPI_STORE, 8, 4096)])
+def test_norm_linear_fused_prologue(epi, M, N):
+    """RMSNorm folded into the weight-streaming kernel equals rmsnorm -> bf16 -> projection."""
+    mod, lib = ops()
+    rng = np.random.default_rng(50 + M + epi)
+    K = 1024
+    x = (rng.standard_normal((M, K)) * rng.uniform(0.05, 10, (M, 1))).astype(np.float32)
+    g = q3synth.round_to_bf16((1 + 0.1 * rng.standard_normal(K)).astype(np.float32))
+    W = rand_bf16(rng, (N, K), 0.02)
+    h = to_bf16(rms_norm(x.astype(np.float64), g.astype(np.float64), 1e-6))
+    dx, dg, dw = dev_f32(x), dev_f32(g), dev_bf16(W)
+    if epi == EPI_SWIGLU:
+        out = torch.zeros((M, N // 2), dtype=torch.int16, device="cuda:0")
+        ldo = N // 2
+    else:
+        out = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+        ldo = N
+    nxt = torch.zeros(M, dtype=torch.int32, device="cuda:0")
+    ws = _ws(lib.q3op_linear_workspace_bytes(SKINNY, epi, M, N, K))
+    call(lib.q3op_norm_linear(epi, dx.data_ptr(), M, dg.data_ptr(), 1e-6, dw.data_ptr(), N, K, out.data_ptr(),
+                              ldo, nxt.data_ptr(), ws.data_ptr(), ws.numel(), None))
+    _sync()
+    if epi == EPI_SWIGLU:
+        gg = h @ W[0::2].astype(np.float64).T  # not the packed layout: rebuild below
+        Wp = W.astype(np.float64)
+        gate = np.concatenate([Wp[32 * r:32 * r + 16] for r in range(N // 32)])
+        up = np.concatenate([Wp[32 * r + 16:32 * r + 32] for r in range(N // 32)])
+        ref = to_bf16(silu(h @ gate.T) * (h @ up.T))
+        got = host_bf16(out)
+        np.testing.assert_allclose(got, ref, rtol=2 ** -7, atol=1e-6)
+        assert np.mean(got == ref) > 0.98
+    else:
+        ref = h @ W.astype(np.float64).T
+        got = out.cpu().numpy()
+        # the prologue rounds to bf16 like the oracle; rare one-ulp flips of h allowed
+        assert _rel(got, ref) < 5e-3
+        assert np.median(np.abs(got - ref)) < 1e-5 * np.sqrt(np.mean(ref ** 2)) + 1e-6
+        if epi == EPI_ARGMAX:
+            for m in range(M):
+                assert nxt.cpu().numpy()[m] == int(np.argmax(got[m]))

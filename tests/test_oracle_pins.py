@@ -317,3 +317,20 @@ def test_page_prompt_ids_are_valid_tokens():
     ids = json.load(open(path))["ids"]
     assert ids == [785, 6722, 315, 9625, 374]
     assert all(0 <= t < q3synth.ModelDims().vocab for t in ids)
+
+
+def test_last_layer_row_pruning_matches_full_rows():
+    # Returning logits for a subset of rows skips work in the last block only;
+    # the kept rows must equal the same rows of the all-rows computation.
+    for n_layers in (1, 2):
+        d, w = _tiny_model(n_layers=n_layers)
+        m = OracleModel(d, w)
+        ids = [5, 17, 3, 3, 88, 41, 0]
+        full = m.forward(ids, m.new_cache(7), logit_rows=range(7))
+        part = m.forward(ids, m.new_cache(7), logit_rows=[1, 6])
+        np.testing.assert_allclose(part, full[[1, 6]], rtol=1e-13, atol=1e-15)
+        # and the cache filled by a pruned call supports exact decode afterwards
+        c1, c2 = m.new_cache(8), m.new_cache(8)
+        m.forward(ids, c1, logit_rows=range(7))
+        m.forward(ids, c2)
+        np.testing.assert_allclose(m.forward([9], c1), m.forward([9], c2), rtol=1e-13, atol=1e-15)
