@@ -1,0 +1,197 @@
+"""Parity at the five workload shapes, through the C ABI, against the CPU oracle.
+
+Where the oracle cannot run the whole workload in seconds, it checks sampled
+sequences (the others run in the same packed GPU call), a 1-layer cut at the
+full sequence length, or properties that hold at any size (decode equals
+recompute, determinism).  Bars: bf16 logits within 3e-2 of the logit RMS;
+greedy tokens equal unless the oracle's top two are within that bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import q3synth
+from gpu_helpers import margin_ok, rel_err, weights_for
+from oracle import OracleModel
+
+pytestmark = pytest.mark.gpu
+
+TOL = 3e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _model(d, **cap):
+    from decoder_only_qwen3_amd import Q3Model
+    return Q3Model(d, **cap)
+
+
+def _prompts(wl, d):
+    lens = [int(x) for x in wl.prompt_lengths()]
+    return [q3synth.make_tokens(L, d.vocab, wl.seed + 1 + i).tolist() for i, L in enumerate(lens)]
+
+
+def _prefill_then_forced(m, slots, prompts, forced):
+    """Packed prefill of all slots, then len(forced[0]) batched decode steps with
+    the given tokens.  Returns logits [steps+1][B][V] as numpy."""
+    dev = m.device
+    B, V = len(slots), m.dims.vocab
+    logits, nxt = m.prefill(slots, prompts)
+    with torch.cuda.stream(m.stream):
+        rows = [logits.clone()]
+        tok = torch.empty(B, dtype=torch.int32, device=dev)
+        lg = torch.empty((B, V), dtype=torch.float32, device=dev)
+        nx = torch.empty(B, dtype=torch.int32, device=dev)
+    n_steps = len(forced[0])
+    for i in range(n_steps):
+        with torch.cuda.stream(m.stream):
+            tok.copy_(torch.tensor([f[i] for f in forced], dtype=torch.int32), non_blocking=False)
+        m.decode_raw(slots, tok, lg, nx)
+        with torch.cuda.stream(m.stream):
+            rows.append(lg.clone())
+    m.synchronize()
+    return np.stack([r.cpu().numpy() for r in rows])
+
+
+def _check(ref, got, what):
+    e = rel_err(got, ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert e <= TOL, f"{what}: logits error {e:.3e}"
+    assert margin_ok(ref, int(np.argmax(got)), TOL * rms), f"{what}: argmax differs beyond a near-tie"
+    return e
+
+
+def test_workload_512_prompt_256_steps():
+    wl = q3synth.WORKLOADS["q06b_bf16_p512_d256"]
+    d = wl.dims
+    w = weights_for(d, wl.seed)
+    prompt = _prompts(wl, d)[0]
+    forced = q3synth.make_tokens(6, d.vocab, wl.seed + 77).tolist()
+    m = _model(d, max_slots=1, max_positions=768, max_prefill_tokens=512, kv_tokens=768)
+    m.load_weights(w)
+    m.seq_alloc(0, 768)
+    got = _prefill_then_forced(m, [0], [prompt], [forced])
+    _say("gpu done; oracle forced run")
+    o = OracleModel(d, w)
+    ref = o.forced_logits(prompt, forced)
+    errs = [_check(ref[i], got[i][0], f"step {i}") for i in range(len(ref))]
+    _say("forced-token errors:", ["%.2e" % e for e in errs])
+    # greedy decode of the full 256 steps, twice: deterministic, finite, in range
+    runs = []
+    for _ in range(2):
+        m.seq_reset([0])
+        logits, nxt = m.prefill([0], [prompt])
+        with torch.cuda.stream(m.stream):
+            toks = [torch.empty(1, dtype=torch.int32, device=m.device) for _ in range(2)]
+            toks[0].copy_(nxt)
+            lg = torch.empty((1, d.vocab), dtype=torch.float32, device=m.device)
+            seq = torch.empty(wl.decode_steps + 1, dtype=torch.int32, device=m.device)
+            seq[0:1].copy_(nxt)
+        for i in range(wl.decode_steps):
+            m.decode_raw([0], toks[i % 2], lg, toks[(i + 1) % 2])
+            with torch.cuda.stream(m.stream):
+                seq[i + 1:i + 2].copy_(toks[(i + 1) % 2])
+        m.synchronize()
+        runs.append((seq.cpu().numpy(), lg.cpu().numpy()))
+    assert m.error_flags() == 0
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1], runs[1][1])
+    assert np.all(np.isfinite(runs[0][1]))
+    assert m.seq_length(0) == 512 + wl.decode_steps
+    # the first greedy tokens against the oracle's own greedy loop
+    toks, lgs = o.generate_greedy(prompt, 3)
+    for i in range(4):
+        rms = float(np.sqrt(np.mean(lgs[i] ** 2)))
+        assert margin_ok(lgs[i], int(runs[0][0][i]), TOL * rms), f"greedy step {i}"
+        if runs[0][0][i] != toks[i]:
+            _say(f"near-tie at greedy step {i}: runs continue from different tokens")
+            break
+
+
+def test_workload_batch32_prefix2048_sampled_sequences():
+    wl = q3synth.WORKLOADS["q06b_bf16_b32_p2048_d128"]
+    d = wl.dims
+    w = weights_for(d, wl.seed)
+    prompts = _prompts(wl, d)
+    B = wl.n_seqs
+    forced = [q3synth.make_tokens(3, d.vocab, wl.seed + 500 + b).tolist() for b in range(B)]
+    m = _model(d, max_slots=B, max_positions=2048 + 8, max_prefill_tokens=B * 2048, kv_tokens=B * 2112)
+    m.load_weights(w)
+    for s in range(B):
+        m.seq_alloc(s, 2048 + 8)
+    got = _prefill_then_forced(m, list(range(B)), prompts, forced)
+    assert m.error_flags() == 0
+    assert np.all(np.isfinite(got))
+    _say("gpu done; oracle on sampled sequences")
+    o = OracleModel(d, w)
+    for b in (0, 19):
+        ref = o.forced_logits(prompts[b], forced[b])
+        errs = [_check(ref[i], got[i][b], f"seq {b} step {i}") for i in range(len(ref))]
+        _say(f"seq {b} errors:", ["%.2e" % e for e in errs])
+
+
+def test_workload_32k_prompt_one_layer_cut_and_properties():
+    wl = q3synth.WORKLOADS["q06b_bf16_p32768_d32"]
+    L = wl.prompt_len
+    # (a) one-layer cut at the full length against the oracle
+    d1 = wl.dims.replace(n_layers=1)
+    w1 = weights_for(d1, wl.seed)
+    prompt = q3synth.make_tokens(L, d1.vocab, wl.seed + 1).tolist()
+    forced = q3synth.make_tokens(2, d1.vocab, wl.seed + 9).tolist()
+    m = _model(d1, max_slots=1, max_positions=L + 64, max_prefill_tokens=L, kv_tokens=L + 64)
+    m.load_weights(w1)
+    m.seq_alloc(0, L + 64)
+    got = _prefill_then_forced(m, [0], [prompt], [forced])
+    _say("1-layer gpu done; oracle")
+    ref = OracleModel(d1, w1).forced_logits(prompt, forced)
+    for i in range(len(ref)):
+        _check(ref[i], got[i][0], f"1-layer step {i}")
+    m.close()
+    del m
+    # (b) full depth: decode after prefill(L-1) equals prefill(L), on the GPU
+    d = wl.dims
+    w = weights_for(d, wl.seed)
+    prompt = q3synth.make_tokens(L, d.vocab, wl.seed + 1).tolist()
+    m = _model(d, max_slots=2, max_positions=L + 64, max_prefill_tokens=L, kv_tokens=2 * (L + 64))
+    m.load_weights(w)
+    m.seq_alloc(0, L + 64)
+    m.seq_alloc(1, L + 64)
+    full, _ = m.prefill([0], [prompt])
+    part = _prefill_then_forced(m, [1], [prompt[:-1]], [[prompt[-1]]])
+    with torch.cuda.stream(m.stream):
+        a = full[0].clone()
+    m.synchronize()
+    a = a.cpu().numpy()
+    b = part[1][0]
+    assert np.all(np.isfinite(a))
+    assert rel_err(b, a) <= TOL, rel_err(b, a)
+    assert m.error_flags() == 0
+
+
+def test_workload_ragged64_sampled_sequences():
+    wl = q3synth.WORKLOADS["q06b_bf16_b64_ragged_d128"]
+    d = wl.dims
+    w = weights_for(d, wl.seed)
+    prompts = _prompts(wl, d)
+    lens = [len(p) for p in prompts]
+    B = wl.n_seqs
+    T = sum(lens)
+    forced = [q3synth.make_tokens(2, d.vocab, wl.seed + 900 + b).tolist() for b in range(B)]
+    cap = max(lens) + 8
+    kv = sum((L + 8 + 63) // 64 * 64 for L in lens)
+    m = _model(d, max_slots=B, max_positions=cap, max_prefill_tokens=T, kv_tokens=kv)
+    m.load_weights(w)
+    for s in range(B):
+        m.seq_alloc(s, lens[s] + 8)
+    got = _prefill_then_forced(m, list(range(B)), prompts, forced)
+    assert m.error_flags() == 0
+    assert np.all(np.isfinite(got))
+    _say(f"gpu done ({T} prompt tokens); oracle on sampled sequences")
+    o = OracleModel(d, w)
+    order = np.argsort(lens)
+    for b in (int(order[0]), int(order[len(order) // 8])):
+        ref = o.forced_logits(prompts[b], forced[b])
+        errs = [_check(ref[i], got[i][b], f"seq {b} (len {lens[b]}) step {i}") for i in range(len(ref))]
+        _say(f"seq {b} len {lens[b]} errors:", ["%.2e" % e for e in errs])
