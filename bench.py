@@ -186,6 +186,14 @@ def main():
     k1.record(m.stream)
     torch.cuda.synchronize()
     per_launch_ms = k0.elapsed_time(k1) / args.kernel_reps
+    # A plain 256 MiB device copy: the reference that scales the profiler's
+    # FETCH_SIZE / WRITE_SIZE counters to bytes (see the profiles directory).
+    with torch.cuda.stream(m.stream):
+        c_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        c_dst = torch.empty_like(c_src)
+        c_dst.copy_(c_src)
+    torch.cuda.synchronize()
+    del c_src, c_dst
     alg_bytes = N * K * 2 + M * K * 2 + M * N * 4 + (N // 16) * M * 8
     achieved = alg_bytes / (per_launch_ms / 1e3) / 1e9
 

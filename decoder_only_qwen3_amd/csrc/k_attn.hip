@@ -404,6 +404,240 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   o[(int64_t)bh * 128 + d] = f2bf(acc / L);
 }
 
+// ---------------------------------------------------------------- fused decode
+// Decode attention with the QK-Norm + RoPE + cache append of Pasos 4-5 folded
+// in, spread over many single-wavefront blocks.  Block (split j, kv head g,
+// sequence b):
+//   A. normalise and rotate the group's query heads from the fused projection
+//      row (into LDS, bf16); the block whose key range holds the new position
+//      also normalises/rotates the new key and stores it and the new value
+//      into the cache;
+//   B. attend over its run of keys (MFMA, as in decode_attn_kernel);
+//   C. one split: write the normalised output.  Several splits: publish a
+//      (max, sum, output) partial with device-coherent stores, count the
+//      finished splits of this (b, g) on a device-coherent counter, and let
+//      the last block merge the partials in split order (deterministic) and
+//      write the output; it also re-arms the counter.
+// The splits publish and read their partials with agent-scope atomic loads
+// and stores (coherent across the GPU's L2 slices) instead of device-wide
+// fences, which on gfx950 would write back and invalidate whole L2 caches.
+// The launch fixes `smax`; the number of splits used and the keys per split
+// follow the sequence's current length on the device.
+struct RopeArgs {
+  const float* qn;
+  const float* kn;
+  const float* cos_t;
+  const float* sin_t;
+  float eps;
+};
+
+struct FusedGeom {
+  int nact;   // non-empty splits
+  int cb;     // keys per split (multiple of 32)
+};
+
+Q3_DEV FusedGeom fused_geom(int ctx, int smax) {
+  int cb = (ctx + smax - 1) / smax;
+  cb = max(128, (cb + 127) & ~127);  // whole 32-key runs for each of the 4 wavefronts
+  return FusedGeom{(ctx + cb - 1) / cb, cb};
+}
+
+Q3_DEV float ld_agent(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+Q3_DEV void st_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Per-head RMSNorm + rotate-half RoPE of one 128-wide head held as lanes
+// (l, l+64); the rotated pair replaces (a, c).
+Q3_DEV void norm_rope_pair(float& a, float& c, const float* w, float eps, float cs, float sn) {
+  const float ss = wave_sum(a * a + c * c);
+  const float inv = rsqrtf(ss * (1.f / 128.f) + eps);
+  const int lane = threadIdx.x & 63;
+  a = a * inv * w[lane];
+  c = c * inv * w[lane + 64];
+  const float ra = a * cs - c * sn, rc = a * sn + c * cs;
+  a = ra;
+  c = rc;
+}
+
+constexpr int FW = 4;  // wavefronts per fused decode block
+
+__global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
+    const float* __restrict__ qkv, SeqBatch sb, const SeqState* __restrict__ st, bf16_t* __restrict__ kv,
+    int layer, int n_q, int n_kv, RopeArgs ra, int smax, float* __restrict__ part, uint32_t* __restrict__ cnt,
+    bf16_t* __restrict__ o, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[8 * 128];
+  __shared__ float wred[FW][8][PSTRIDE];
+  __shared__ float wsh[64];
+  __shared__ int last;
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, fr = lane & 15, fq = lane >> 4;
+  const int group = n_q / n_kv;
+  const SeqState s = st[sb.slot[b]];
+  const int pos = s.len, ctx = pos + 1;
+  const FusedGeom fg = fused_geom(ctx, smax);
+  if (j >= fg.nact) return;
+  const int k_begin = j * fg.cb, k_end = min(ctx, k_begin + fg.cb);
+  const KvGeom geo{n_kv, layer};
+  bf16_t* Kc = kv_k(kv, s, geo, g);
+  bf16_t* Vt = kv_vt(kv, s, geo, g);
+
+  // A: wavefront u handles unit u, u+FW, ...: the group's query heads, then
+  // (in the block holding the new position) the new key and value.
+  const int units = n_q + 2 * n_kv;
+  const float* row = qkv + (int64_t)b * units * 128;
+  const float cs = ra.cos_t[(int64_t)pos * 64 + lane], sn = ra.sin_t[(int64_t)pos * 64 + lane];
+  const bool owns = pos >= k_begin && pos < k_end;
+  for (int u = wid; u < group + (owns ? 1 : 0); u += FW) {
+    if (u < group) {
+      const int h = g * group + u;
+      float a = row[h * 128 + lane], c = row[h * 128 + lane + 64];
+      norm_rope_pair(a, c, ra.qn, ra.eps, cs, sn);
+      qs[u * 128 + lane] = f2bf(a);
+      qs[u * 128 + lane + 64] = f2bf(c);
+    } else {
+      float a = row[(n_q + g) * 128 + lane], c = row[(n_q + g) * 128 + lane + 64];
+      norm_rope_pair(a, c, ra.kn, ra.eps, cs, sn);
+      Kc[(int64_t)pos * 128 + lane] = f2bf(a);
+      Kc[(int64_t)pos * 128 + lane + 64] = f2bf(c);
+      const float va = row[(n_q + n_kv + g) * 128 + lane], vc = row[(n_q + n_kv + g) * 128 + lane + 64];
+      Vt[(int64_t)lane * s.cap + pos] = f2bf(va);
+      Vt[(int64_t)(lane + 64) * s.cap + pos] = f2bf(vc);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the new key/value are stored before the loads below
+  __syncthreads();
+
+  // B: this wavefront's share of the block's keys.
+  const int cw = fg.cb / FW;
+  const int w0 = k_begin + wid * cw, w1 = min(k_end, w0 + cw);
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (fr < group) v = *reinterpret_cast<const u32x4*>(&qs[fr * 128 + ks * 32 + fq * 8]);
+    qf[ks] = as_bf16x8(v);
+  }
+  f32x4 oacc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int c0 = w0; c0 < w1; c0 += 32) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk) {
+      sacc[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = min(c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), w1 - 1);
+      const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16(kp + ks * 32)), qf[ks], sacc[sbk]);
+    }
+    u32x4 vraw[8];
+    const int vkey0 = c0 + fq * 8;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) vraw[d] = mask_keys(ld16(Vt + (int64_t)(d * 16 + fr) * s.cap + vkey0), vkey0, w1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sacc[sbk][r] * scale_log2;
+        if (c0 + 8 * fq + 4 * sbk + r >= w1) v = -INFINITY;
+        sacc[sbk][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = exp2_f(mrun - mnew);
+    mrun = mnew;
+#pragma unroll
+    for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[sbk][r] = exp2_f(sacc[sbk][r] - mnew);
+    const f16x8 pf = pack_p(sacc[0], sacc[1]);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls += sacc[0][r] + sacc[1][r];
+    lrun = lrun * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(vraw[d])), pf, oacc[d] * alpha);
+  }
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  if (fr < group) {
+    float* wp = wred[wid][fr];
+    if (fq == 0) {
+      wp[0] = mrun;
+      wp[1] = lrun;
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wp[2 + d * 16 + fq * 4 + r] = oacc[d][r];
+  }
+  __syncthreads();
+
+  // C: merge the block's wavefronts in order; then output or publish.
+  for (int e = tid; e < group * 128; e += 64 * FW) {
+    const int hh = e >> 7, d = e & 127;
+    float M = -INFINITY;
+    for (int w = 0; w < FW; ++w) M = fmaxf(M, wred[w][hh][0]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < FW; ++w) {
+      if (wred[w][hh][0] == -INFINITY) continue;
+      const float wt = exp2_f(wred[w][hh][0] - M);
+      L += wred[w][hh][1] * wt;
+      A += wred[w][hh][2 + d] * wt;
+    }
+    const int h = g * group + hh;
+    if (fg.nact == 1) {
+      o[((int64_t)b * n_q + h) * 128 + d] = f2bf(A / L);
+    } else {
+      float* pp = part + (((int64_t)b * n_q + h) * smax + j) * PSTRIDE;
+      if (d == 0) {
+        st_agent(pp, M);
+        st_agent(pp + 1, L);
+      }
+      st_agent(pp + 2 + d, A);
+    }
+  }
+  if (fg.nact == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);  // partial stores complete before the count below
+  __syncthreads();
+  uint32_t* c = cnt + (int64_t)b * n_kv + g;
+  if (tid == 0) last = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(fg.nact - 1);
+  __syncthreads();
+  if (!last) return;
+  // Last block of (b, g): merge the splits of each head in split order.
+  for (int e = tid; e < group * 128; e += 64 * FW) {
+    const int hh = e >> 7, d = e & 127;
+    const float* pp = part + ((int64_t)b * n_q + g * group + hh) * smax * PSTRIDE;
+    float mj[8], lj[8], aj[8];
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int j0 = 0; j0 < fg.nact; j0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = min(j0 + u, fg.nact - 1);
+        const float* q = pp + (int64_t)jj * PSTRIDE;
+        mj[u] = ld_agent(q);
+        lj[u] = ld_agent(q + 1);
+        aj[u] = ld_agent(q + 2 + d);
+      }
+      // running merge in split order
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= fg.nact) break;
+        const float mn = fmaxf(M, mj[u]);
+        const float so = exp2_f(M - mn), sj = exp2_f(mj[u] - mn);
+        L = L * so + lj[u] * sj;
+        A = A * so + aj[u] * sj;
+        M = mn;
+      }
+    }
+    o[((int64_t)b * n_q + g * group + hh) * 128 + d] = f2bf(A / L);
+  }
+  if (tid == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- float32
 constexpr int F32_MAX_CTX = 8192;
 
@@ -495,6 +729,30 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine_kernel<<<sb.n * n_q, 128, 0, s>>>(part, sb, st, n_q, splits, o);
+  return hipGetLastError();
+}
+
+int fused_attn_smax(int B, int n_kv, int64_t max_ctx) {
+  // about 512 four-wavefront blocks, at least 128 keys each, at most 64 splits
+  int64_t by_len = (max_ctx + 127) / 128;
+  int64_t want = (512 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
+  int64_t sm = by_len < want ? by_len : want;
+  if (sm > 64) sm = 64;
+  return sm < 1 ? 1 : (int)sm;
+}
+
+hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
+                             int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,
+                             const float* sin_t, int smax, float* part, uint32_t* counters, bf16_t* o,
+                             hipStream_t s) {
+  if (sb.n <= 0) return hipSuccess;
+  const int group = n_q / n_kv;
+  if (group < 1 || group > 8) return hipErrorInvalidValue;
+  const float scale_log2 = kLog2e / sqrtf(128.f);
+  RopeArgs ra{qn, kn, cos_t, sin_t, eps};
+  dim3 grid(smax, n_kv, sb.n);
+  decode_attn_fused_kernel<<<grid, 64 * FW, 0, s>>>(qkv, sb, st, kv, layer, n_q, n_kv, ra, smax, part, counters,
+                                                    o, scale_log2);
   return hipGetLastError();
 }
 

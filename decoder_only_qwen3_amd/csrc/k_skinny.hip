@@ -58,26 +58,29 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
 
   float* red = smem;                                  // [nw][RG][MT][256]
   float* inv = smem + nw * RG * MT * 256;             // [kNormMaxM] (NORM only)
+  // NORM: this wavefront's slice of the float32 residual rows, loaded once;
+  // the row sums of squares are reduced from the slices across wavefronts.
+  float4 xs[NORM ? MT : 1][NORM ? NST : 1][2];
   if constexpr (NORM) {
-    // Sums of squares of the M residual rows, reduced over the block.
     const float* x = reinterpret_cast<const float*>(Xin);
-    float ss[kNormMaxM];
+    const int m = lane & 15;  // MT == 1 when NORM (M <= 8)
+    float ss = 0.f;
 #pragma unroll
-    for (int m = 0; m < kNormMaxM; ++m) ss[m] = 0.f;
-    for (int k = threadIdx.x * 4; k < K; k += blockDim.x * 4) {
-#pragma unroll
-      for (int m = 0; m < kNormMaxM; ++m) {
-        if (m < M) {
-          const float4 v = *reinterpret_cast<const float4*>(x + (int64_t)m * K + k);
-          ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
+    for (int s2 = 0; s2 < NST; ++s2) {
+      if (m < M) {
+        const float* xp = x + (int64_t)m * K + k0 + s2 * 32;
+        xs[0][s2][0] = *reinterpret_cast<const float4*>(xp);
+        xs[0][s2][1] = *reinterpret_cast<const float4*>(xp + 4);
+      } else {
+        xs[0][s2][0] = xs[0][s2][1] = float4{0.f, 0.f, 0.f, 0.f};
       }
+      const float4 a = xs[0][s2][0], b = xs[0][s2][1];
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
     }
-#pragma unroll
-    for (int m = 0; m < kNormMaxM; ++m) {
-      const float t = wave_sum(ss[m]);
-      if (lane == 0) red[wid * kNormMaxM + m] = t;
-    }
+    // lanes m, m+16, m+32, m+48 hold row m's four K groups
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (lane < kNormMaxM) red[wid * kNormMaxM + lane] = ss;
     __syncthreads();
     if (threadIdx.x < kNormMaxM) {
       float t = 0.f;
@@ -101,9 +104,8 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
       u32x4 xv = {0u, 0u, 0u, 0u};
       if constexpr (NORM) {
         if (live) {
-          const float* xp = reinterpret_cast<const float*>(Xin) + (int64_t)m * K + k0 + s * 32;
-          const float4 a = *reinterpret_cast<const float4*>(xp);
-          const float4 b = *reinterpret_cast<const float4*>(xp + 4);
+          const float4 a = xs[0][s][0];
+          const float4 b = xs[0][s][1];
           const float4 ga = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32);
           const float4 gb = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32 + 4);
           const float r = inv[m];
@@ -261,6 +263,91 @@ hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, in
     case EPI_ARGMAX: return launch_norm<EPI_ARGMAX>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- row-parallel decode GEMV
+// One wavefront per output row for M <= 4 activation rows: lane l reads
+// 16-byte runs W[n][k .. k+8) at k = 8*l + 512*i (the whole row in flight at
+// once), multiplies them with the matching bf16 activations by packed bf16
+// dot products (fp32 accumulate) and the wavefront sums its lanes.  No
+// cross-wavefront or cross-block reduction, so matrices with few rows (the
+// 1024-row o and down projections) still spread over every CU.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int EPI, int MR, int KS>
+__global__ __launch_bounds__(256) void rowdot_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
+                                                     int N, int K, float* __restrict__ out, int64_t ldo) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const bf16_t* wr = W + (int64_t)n * K + lane * 8;
+  u32x4 wv[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) wv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + i * 512));
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    acc[m] = 0.f;
+    const bf16_t* xr = X + (int64_t)m * K + lane * 8;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const u32x4 xv = ld16(xr + i * 512);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // element copies first: bit-casting a vector element in place picked
+        // the wrong element in this compiler
+        const uint32_t wu = wv[i][c], xu = xv[c];
+        acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wu), __builtin_bit_cast(bf16x2_t, xu),
+                                                 acc[m], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const float v = wave_sum(acc[m]);
+    if (lane == 0) {
+      float* o = out + (int64_t)m * ldo + n;
+      if constexpr (EPI == EPI_RESADD) *o += v; else *o = v;
+    }
+  }
+}
+
+bool rowdot_ok(int M, int K) { return M >= 1 && M <= 4 && K % 512 == 0 && K / 512 <= 8; }
+
+template <int EPI, int MR>
+hipError_t rowdot_ks(int KS, dim3 grid, const bf16_t* X, const bf16_t* W, int N, int K, float* out, int64_t ldo,
+                     hipStream_t s) {
+  switch (KS) {
+    case 1: rowdot_kernel<EPI, MR, 1><<<grid, 256, 0, s>>>(X, W, N, K, out, ldo); break;
+    case 2: rowdot_kernel<EPI, MR, 2><<<grid, 256, 0, s>>>(X, W, N, K, out, ldo); break;
+    case 4: rowdot_kernel<EPI, MR, 4><<<grid, 256, 0, s>>>(X, W, N, K, out, ldo); break;
+    case 6: rowdot_kernel<EPI, MR, 6><<<grid, 256, 0, s>>>(X, W, N, K, out, ldo); break;
+    case 8: rowdot_kernel<EPI, MR, 8><<<grid, 256, 0, s>>>(X, W, N, K, out, ldo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t rowdot_m(int M, int KS, dim3 grid, const bf16_t* X, const bf16_t* W, int N, int K, float* out,
+                    int64_t ldo, hipStream_t s) {
+  switch (M) {
+    case 1: return rowdot_ks<EPI, 1>(KS, grid, X, W, N, K, out, ldo, s);
+    case 2: return rowdot_ks<EPI, 2>(KS, grid, X, W, N, K, out, ldo, s);
+    case 3: return rowdot_ks<EPI, 3>(KS, grid, X, W, N, K, out, ldo, s);
+    default: return rowdot_ks<EPI, 4>(KS, grid, X, W, N, K, out, ldo, s);
+  }
+}
+
+hipError_t rowdot_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, float* out, int64_t ldo,
+                       hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!rowdot_ok(M, K) || (epi != EPI_STORE && epi != EPI_RESADD)) return hipErrorInvalidValue;
+  const int KS = K / 512;
+  if (KS != 1 && KS != 2 && KS != 4 && KS != 6 && KS != 8) return hipErrorInvalidValue;
+  dim3 grid((N + 3) / 4);
+  if (epi == EPI_RESADD) return rowdot_m<EPI_RESADD>(M, KS, grid, X, W, N, K, out, ldo, s);
+  return rowdot_m<EPI_STORE>(M, KS, grid, X, W, N, K, out, ldo, s);
 }
 
 // ---------------------------------------------------------------- float32 model

@@ -62,6 +62,11 @@ int skinny_argmax_blocks(int N);
 // per-block (max, index) partials, N/16 blocks x M.
 hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
                        float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s);
+// Row-parallel bf16 GEMV for decode with M <= 4 rows: one wavefront per
+// output row (EPI_STORE / EPI_RESADD), K a multiple of 512 up to 4096.
+bool rowdot_ok(int M, int K);
+hipError_t rowdot_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, float* out, int64_t ldo,
+                       hipStream_t s);
 // float32 weights and activations (the float32 model); any M.
 hipError_t gemv_f32(int epi, const float* X, int M, const float* W, int N, int K, void* out,
                     int64_t ldo, hipStream_t s);
@@ -74,6 +79,16 @@ int decode_attn_splits(int B, int n_kv, int64_t max_ctx);
 hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, const bf16_t* kv,
                        int layer, int n_q, int n_kv, int splits, float* part, bf16_t* o,
                        hipStream_t s);
+// Decode attention with QK-Norm + RoPE + cache append folded in; reads the
+// fused projection rows qkv [B][(n_q+2n_kv)*128] float32.  `smax` splits per
+// (sequence, kv head) at most (fused_attn_smax); partials need
+// B * n_q * smax * 130 floats and `counters` B * n_kv zeroed words (left
+// zeroed by the kernel).
+int fused_attn_smax(int B, int n_kv, int64_t max_ctx);
+hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
+                             int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,
+                             const float* sin_t, int smax, float* part, uint32_t* counters, bf16_t* o,
+                             hipStream_t s);
 hipError_t attn_f32(const float* q, int T, const SeqBatch& sb, const SeqState* st,
                     const float* kv, int layer, int n_q, int n_kv, float* o, hipStream_t s);
 

@@ -144,6 +144,12 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
     }
     return Q3_OK;
   }
+  if (kernel == Q3OP_ROWDOT) {
+    if (!rowdot_ok(M, K) || (epi != EPI_STORE && epi != EPI_RESADD))
+      return op_fail(Q3_E_UNSUPPORTED, "the row GEMV takes M <= 4, K a multiple of 512, epilogue 0 or 1");
+    OP_TRY(rowdot_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, (float*)d_out, ldo, s));
+    return Q3_OK;
+  }
   if (kernel == Q3OP_SKINNY) {
     if (M > Q3_MAX_BATCH) return op_fail(Q3_E_UNSUPPORTED, "the weight-streaming kernel takes M <= 64");
     return skinny_op(epi, d_x, M, nullptr, 0.f, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, s);
@@ -248,6 +254,53 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
   } else {
     return op_fail(Q3_E_ARG, "unknown kernel");
   }
+  return Q3_OK;
+}
+
+size_t q3op_decode_attn_fused_workspace_bytes(int32_t n_seqs, int32_t n_q, int32_t smax, int32_t max_pos) {
+  return al(n_seqs * sizeof(SeqState)) + 2 * al((size_t)max_pos * 64 * 4) +
+         al((size_t)n_seqs * n_q * (smax > 0 ? smax : 64) * 130 * 4) + al((size_t)n_seqs * n_q * 4);
+}
+
+q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h_base, const int32_t* h_cap,
+                                 const int32_t* h_len, void* d_kv, int32_t n_q, int32_t n_kv, const float* d_qn,
+                                 const float* d_kn, float eps, double theta, int32_t max_pos, int32_t smax,
+                                 void* d_out, void* d_ws, size_t ws_bytes, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  SeqBatch sb;
+  q3_status st = make_batch(n, nullptr, 1, &sb);
+  if (st != Q3_OK) return st;
+  if (!d_qkv || !d_kv || !d_qn || !d_kn || !d_out || !h_base || !h_cap || !h_len || max_pos <= 0)
+    return op_fail(Q3_E_ARG, "bad argument");
+  if (n_kv <= 0 || n_q % n_kv != 0 || n_q / n_kv > 8) return op_fail(Q3_E_UNSUPPORTED, "head grouping");
+  int64_t mc = 1;
+  for (int b = 0; b < n; ++b) {
+    if (h_len[b] + 1 > h_cap[b] || h_len[b] + 1 > max_pos) return op_fail(Q3_E_CAPACITY, "position beyond capacity");
+    mc = std::max<int64_t>(mc, h_cap[b]);
+  }
+  if (smax <= 0) smax = fused_attn_smax(n, n_kv, mc);
+  if (smax > 64) return op_fail(Q3_E_ARG, "smax must be <= 64");
+  if (!d_ws || ws_bytes < q3op_decode_attn_fused_workspace_bytes(n, n_q, smax, max_pos))
+    return op_fail(Q3_E_ARG, "workspace too small");
+  char* ws = (char*)d_ws;
+  st = upload_states(n, h_base, h_cap, h_len, ws, s);
+  if (st != Q3_OK) return st;
+  float* cos_t = (float*)(ws + al(n * sizeof(SeqState)));
+  float* sin_t = (float*)((char*)cos_t + al((size_t)max_pos * 64 * 4));
+  float* part = (float*)((char*)sin_t + al((size_t)max_pos * 64 * 4));
+  uint32_t* cnt = (uint32_t*)((char*)part + al((size_t)n * n_q * smax * 130 * 4));
+  OP_TRY(fill_u32(cnt, 0u, (int64_t)n * n_kv, s));
+  std::vector<float> cs((size_t)max_pos * 64), sn((size_t)max_pos * 64);
+  for (int p = 0; p < max_pos; ++p)
+    for (int i = 0; i < 64; ++i) {
+      const double a = (double)p * std::pow(theta, -(double)i / 64.0);
+      cs[(size_t)p * 64 + i] = (float)std::cos(a);
+      sn[(size_t)p * 64 + i] = (float)std::sin(a);
+    }
+  OP_TRY(hipMemcpy(cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+  OP_TRY(hipMemcpy(sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+  OP_TRY(decode_attn_fused(d_qkv, sb, (const SeqState*)ws, (bf16_t*)d_kv, 0, n_q, n_kv, d_qn, d_kn, eps, cos_t,
+                           sin_t, smax, part, cnt, (bf16_t*)d_out, s));
   return Q3_OK;
 }
 

@@ -51,7 +51,7 @@ struct WeightLayout {
 };
 
 struct WsLayout {
-  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, state, err, total;
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, state, err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
   int amax_blocks;
 };
@@ -115,8 +115,10 @@ WeightLayout weight_layout(const q3_config& c) {
 
 int max_attn_splits_rows(const q3_config& c) {
   int best = 0;
-  for (int B = 1; B <= Q3_MAX_BATCH; ++B)
+  for (int B = 1; B <= Q3_MAX_BATCH; ++B) {
     best = std::max(best, B * decode_attn_splits(B, c.n_kv_heads, c.max_positions));
+    best = std::max(best, B * fused_attn_smax(B, c.n_kv_heads, c.max_positions));
+  }
   return best;
 }
 
@@ -138,6 +140,7 @@ WsLayout ws_layout(const q3_config& c) {
   W.amax_val = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
   W.amax_idx = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
   W.attn_part = take((size_t)max_attn_splits_rows(c) * c.n_q_heads * 130 * 4);
+  W.attn_cnt = take((size_t)Q3_MAX_BATCH * c.n_kv_heads * 4);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -234,12 +237,14 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   RowMap all;
   all.n = -1;
   const bool bf = c.dtype == Q3_BF16;
-  int splits = 1;
+  int smax = 1;
   if (decode && bf) {
     int64_t maxcap = 1;
     for (int b = 0; b < sb.n; ++b) maxcap = std::max(maxcap, m->slots[sb.slot[b]].cap);
-    splits = decode_attn_splits(sb.n, c.n_kv_heads, std::min<int64_t>(maxcap, c.max_positions));
+    smax = fused_attn_smax(sb.n, c.n_kv_heads, std::min<int64_t>(maxcap, c.max_positions));
   }
+  const bool rows_o = bf && decode && rowdot_ok(T, Q);
+  const bool rows_d = bf && decode && rowdot_ok(T, I);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
     // Paso 3 + Paso 5: normalised input, fused q/k/v projection.  Decode with
@@ -254,16 +259,21 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else {
       LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, s));
     }
-    // QK-Norm, RoPE, cache append (Pasos 4-5).
-    LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
-                       m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s));
-    // Attention (Paso 5).
+    // QK-Norm, RoPE, cache append and attention (Pasos 4-5).  bf16 decode does
+    // all of it in one kernel; the other paths append first.
+    if (bf && decode) {
+      LAUNCH(decode_attn_fused(qkv, sb, m->state(), (bf16_t*)m->kv, l, c.n_q_heads, c.n_kv_heads,
+                               m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, smax,
+                               m->WS<float>(L.attn_part), m->WS<uint32_t>(L.attn_cnt), (bf16_t*)ob, s));
+    } else {
+      LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
+                         m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s));
+    }
     if (!bf) {
       LAUNCH(attn_f32((const float*)qb, T, sb, m->state(), (const float*)m->kv, l, c.n_q_heads, c.n_kv_heads,
                       (float*)ob, s));
     } else if (decode) {
-      LAUNCH(decode_attn((const bf16_t*)qb, sb, m->state(), (const bf16_t*)m->kv, l, c.n_q_heads, c.n_kv_heads,
-                         splits, m->WS<float>(L.attn_part), (bf16_t*)ob, s));
+      // done above
     } else {
       LAUNCH(flash_prefill((const bf16_t*)qb, T, sb, m->state(), (const bf16_t*)m->kv, l, c.n_q_heads,
                            c.n_kv_heads, (bf16_t*)ob, s));
@@ -271,6 +281,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     // Output projection + residual (Paso 5 end, Paso 7).
     if (!bf) {
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
+    } else if (rows_o) {
+      LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
     } else if (decode) {
       LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s));
     } else {
@@ -284,7 +296,10 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else if (decode) {
       LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.gu), 2 * I, H,
                          fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps, mb, I, nullptr, nullptr, s));
-      LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s));
+      if (rows_d)
+        LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
+      else
+        LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s));
     } else {
       LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
@@ -413,6 +428,7 @@ q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, voi
   std::vector<SeqState> zero(c.max_slots, SeqState{0, 0, 0});
   HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
   HIP_TRY(fill_u32(m->err(), 0u, 4, s));
+  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.attn_cnt), 0u, (int64_t)Q3_MAX_BATCH * c.n_kv_heads, s));
   HIP_TRY(hipStreamSynchronize(s));
   m->bound = true;
   g_err.clear();

@@ -1,0 +1,137 @@
+"""Single-kernel timing harness (HIP events) for libq3's kernels at the
+Qwen3-0.6B shapes, through the entry points of include/q3_ops.h.
+
+    python -m decoder_only_qwen3_amd.kbench [--kernels lm_head,qkv,...] [--reps 50]
+
+Prints one JSON object per kernel: average launch time, algorithmic bytes or
+FLOPs per launch and the achieved rate against the MI355X peak (HBM 8 TB/s,
+dense bf16 MFMA 2.5 PFLOP/s).  It also runs one 256 MiB device copy, the
+reference for scaling profiler byte counters.  Inputs are random (the
+numbers produced are not checked here; the parity tests do that).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+
+import torch
+
+from . import _lib
+
+HBM = 8000.0
+MFMA = 2500.0
+H, Q, KVW, I, V = 1024, 2048, 1024, 3072, 151936
+
+
+def _rand_bf16(shape, scale=1.0):
+    return (torch.randn(shape, device="cuda:0") * scale).to(torch.bfloat16).view(torch.int16)
+
+
+def _time(fn, reps, stream):
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3  # microseconds
+
+
+def linear_case(lib, name, epi, M, N, K, reps, stream, kernel=1):
+    x = _rand_bf16((M, K))
+    w = _rand_bf16((N, K), 0.02)
+    if epi == 2:
+        out = torch.empty((M, N // 2), dtype=torch.int16, device="cuda:0")
+        ldo = N // 2
+    else:
+        out = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
+        ldo = N
+    ws = torch.zeros(max(256, lib.q3op_linear_workspace_bytes(kernel, epi, M, N, K)), dtype=torch.uint8,
+                     device="cuda:0")
+    sh = stream.cuda_stream
+
+    def fn():
+        _lib.check(lib.q3op_linear(kernel, epi, x.data_ptr(), M, w.data_ptr(), N, K, out.data_ptr(), ldo, None,
+                                   ws.data_ptr(), ws.numel(), sh))
+    us = _time(fn, reps, stream)
+    if kernel == 1:
+        out_b = M * N * 4 if epi != 2 else M * (N // 2) * 2
+        byts = N * K * 2 + M * K * 2 + out_b + (M * N * 4 if epi == 1 else 0)
+        return {"kernel": name, "M": M, "N": N, "K": K, "us": round(us, 2), "bytes": byts,
+                "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
+    fl = 2 * M * N * K
+    return {"kernel": name, "M": M, "N": N, "K": K, "us": round(us, 2), "flops": fl,
+            "TFLOPs": round(fl / us / 1e6, 1), "mfma_frac": round(fl / us / 1e6 / MFMA, 4)}
+
+
+def attention_case(lib, name, kernel, L, B, reps, stream):
+    n_q, n_kv = 16, 8
+    cap = (L + 1 + 63) // 64 * 64
+    region = 2 * n_kv * cap * 128
+    kv = _rand_bf16((B * region,))
+    bases = [b * region for b in range(B)]
+    if kernel == 0:
+        cu = [b * L for b in range(B + 1)]
+        q = _rand_bf16((B * L, n_q, 128))
+        out = torch.empty_like(q)
+        lens, decode = [0] * B, 0
+    else:
+        cu = list(range(B + 1))
+        q = _rand_bf16((B, n_q, 128))
+        out = torch.empty_like(q)
+        lens, decode = [L] * B, 1
+    ws = torch.zeros(max(256, lib.q3op_attention_workspace_bytes(kernel, B, n_q, 0)), dtype=torch.uint8,
+                     device="cuda:0")
+    sh = stream.cuda_stream
+    a_cu, a_b, a_c, a_l = _lib.i32_array(cu), _lib.i64_array(bases), _lib.i32_array([cap] * B), _lib.i32_array(lens)
+
+    def fn():
+        _lib.check(lib.q3op_attention(kernel, q.data_ptr(), B, a_cu, decode, a_b, a_c, a_l, kv.data_ptr(),
+                                      n_q, n_kv, 0, out.data_ptr(), ws.data_ptr(), ws.numel(), sh))
+    us = _time(fn, reps, stream)
+    if kernel == 0:
+        fl = B * 4 * n_q * 128 * L * (L + 1) // 2
+        return {"kernel": name, "L": L, "B": B, "us": round(us, 2), "flops": fl,
+                "TFLOPs": round(fl / us / 1e6, 1), "mfma_frac": round(fl / us / 1e6 / MFMA, 4)}
+    byts = B * (L + 1) * n_kv * 128 * 2 * 2
+    return {"kernel": name, "ctx": L + 1, "B": B, "us": round(us, 2), "bytes": byts,
+            "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
+
+
+CASES = {
+    "lm_head": lambda lib, r, s: linear_case(lib, "lm_head", 3, 1, V, H, r, s),
+    "qkv": lambda lib, r, s: linear_case(lib, "qkv", 0, 1, Q + 2 * KVW, H, r, s),
+    "o": lambda lib, r, s: linear_case(lib, "o", 1, 1, H, Q, r, s),
+    "gate_up": lambda lib, r, s: linear_case(lib, "gate_up", 2, 1, 2 * I, H, r, s),
+    "down": lambda lib, r, s: linear_case(lib, "down", 1, 1, H, I, r, s),
+    "lm_head_b64": lambda lib, r, s: linear_case(lib, "lm_head_b64", 3, 64, V, H, r, s),
+    "gemm_qkv_32k": lambda lib, r, s: linear_case(lib, "gemm_qkv_32k", 0, 32768, Q + 2 * KVW, H, r, s, kernel=0),
+    "gemm_gate_up_32k": lambda lib, r, s: linear_case(lib, "gemm_gate_up_32k", 2, 32768, 2 * I, H, r, s, kernel=0),
+    "gemm_down_32k": lambda lib, r, s: linear_case(lib, "gemm_down_32k", 1, 32768, H, I, r, s, kernel=0),
+    "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
+    "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),
+    "decode_attn_b64_8k": lambda lib, r, s: attention_case(lib, "decode_attn_b64_8k", 1, 8191, 64, r, s),
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--kernels", default="lm_head,qkv,o,gate_up,down")
+    ap.add_argument("--reps", type=int, default=50)
+    args = ap.parse_args()
+    lib = _lib.load()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for k in args.kernels.split(","):
+            print(json.dumps(CASES[k](lib, args.reps, stream)), flush=True)
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "copy_calibration", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4}))
+
+
+if __name__ == "__main__":
+    main()

@@ -44,10 +44,13 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  *     kernel's per-block (max, index) partials are produced (one launch).
  * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0);
  * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
- * kernel 2 = float32 GEMV (float32 model).  bf16 kernels take bf16 X and W. */
+ * kernel 2 = float32 GEMV (float32 model);
+ * kernel 3 = bf16 row-per-wavefront GEMV (decode with M <= 4, epi 0 or 1,
+ * K a multiple of 512).  bf16 kernels take bf16 X and W. */
 #define Q3OP_GEMM 0
 #define Q3OP_SKINNY 1
 #define Q3OP_GEMV_F32 2
+#define Q3OP_ROWDOT 3  /* bf16 row-per-wavefront GEMV (decode, M <= 4, epi 0-1) */
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K);
 q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
                       int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
@@ -92,6 +95,18 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n_seqs, const 
                          const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len, const void* d_kv,
                          int32_t n_q, int32_t n_kv, int32_t splits, void* d_out, void* d_ws, size_t ws_bytes,
                          void* stream);
+
+/* Pasos 4-5 for bf16 decode in one kernel: from the fused projection rows
+ * d_qkv [n_seqs][(n_q + 2 n_kv)*128] float32, the new token of sequence b sits
+ * at position h_len[b]; its key (QK-Norm + RoPE) and value are written into
+ * the arena above, and its queries (QK-Norm + RoPE) attend over keys
+ * 0..h_len[b]; output d_out [n_seqs][n_q][128] bf16.  `smax` <= 0 picks the
+ * library's split count. */
+size_t q3op_decode_attn_fused_workspace_bytes(int32_t n_seqs, int32_t n_q, int32_t smax, int32_t max_pos);
+q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64_t* h_base, const int32_t* h_cap,
+                                 const int32_t* h_len, void* d_kv, int32_t n_q, int32_t n_kv, const float* d_qn,
+                                 const float* d_kn, float eps, double theta, int32_t max_pos, int32_t smax,
+                                 void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

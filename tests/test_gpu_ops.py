@@ -83,7 +83,7 @@ def _linear(kernel, epi, X, W, out_init=None, ldo=None, want_next=False):
     mod, lib = ops()
     M, K = X.shape
     N = W.shape[0]
-    bf = kernel in (GEMM, SKINNY)
+    bf = kernel in (GEMM, SKINNY, 3)
     dx = dev_bf16(X) if bf else dev_f32(X)
     dw = dev_bf16(W) if bf else dev_f32(W)
     if epi == EPI_SWIGLU:
@@ -397,3 +397,75 @@ def test_norm_linear_fused_prologue(epi, M, N):
         if epi == EPI_ARGMAX:
             for m in range(M):
                 assert nxt.cpu().numpy()[m] == int(np.argmax(got[m]))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("N,K", [(1024, 2048), (1024, 3072), (4096, 1024)])
+def test_rowdot_gemv(M, N, K):
+    rng = np.random.default_rng(M * 13 + N + K)
+    X = rand_bf16(rng, (M, K))
+    W = rand_bf16(rng, (N, K), 0.02)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    got, _ = _linear(3, EPI_STORE, X, W)
+    assert _rel(got, ref) < 2e-5
+    base = rng.standard_normal((M, N)).astype(np.float32)
+    got, _ = _linear(3, EPI_RESADD, X, W, out_init=base)
+    assert _rel(got - base, ref) < 2e-5
+
+
+@pytest.mark.parametrize("prior,smax", [([0], 0), ([5, 700], 0), ([1500], 0), ([1500, 40], 3), ([32799], 0),
+                                        ([2047, 0, 4100], 0)])
+def test_decode_attention_fused_rope_append(prior, smax):
+    """QK-Norm + RoPE of the new token, its cache append, and attention over the
+    cache, in one kernel, against the oracle's functions."""
+    mod, lib = ops()
+    rng = np.random.default_rng(sum(prior) + smax)
+    n_q, n_kv, n = 16, 8, len(prior)
+    units = n_q + 2 * n_kv
+    caps = [((p + 1 + 63) // 64) * 64 for p in prior]
+    bases, total = _arena(caps, n_kv, 2)
+    arena = np.zeros(total, np.float32)
+    old_k, old_v = [], []
+    for b in range(n):
+        K = rand_bf16(rng, (prior[b], n_kv, 128))
+        V = rand_bf16(rng, (prior[b], n_kv, 128))
+        old_k.append(K)
+        old_v.append(V)
+        cap = caps[b]
+        region = np.zeros(2 * n_kv * cap * 128, np.float32)
+        region[:n_kv * cap * 128].reshape(n_kv, cap, 128)[:, :prior[b], :] = K.transpose(1, 0, 2)
+        region[n_kv * cap * 128:].reshape(n_kv, 128, cap)[:, :, :prior[b]] = V.transpose(1, 2, 0)
+        arena[bases[b]:bases[b] + region.size] = region
+    qkv = rng.standard_normal((n, units * 128)).astype(np.float32)
+    qn = q3synth.round_to_bf16((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+    kn = q3synth.round_to_bf16((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+    dkv = dev_bf16(arena)
+    dqkv, dqn, dkn = dev_f32(qkv), dev_f32(qn), dev_f32(kn)
+    out = torch.zeros((n, n_q, 128), dtype=torch.int16, device="cuda:0")
+    max_pos = max(prior) + 1
+    ws = _ws(lib.q3op_decode_attn_fused_workspace_bytes(n, n_q, smax, max_pos))
+    call(lib.q3op_decode_attn_fused(dqkv.data_ptr(), n, mod.i64_array(bases), mod.i32_array(caps),
+                                    mod.i32_array(prior), dkv.data_ptr(), n_q, n_kv, dqn.data_ptr(), dkn.data_ptr(),
+                                    1e-6, 1e6, max_pos, smax, out.data_ptr(), ws.data_ptr(), ws.numel(), None))
+    _sync()
+    got = host_bf16(out)
+    kv_got = host_bf16(dkv)
+    for b in range(n):
+        x = qkv[b].astype(np.float64).reshape(units, 128)[None]
+        c, s_ = rope_cos_sin([prior[b]], 128, 1e6)
+        q_hat = to_bf16(rope_rotate(rms_norm(x[:, :n_q], qn, 1e-6), c, s_))
+        k_new = to_bf16(rope_rotate(rms_norm(x[:, n_q:n_q + n_kv], kn, 1e-6), c, s_))
+        v_new = to_bf16(x[:, n_q + n_kv:])
+        cap = caps[b]
+        region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
+        Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        np.testing.assert_allclose(Kc[:, prior[b], :], k_new[0], rtol=2 ** -7, atol=1e-6)
+        np.testing.assert_array_equal(Vt[:, :, prior[b]], v_new[0].astype(np.float32))
+        keys = np.concatenate([old_k[b].astype(np.float64), k_new], axis=0)
+        vals = np.concatenate([old_v[b].astype(np.float64), v_new], axis=0)
+        ref = attention_rows(q_hat, keys, vals, np.array([prior[b]]), np.arange(prior[b] + 1))[0]
+        rms = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+        bound = 2.0 ** -8 * np.abs(ref) + 2e-3 * rms
+        # the kernel's own new key may differ from the oracle's by one bf16 ulp
+        assert float(np.max(np.abs(got[b] - ref) / (bound + 4e-3 * rms))) < 1.0, b
