@@ -24,7 +24,7 @@ EXPORTS = [
     "q3_last_error",
     "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear", "q3op_norm_linear",
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
-    "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused",
+    "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
 ]
 
 
@@ -91,6 +91,7 @@ def load() -> C.CDLL:
         "q3op_rope_workspace_bytes": (SZ, [I32, I32]),
         "q3op_rope_append": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP,
                                    C.c_float, C.c_double, I32, VP, VP, SZ, VP]),
+        "q3op_tune": (I32, [I32, I32]),
         "q3op_attention_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "q3op_decode_attn_fused_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "q3op_decode_attn_fused": (I32, [VP, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP, C.c_float, C.c_double,

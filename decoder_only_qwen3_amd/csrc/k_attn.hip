@@ -21,6 +21,8 @@
 // (relative error 2^-11, eight times finer than bf16) and the bf16 values are
 // converted to fp16 exactly.  The softmax denominator sums the rounded
 // weights, so the output is a properly normalised average of the values.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace q3k {
@@ -70,10 +72,12 @@ struct TileTable {
 };
 
 // Block: one kv head and one query tile of `qt` tokens of one sequence; its
-// 128 query rows are the group's query heads x qt tokens (row r -> head
-// r / qt, token r % qt).  4 wavefronts x 32 rows.  K and V^T tiles of 64 keys
-// are double-buffered in LDS and shared by the 4 wavefronts.
-__global__ __launch_bounds__(256) void flash_prefill_kernel(
+// 64*CB query rows are the group's query heads x qt tokens (row r -> head
+// r / qt, token r % qt).  4 wavefronts x 16*CB rows.  K and V^T tiles of 64
+// keys are double-buffered in LDS and shared by the 4 wavefronts; more rows
+// per wavefront means fewer LDS reads per MFMA.
+template <int CB>
+__global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
     const bf16_t* __restrict__ kv, int layer, int n_q, int n_kv, int qt, bf16_t* __restrict__ o,
     float scale_log2) {
@@ -102,12 +106,12 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
 
-  // Query fragments (B operand of S^T) for this wavefront's two 16-row blocks.
-  bf16x8 qf[2][4];
-  int qpos[2], qhead[2];
+  // Query fragments (B operand of S^T) for this wavefront's 16-row blocks.
+  bf16x8 qf[CB][4];
+  int qpos[CB], qhead[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = wid * 32 + cb * 16 + fr;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = wid * 16 * CB + cb * 16 + fr;
     const int hh = r / qt, tq = r - hh * qt;
     qpos[cb] = q0 + tq;
     qhead[cb] = g * group + hh;
@@ -144,12 +148,17 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
     }
   };
 
-  f32x4 oacc[8][2];
+  f32x4 oacc[8][CB];
 #pragma unroll
   for (int d = 0; d < 8; ++d)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) oacc[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun[CB], lrun[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    mrun[cb] = -INFINITY;
+    lrun[cb] = 0.f;
+  }
 
   gload(0);
   sstore(0);
@@ -159,25 +168,25 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
     if (kt + 1 < ntiles) gload(kt + 1);
 
     // S^T for the tile: sacc[c][sb][cb], keys kt*64 + c*32 + 8*fq + 4*sb + r.
-    f32x4 sacc[2][2][2];
+    f32x4 sacc[2][2][CB];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int sbk = 0; sbk < 2; ++sbk) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int krow = c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][krow * LDSK + ks * 32 + fq * 8]);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) sacc[c][sbk][cb] = mfma16(kf, qf[cb][ks], sacc[c][sbk][cb]);
+          for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf, qf[cb][ks], sacc[c][sbk][cb]);
         }
       }
 
     const bool diag = kt * KT + KT - 1 > q0 || kt * KT + KT > L;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -213,9 +222,9 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
     // O^T += V^T . P^T  (fp16 operands)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      f16x8 pf[2];
+      f16x8 pf[CB];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         pf[cb] = pack_p(sacc[c][0][cb], sacc[c][1][cb]);
         float ls = 0.f;
 #pragma unroll
@@ -226,7 +235,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
       for (int d = 0; d < 8; ++d) {
         const f16x8 vf = *reinterpret_cast<const f16x8*>(&sV[buf][(d * 16 + fr) * LDSV + c * 32 + fq * 8]);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) oacc[d][cb] = mfma16_f16(vf, pf[cb], oacc[d][cb]);
+        for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = mfma16_f16(vf, pf[cb], oacc[d][cb]);
       }
     }
 
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(
 
   // Normalise and store: lane holds dims d*16 + fq*4 + r of row (cb, fr).
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     float l = lrun[cb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
@@ -691,12 +700,21 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
 }
 }  // namespace
 
+namespace {
+int g_flash_cb = -1;  // rows-per-wavefront override (q3op_tune); -1 = automatic
+}
+void flash_set_rows(int cb) { g_flash_cb = cb; }
+
 hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
                          const bf16_t* kv, int layer, int n_q, int n_kv, bf16_t* o, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int group = n_q / n_kv;
   if (group < 1 || group > 8 || 128 % group != 0) return hipErrorInvalidValue;
-  const int qt = 128 / group;
+  // Rows per wavefront (16*CB).  CB = 1 keeps the kernel within 256 registers
+  // per lane, so two blocks share a CU; on gfx950 that beat the larger
+  // register tiles at every length measured (512 to 32768 keys).
+  const int CB = g_flash_cb < 0 ? 1 : g_flash_cb;
+  const int qt = 64 * CB / group;
   TileTable tt;
   tt.tile_cu[0] = 0;
   for (int b = 0; b < sb.n; ++b) {
@@ -707,7 +725,19 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   if (total <= 0) return hipSuccess;
   dim3 grid(total, n_kv);
   const float scale_log2 = kLog2e / sqrtf(128.f);
-  flash_prefill_kernel<<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+  switch (CB) {
+    case 4:
+      flash_prefill_kernel<4><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      break;
+    case 2:
+      flash_prefill_kernel<2><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      break;
+    case 1:
+      flash_prefill_kernel<1><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 // C[M,N] = A[M,K] . W[N,K]^T with bf16 operands on MFMA; K % 64 == 0.
 hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
                      int64_t ldo, hipStream_t s);
+void gemm_set_config(int cfg);  // tile configuration override; -1 = automatic
+void flash_set_rows(int cb);    // prefill attention rows per wavefront / 16 (1, 2, 4); -1 = automatic
 
 // ---------------------------------------------------------------- k_skinny.hip
 struct SkinnyPlan {

@@ -304,4 +304,19 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h
   return Q3_OK;
 }
 
+q3_status q3op_tune(int32_t key, int32_t value) {
+  if (key == Q3OP_TUNE_GEMM_TILES) {
+    if (value < -1 || value > 6) return op_fail(Q3_E_ARG, "tile configuration out of range");
+    gemm_set_config(value);
+    return Q3_OK;
+  }
+  if (key == Q3OP_TUNE_FLASH_ROWS) {
+    if (value != -1 && value != 1 && value != 2 && value != 4)
+      return op_fail(Q3_E_ARG, "rows per wavefront must be -1, 1, 2 or 4");
+    flash_set_rows(value);
+    return Q3_OK;
+  }
+  return op_fail(Q3_E_ARG, "unknown tuning key");
+}
+
 }  // extern "C"

@@ -110,6 +110,11 @@ CASES = {
     "gemm_qkv_32k": lambda lib, r, s: linear_case(lib, "gemm_qkv_32k", 0, 32768, Q + 2 * KVW, H, r, s, kernel=0),
     "gemm_gate_up_32k": lambda lib, r, s: linear_case(lib, "gemm_gate_up_32k", 2, 32768, 2 * I, H, r, s, kernel=0),
     "gemm_down_32k": lambda lib, r, s: linear_case(lib, "gemm_down_32k", 1, 32768, H, I, r, s, kernel=0),
+    "gemm_qkv_512": lambda lib, r, s: linear_case(lib, "gemm_qkv_512", 0, 512, Q + 2 * KVW, H, r, s, kernel=0),
+    "gemm_o_512": lambda lib, r, s: linear_case(lib, "gemm_o_512", 1, 512, H, Q, r, s, kernel=0),
+    "gemm_gate_up_512": lambda lib, r, s: linear_case(lib, "gemm_gate_up_512", 2, 512, 2 * I, H, r, s, kernel=0),
+    "gemm_down_512": lambda lib, r, s: linear_case(lib, "gemm_down_512", 1, 512, H, I, r, s, kernel=0),
+    "flash_512": lambda lib, r, s: attention_case(lib, "flash_512", 0, 512, 1, r, s),
     "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
     "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),
     "decode_attn_b64_8k": lambda lib, r, s: attention_case(lib, "decode_attn_b64_8k", 1, 8191, 64, r, s),
@@ -120,8 +125,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--kernels", default="lm_head,qkv,o,gate_up,down")
     ap.add_argument("--reps", type=int, default=50)
+    ap.add_argument("--gemm-tiles", type=int, default=-1, help="prefill GEMM tile configuration (-1 automatic)")
+    ap.add_argument("--flash-rows", type=int, default=-1, help="prefill attention rows per wavefront / 16")
     args = ap.parse_args()
     lib = _lib.load()
+    _lib.check(lib.q3op_tune(1, args.gemm_tiles))
+    _lib.check(lib.q3op_tune(2, args.flash_rows))
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for k in args.kernels.split(","):

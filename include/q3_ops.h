@@ -108,6 +108,16 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
                                  const float* d_kn, float eps, double theta, int32_t max_pos, int32_t smax,
                                  void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
+ * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.
+ * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,
+ *   0..6 = fixed tile shapes (listed in k_gemm.hip).
+ * Q3OP_TUNE_FLASH_ROWS: prefill attention query rows per wavefront / 16,
+ *   -1 = automatic, or 1, 2, 4. */
+#define Q3OP_TUNE_GEMM_TILES 1
+#define Q3OP_TUNE_FLASH_ROWS 2
+q3_status q3op_tune(int32_t key, int32_t value);
+
 #ifdef __cplusplus
 }
 #endif

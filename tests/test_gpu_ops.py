@@ -120,6 +120,37 @@ def test_linear_store_and_residual(kernel, M, N, K):
     assert _rel(got - base, ref) < 2e-5
 
 
+@pytest.mark.parametrize("cfg", list(range(7)))
+def test_gemm_tile_configurations(cfg):
+    """Every prefill GEMM tile shape, with ragged row and column tails."""
+    _, lib = ops()
+    call(lib.q3op_tune(1, cfg))
+    try:
+        M, N, K = 300, 1088, 1024
+        rng = np.random.default_rng(100 + cfg)
+        X = rand_bf16(rng, (M, K))
+        W = rand_bf16(rng, (N, K), 0.02)
+        ref = X.astype(np.float64) @ W.astype(np.float64).T
+        got, _ = _linear(GEMM, EPI_STORE, X, W)
+        assert _rel(got, ref) < 2e-5
+        base = rng.standard_normal((M, N)).astype(np.float32)
+        got, _ = _linear(GEMM, EPI_RESADD, X, W, out_init=base)
+        assert _rel(got - base, ref) < 2e-5
+        g, u = ref.reshape(M, N // 32, 2, 16)[:, :, 0, :], ref.reshape(M, N // 32, 2, 16)[:, :, 1, :]
+        act = (silu(g) * u).reshape(M, N // 2)
+        got, _ = _linear(GEMM, EPI_SWIGLU, X, W)
+        np.testing.assert_allclose(got, to_bf16(act), rtol=2.0 ** -7, atol=1e-6 * np.sqrt(np.mean(act ** 2)))
+    finally:
+        call(lib.q3op_tune(1, -1))
+
+
+def test_tune_rejects_bad_values():
+    _, lib = ops()
+    assert lib.q3op_tune(1, 7) != 0
+    assert lib.q3op_tune(2, 3) != 0
+    assert lib.q3op_tune(99, 0) != 0
+
+
 @pytest.mark.parametrize("kernel,M", [(GEMM, 3), (GEMM, 200), (SKINNY, 1), (SKINNY, 40), (GEMV_F32, 6)])
 def test_linear_swiglu(kernel, M):
     rng = np.random.default_rng(M)
@@ -321,11 +352,25 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
     return worst
 
 
-@pytest.mark.parametrize("lens", [[1], [5], [64], [65], [130, 1, 63, 200], [513]])
+@pytest.mark.parametrize("lens", [[1], [5], [64], [65], [130, 1, 63, 200], [513], [600, 3, 130, 1100]])
 def test_flash_prefill_attention(lens):
     caps = [((L + 63) // 64) * 64 for L in lens]
     worst = _attention_case(0, lens, None, caps, seed=len(lens) + lens[0])
     assert worst < 1.0, worst
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4])
+def test_flash_prefill_rows_per_wavefront(rows):
+    _, lib = ops()
+    call(lib.q3op_tune(2, rows))
+    try:
+        for n_q, n_kv in [(16, 8), (16, 2), (8, 1)]:
+            lens = [600, 3, 130, 257]
+            caps = [((L + 63) // 64) * 64 for L in lens]
+            worst = _attention_case(0, lens, None, caps, n_q=n_q, n_kv=n_kv, seed=rows * 10 + n_kv)
+            assert worst < 1.0, (rows, n_q, n_kv, worst)
+    finally:
+        call(lib.q3op_tune(2, -1))
 
 
 def test_flash_prefill_gqa_groups():
