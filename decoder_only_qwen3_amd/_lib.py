@@ -87,7 +87,7 @@ def load() -> C.CDLL:
         "q3op_rmsnorm": (I32, [I32, VP, I32, VP, I32, C.c_float, VP, VP]),
         "q3op_linear_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "q3op_linear": (I32, [I32, I32, VP, I32, VP, I32, I32, VP, I64, VP, VP, SZ, VP]),
-        "q3op_norm_linear": (I32, [I32, VP, I32, VP, C.c_float, VP, I32, I32, VP, I64, VP, VP, SZ, VP]),
+        "q3op_norm_linear": (I32, [I32, I32, VP, I32, VP, C.c_float, VP, I32, I32, VP, I64, VP, VP, SZ, VP]),
         "q3op_rope_workspace_bytes": (SZ, [I32, I32]),
         "q3op_rope_append": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP,
                                    C.c_float, C.c_double, I32, VP, VP, SZ, VP]),

@@ -415,23 +415,29 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 
 // ---------------------------------------------------------------- fused decode
 // Decode attention with the QK-Norm + RoPE + cache append of Pasos 4-5 folded
-// in, spread over many single-wavefront blocks.  Block (split j, kv head g,
-// sequence b):
+// in.  Block (split j, kv head g, sequence b), FW wavefronts:
+//   0. read the sequence's length; every wavefront issues the loads of its
+//      first 32 cached keys and values at once, so the cache stream starts
+//      before any of the steps below;
 //   A. normalise and rotate the group's query heads from the fused projection
-//      row (into LDS, bf16); the block whose key range holds the new position
-//      also normalises/rotates the new key and stores it and the new value
-//      into the cache;
-//   B. attend over its run of keys (MFMA, as in decode_attn_kernel);
-//   C. one split: write the normalised output.  Several splits: publish a
-//      (max, sum, output) partial with device-coherent stores, count the
-//      finished splits of this (b, g) on a device-coherent counter, and let
-//      the last block merge the partials in split order (deterministic) and
-//      write the output; it also re-arms the counter.
-// The splits publish and read their partials with agent-scope atomic loads
-// and stores (coherent across the GPU's L2 slices) instead of device-wide
-// fences, which on gfx950 would write back and invalidate whole L2 caches.
-// The launch fixes `smax`; the number of splits used and the keys per split
-// follow the sequence's current length on the device.
+//      row (into LDS, bf16).  The block whose key range holds the new
+//      position also normalises/rotates the new key, stores it and the new
+//      value into the cache for later steps, and keeps both in LDS: this
+//      step takes the new key from LDS, never from the cache, so nothing
+//      waits on those stores;
+//   B. attend over the wavefront's cached keys (MFMA, next 32-key run loaded
+//      while the current one is used), then the wavefront that holds the new
+//      position adds the new key as one more online-softmax term;
+//   C. merge the block's wavefronts in order.  One split: write the output.
+//      Several splits: publish a (max, sum, output) partial with agent-scope
+//      stores, count the finished splits of this (b, g) on an agent-scope
+//      counter, and let the last block merge the partials in split order
+//      (deterministic) and re-arm the counter.
+// Agent-scope atomic loads/stores keep the partials coherent across the
+// GPU's L2 slices without device-wide fences (which on gfx950 write back and
+// invalidate whole L2 caches).  The launch fixes `smax`; the number of
+// splits used and the keys per split follow the sequence's current length
+// on the device, so a captured graph stays valid as the cache grows.
 struct RopeArgs {
   const float* qn;
   const float* kn;
@@ -469,13 +475,35 @@ Q3_DEV void norm_rope_pair(float& a, float& c, const float* w, float eps, float 
 
 constexpr int FW = 4;  // wavefronts per fused decode block
 
+// One 32-key run of the cache in registers, in the MFMA operand layouts:
+// k[sbk][ks] = K[key(sbk)][ks*32 + fq*8 ..], key(sbk) = c0 + 8*(fr/4) + 4*sbk + fr%4
+// (clamped to the last valid key); v[d] = V^T[d*16 + fr][c0 + fq*8 ..] with
+// keys at or beyond `end` zeroed.
+struct KvRun {
+  u32x4 k[2][4];
+  u32x4 v[8];
+};
+
+Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int cap, int c0, int end, int fr, int fq) {
+#pragma unroll
+  for (int sbk = 0; sbk < 2; ++sbk) {
+    const int key = min(c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), end - 1);
+    const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16(kp + ks * 32);
+  }
+  const int vkey0 = c0 + fq * 8;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) r.v[d] = ld16(Vt + (int64_t)(d * 16 + fr) * cap + vkey0);
+}
+
 __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
     const float* __restrict__ qkv, SeqBatch sb, const SeqState* __restrict__ st, bf16_t* __restrict__ kv,
     int layer, int n_q, int n_kv, RopeArgs ra, int smax, float* __restrict__ part, uint32_t* __restrict__ cnt,
     bf16_t* __restrict__ o, float scale_log2) {
   __shared__ __attribute__((aligned(16))) uint16_t qs[8 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t knew[128], vnew[128];
   __shared__ float wred[FW][8][PSTRIDE];
-  __shared__ float wsh[64];
   __shared__ int last;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, fr = lane & 15, fq = lane >> 4;
@@ -488,6 +516,15 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
   const KvGeom geo{n_kv, layer};
   bf16_t* Kc = kv_k(kv, s, geo, g);
   bf16_t* Vt = kv_vt(kv, s, geo, g);
+
+  // 0: this wavefront's keys are [w0, w1); those before `pos` come from the
+  // cache ([w0, cend)), the key at `pos` (if in range) from LDS.
+  const int cw = fg.cb / FW;
+  const int w0 = k_begin + wid * cw, w1 = min(k_end, w0 + cw);
+  const int cend = min(w1, pos);
+  const bool has_new = pos >= w0 && pos < w1;
+  KvRun run[2];
+  if (w0 < cend) load_run(run[0], Kc, Vt, s.cap, w0, cend, fr, fq);
 
   // A: wavefront u handles unit u, u+FW, ...: the group's query heads, then
   // (in the block holding the new position) the new key and value.
@@ -505,19 +542,22 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
     } else {
       float a = row[(n_q + g) * 128 + lane], c = row[(n_q + g) * 128 + lane + 64];
       norm_rope_pair(a, c, ra.kn, ra.eps, cs, sn);
-      Kc[(int64_t)pos * 128 + lane] = f2bf(a);
-      Kc[(int64_t)pos * 128 + lane + 64] = f2bf(c);
-      const float va = row[(n_q + n_kv + g) * 128 + lane], vc = row[(n_q + n_kv + g) * 128 + lane + 64];
-      Vt[(int64_t)lane * s.cap + pos] = f2bf(va);
-      Vt[(int64_t)(lane + 64) * s.cap + pos] = f2bf(vc);
+      const bf16_t ka = f2bf(a), kc = f2bf(c);
+      const bf16_t va = f2bf(row[(n_q + n_kv + g) * 128 + lane]);
+      const bf16_t vc = f2bf(row[(n_q + n_kv + g) * 128 + lane + 64]);
+      Kc[(int64_t)pos * 128 + lane] = ka;
+      Kc[(int64_t)pos * 128 + lane + 64] = kc;
+      Vt[(int64_t)lane * s.cap + pos] = va;
+      Vt[(int64_t)(lane + 64) * s.cap + pos] = vc;
+      knew[lane] = ka;
+      knew[lane + 64] = kc;
+      vnew[lane] = va;
+      vnew[lane + 64] = vc;
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the new key/value are stored before the loads below
   __syncthreads();
 
-  // B: this wavefront's share of the block's keys.
-  const int cw = fg.cb / FW;
-  const int w0 = k_begin + wid * cw, w1 = min(k_end, w0 + cw);
+  // B: cached keys, 32 at a time.
   bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -529,28 +569,22 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
 #pragma unroll
   for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
-  for (int c0 = w0; c0 < w1; c0 += 32) {
+  auto attend = [&](const KvRun& r, int c0) {
     f32x4 sacc[2];
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk) {
       sacc[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = min(c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), w1 - 1);
-      const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16(kp + ks * 32)), qf[ks], sacc[sbk]);
+      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(r.k[sbk][ks]), qf[ks], sacc[sbk]);
     }
-    u32x4 vraw[8];
-    const int vkey0 = c0 + fq * 8;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) vraw[d] = mask_keys(ld16(Vt + (int64_t)(d * 16 + fr) * s.cap + vkey0), vkey0, w1);
     float mx = -INFINITY;
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sacc[sbk][r] * scale_log2;
-        if (c0 + 8 * fq + 4 * sbk + r >= w1) v = -INFINITY;
-        sacc[sbk][r] = v;
+      for (int rr = 0; rr < 4; ++rr) {
+        float v = sacc[sbk][rr] * scale_log2;
+        if (c0 + 8 * fq + 4 * sbk + rr >= cend) v = -INFINITY;
+        sacc[sbk][rr] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -561,14 +595,45 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[sbk][r] = exp2_f(sacc[sbk][r] - mnew);
+      for (int rr = 0; rr < 4; ++rr) sacc[sbk][rr] = exp2_f(sacc[sbk][rr] - mnew);
     const f16x8 pf = pack_p(sacc[0], sacc[1]);
     float ls = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ls += sacc[0][r] + sacc[1][r];
+    for (int rr = 0; rr < 4; ++rr) ls += sacc[0][rr] + sacc[1][rr];
     lrun = lrun * alpha + ls;
+    const int vkey0 = c0 + fq * 8;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(vraw[d])), pf, oacc[d] * alpha);
+    for (int d = 0; d < 8; ++d)
+      oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(mask_keys(r.v[d], vkey0, cend))), pf, oacc[d] * alpha);
+  };
+  // Two register buffers, used in turn: the next run loads while one is used.
+  for (int c0 = w0; c0 < cend; c0 += 64) {
+    if (c0 + 32 < cend) load_run(run[1], Kc, Vt, s.cap, c0 + 32, cend, fr, fq);
+    attend(run[0], c0);
+    if (c0 + 32 >= cend) break;
+    if (c0 + 64 < cend) load_run(run[0], Kc, Vt, s.cap, c0 + 64, cend, fr, fq);
+    attend(run[1], c0 + 32);
+  }
+  if (has_new) {
+    // The new key: score q.k over 128 dims (bf16 operands, fp32 sums), then
+    // one more term of the online softmax with its fp16-rounded weight.
+    const float k0 = bf2f(knew[lane]), k1 = bf2f(knew[lane + 64]);
+    float snew = -INFINITY;
+    for (int hh = 0; hh < group; ++hh) {
+      const float d = wave_sum(bf2f(qs[hh * 128 + lane]) * k0 + bf2f(qs[hh * 128 + lane + 64]) * k1);
+      if (fr == hh) snew = d * scale_log2;
+    }
+    if (fr < group) {
+      const float mnew = fmaxf(mrun, snew);
+      const float alpha = exp2_f(mrun - mnew);
+      const float p = (float)(_Float16)exp2_f(snew - mnew);
+      mrun = mnew;
+      lrun = lrun * alpha + (fq == 0 ? p : 0.f);
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) oacc[d][rr] = oacc[d][rr] * alpha + p * bf2f(vnew[d * 16 + fq * 4 + rr]);
+    }
   }
   lrun += __shfl_xor(lrun, 16, 64);
   lrun += __shfl_xor(lrun, 32, 64);
@@ -581,7 +646,7 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
 #pragma unroll
     for (int d = 0; d < 8; ++d)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wp[2 + d * 16 + fq * 4 + r] = oacc[d][r];
+      for (int rr = 0; rr < 4; ++rr) wp[2 + d * 16 + fq * 4 + rr] = oacc[d][rr];
   }
   __syncthreads();
 
@@ -762,12 +827,18 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
   return hipGetLastError();
 }
 
+namespace {
+int g_attn_smax_cap = -1;  // upper bound on splits (q3op_tune); -1 = none
+}
+void decode_attn_set_split_cap(int cap) { g_attn_smax_cap = cap; }
+
 int fused_attn_smax(int B, int n_kv, int64_t max_ctx) {
   // about 512 four-wavefront blocks, at least 128 keys each, at most 64 splits
   int64_t by_len = (max_ctx + 127) / 128;
   int64_t want = (512 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   int64_t sm = by_len < want ? by_len : want;
   if (sm > 64) sm = 64;
+  if (g_attn_smax_cap > 0 && sm > g_attn_smax_cap) sm = g_attn_smax_cap;
   return sm < 1 ? 1 : (int)sm;
 }
 

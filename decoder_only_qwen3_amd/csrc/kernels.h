@@ -67,6 +67,17 @@ hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, in
 // Row-parallel bf16 GEMV for decode with M <= 4 rows: one wavefront per
 // output row (EPI_STORE / EPI_RESADD), K a multiple of 512 up to 4096.
 bool rowdot_ok(int M, int K);
+
+// ---------------------------------------------------------------- k_rowgemv.hip
+// One activation row (M = 1), K = 512 * {1,2,4,6,8}.  gnorm != nullptr: X is
+// the float32 residual row and RMSNorm is fused (epi STORE or SWIGLU);
+// otherwise X is bf16.  ARGMAX writes float32 logits to out and one
+// (max, index) partial per block (rowgemv_argmax_blocks(N, K) of them).
+bool rowgemv_ok(int M, int K);
+int rowgemv_argmax_blocks(int N, int K);
+void rowgemv_set_plan(int rows, int waves);  // -1 = automatic
+hipError_t rowgemv_bf16(int epi, const void* X, const bf16_t* W, int N, int K, const float* gnorm, float eps,
+                        void* out, float* amax_val, int32_t* amax_idx, hipStream_t s);
 hipError_t rowdot_bf16(int epi, const bf16_t* X, int M, const bf16_t* W, int N, int K, float* out, int64_t ldo,
                        hipStream_t s);
 // float32 weights and activations (the float32 model); any M.
@@ -87,6 +98,7 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
 // B * n_q * smax * 130 floats and `counters` B * n_kv zeroed words (left
 // zeroed by the kernel).
 int fused_attn_smax(int B, int n_kv, int64_t max_ctx);
+void decode_attn_set_split_cap(int cap);  // -1 = no cap (benchmarks only)
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
                              int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,
                              const float* sin_t, int smax, float* part, uint32_t* counters, bf16_t* o,

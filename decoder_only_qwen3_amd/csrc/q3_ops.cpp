@@ -72,6 +72,35 @@ q3_status skinny_op(int epi, const void* X, int M, const float* gnorm, float eps
   return Q3_OK;
 }
 
+struct RowWs {
+  size_t err, amax_val, amax_idx, total;
+};
+RowWs row_ws(int N) {
+  RowWs w;
+  const size_t parts = (size_t)N;  // at most one partial per row, whatever the plan
+  w.err = 0;
+  w.amax_val = al(16);
+  w.amax_idx = w.amax_val + al(parts * 4);
+  w.total = w.amax_idx + al(parts * 4);
+  return w;
+}
+
+q3_status rowgemv_op(int epi, const void* X, const float* gnorm, float eps, const void* W, int N, int K, void* out,
+                     int32_t* next, void* d_ws, size_t ws_bytes, hipStream_t s) {
+  RowWs w = row_ws(N);
+  if (epi == EPI_ARGMAX && (!d_ws || ws_bytes < w.total)) return op_fail(Q3_E_ARG, "workspace too small");
+  char* ws = (char*)d_ws;
+  float* av = epi == EPI_ARGMAX ? (float*)(ws + w.amax_val) : nullptr;
+  int32_t* ai = epi == EPI_ARGMAX ? (int32_t*)(ws + w.amax_idx) : nullptr;
+  OP_TRY(rowgemv_bf16(epi, X, (const bf16_t*)W, N, K, gnorm, eps, out, av, ai, s));
+  if (epi == EPI_ARGMAX) {
+    SeqBatch none;
+    std::memset(&none, 0, sizeof(none));
+    OP_TRY(argmax_finish(av, ai, rowgemv_argmax_blocks(N, K), 1, next, none, nullptr, (uint32_t*)(ws + w.err), s));
+  }
+  return Q3_OK;
+}
+
 q3_status make_batch(int n, const int32_t* cu, int decode, SeqBatch* sb) {
   if (n < 1 || n > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "n_seqs must be in [1, 64]");
   std::memset(sb, 0, sizeof(*sb));
@@ -112,6 +141,7 @@ size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32
   (void)epi;
   (void)K;
   if (kernel == Q3OP_SKINNY) return skinny_ws(M, N).total;
+  if (kernel == Q3OP_ROWGEMV) return row_ws(N).total;
   return 256;
 }
 
@@ -154,15 +184,28 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
     if (M > Q3_MAX_BATCH) return op_fail(Q3_E_UNSUPPORTED, "the weight-streaming kernel takes M <= 64");
     return skinny_op(epi, d_x, M, nullptr, 0.f, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, s);
   }
+  if (kernel == Q3OP_ROWGEMV) {
+    if (!rowgemv_ok(M, K)) return op_fail(Q3_E_UNSUPPORTED, "the single-row GEMV takes M = 1, K = 512 * {1,2,4,6,8}");
+    if (epi == EPI_SWIGLU && N % 32 != 0) return op_fail(Q3_E_UNSUPPORTED, "SwiGLU needs N % 32 == 0");
+    return rowgemv_op(epi, d_x, nullptr, 0.f, d_w, N, K, d_out, d_next, d_ws, ws_bytes, s);
+  }
   return op_fail(Q3_E_ARG, "unknown kernel");
 }
 
-q3_status q3op_norm_linear(int32_t epi, const float* d_x, int32_t M, const float* d_gnorm, float eps,
-                           const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo, int32_t* d_next,
-                           void* d_ws, size_t ws_bytes, void* stream) {
+q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_t M, const float* d_gnorm,
+                           float eps, const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo,
+                           int32_t* d_next, void* d_ws, size_t ws_bytes, void* stream) {
   if (!d_x || !d_gnorm || !d_w || !d_out || M <= 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
   if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
   if (epi == EPI_ARGMAX && !d_next) return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
+  if (kernel == Q3OP_ROWGEMV) {
+    if (!rowgemv_ok(M, K)) return op_fail(Q3_E_UNSUPPORTED, "the single-row GEMV takes M = 1, K = 512 * {1,2,4,6,8}");
+    if (epi != EPI_STORE && epi != EPI_SWIGLU)
+      return op_fail(Q3_E_UNSUPPORTED, "the single-row GEMV fuses RMSNorm for epilogues 0 and 2 only");
+    if (epi == EPI_SWIGLU && N % 32 != 0) return op_fail(Q3_E_UNSUPPORTED, "SwiGLU needs N % 32 == 0");
+    return rowgemv_op(epi, d_x, d_gnorm, eps, d_w, N, K, d_out, d_next, d_ws, ws_bytes, (hipStream_t)stream);
+  }
+  if (kernel != Q3OP_SKINNY) return op_fail(Q3_E_ARG, "the fused RMSNorm prologue exists in kernels 1 and 4");
   if (!skinny_norm_ok(M)) return op_fail(Q3_E_UNSUPPORTED, "the fused RMSNorm prologue takes M <= 8");
   return skinny_op(epi, d_x, M, d_gnorm, eps, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, (hipStream_t)stream);
 }
@@ -308,6 +351,18 @@ q3_status q3op_tune(int32_t key, int32_t value) {
   if (key == Q3OP_TUNE_GEMM_TILES) {
     if (value < -1 || value > 6) return op_fail(Q3_E_ARG, "tile configuration out of range");
     gemm_set_config(value);
+    return Q3_OK;
+  }
+  if (key == Q3OP_TUNE_ROWGEMV) {
+    const int rows = value < 0 ? -1 : value & 0xff, waves = value < 0 ? -1 : value >> 8;
+    if (value >= 0 && (!(rows == 1 || rows == 2 || rows == 4 || rows == 8) || waves < 1 || waves > 4))
+      return op_fail(Q3_E_ARG, "rows per wavefront must be 1, 2, 4 or 8 and wavefronts per block 1..4");
+    rowgemv_set_plan(rows, waves);
+    return Q3_OK;
+  }
+  if (key == Q3OP_TUNE_ATTN_SPLITS) {
+    if (value == 0 || value < -1 || value > 64) return op_fail(Q3_E_ARG, "split cap must be -1 or 1..64");
+    decode_attn_set_split_cap(value);
     return Q3_OK;
   }
   if (key == Q3OP_TUNE_FLASH_ROWS) {

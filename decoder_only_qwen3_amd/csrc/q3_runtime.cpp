@@ -243,16 +243,24 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     for (int b = 0; b < sb.n; ++b) maxcap = std::max(maxcap, m->slots[sb.slot[b]].cap);
     smax = fused_attn_smax(sb.n, c.n_kv_heads, std::min<int64_t>(maxcap, c.max_positions));
   }
+  // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
+  // into q/k/v and gate/up).  Small batches: row GEMV for o and down.
+  const bool one_h = bf && decode && rowgemv_ok(T, H);
+  const bool one_q = bf && decode && rowgemv_ok(T, Q);
+  const bool one_i = bf && decode && rowgemv_ok(T, I);
   const bool rows_o = bf && decode && rowdot_ok(T, Q);
   const bool rows_d = bf && decode && rowdot_ok(T, I);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
     // Paso 3 + Paso 5: normalised input, fused q/k/v projection.  Decode with
     // few rows folds the RMSNorm into the projection kernel's prologue.
-    const bool fuse_norm = bf && decode && skinny_norm_ok(T);
+    const bool fuse_norm = bf && decode && (one_h || skinny_norm_ok(T));
     if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
     if (!bf) {
       LAUNCH(gemv_f32(EPI_STORE, (const float*)h, T, m->W<float>(lw.qkv), NQKV, H, qkv, NQKV, s));
+    } else if (one_h) {
+      LAUNCH(rowgemv_bf16(EPI_STORE, x, m->W<bf16_t>(lw.qkv), NQKV, H, m->W<float>(lw.in_norm), c.rms_eps, qkv,
+                          nullptr, nullptr, s));
     } else if (decode) {
       LAUNCH(skinny_bf16(EPI_STORE, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.qkv), NQKV, H,
                          fuse_norm ? m->W<float>(lw.in_norm) : nullptr, c.rms_eps, qkv, NQKV, nullptr, nullptr, s));
@@ -281,6 +289,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     // Output projection + residual (Paso 5 end, Paso 7).
     if (!bf) {
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
+    } else if (one_q) {
+      LAUNCH(rowgemv_bf16(EPI_RESADD, ob, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, nullptr, nullptr, s));
     } else if (rows_o) {
       LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
     } else if (decode) {
@@ -294,9 +304,15 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       LAUNCH(gemv_f32(EPI_SWIGLU, (const float*)h, T, m->W<float>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)mb, T, m->W<float>(lw.d), H, I, x, H, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.gu), 2 * I, H,
-                         fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps, mb, I, nullptr, nullptr, s));
-      if (rows_d)
+      if (one_h)
+        LAUNCH(rowgemv_bf16(EPI_SWIGLU, x, m->W<bf16_t>(lw.gu), 2 * I, H, m->W<float>(lw.post_norm), c.rms_eps, mb,
+                            nullptr, nullptr, s));
+      else
+        LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.gu), 2 * I, H,
+                           fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps, mb, I, nullptr, nullptr, s));
+      if (one_i)
+        LAUNCH(rowgemv_bf16(EPI_RESADD, mb, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, nullptr, nullptr, s));
+      else if (rows_d)
         LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
       else
         LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s));
@@ -322,7 +338,12 @@ q3_status enqueue_head(q3_model* m, const RowMap& rows, int nrows, const SeqBatc
   const bool fuse_norm = false;
   if (!fuse_norm)
     LAUNCH(rmsnorm(c.dtype, x, nrows, rows, m->W<float>(m->wl.final_norm), c.hidden, c.rms_eps, h, s));
-  if (c.dtype == Q3_BF16) {
+  if (c.dtype == Q3_BF16 && rowgemv_ok(nrows, c.hidden)) {
+    LAUNCH(rowgemv_bf16(EPI_ARGMAX, h, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, nullptr, 0.f, logits,
+                        m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
+    LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), rowgemv_argmax_blocks(c.vocab, c.hidden),
+                         nrows, d_next, sb, m->state(), m->err(), s));
+  } else if (c.dtype == Q3_BF16) {
     LAUNCH(skinny_bf16(EPI_ARGMAX, fuse_norm ? (const void*)x : h, nrows, m->W<bf16_t>(m->wl.embed), c.vocab,
                        c.hidden, fuse_norm ? m->W<float>(m->wl.final_norm) : nullptr, c.rms_eps, logits, c.vocab,
                        m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));

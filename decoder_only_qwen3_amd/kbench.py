@@ -39,26 +39,41 @@ def _time(fn, reps, stream):
     return e0.elapsed_time(e1) / reps * 1e3  # microseconds
 
 
-def linear_case(lib, name, epi, M, N, K, reps, stream, kernel=1):
-    x = _rand_bf16((M, K))
-    w = _rand_bf16((N, K), 0.02)
+def linear_case(lib, name, epi, M, N, K, reps, stream, kernel=1, norm=False, pool=1):
+    """`pool` > 1 cycles through that many copies of the weight matrix, so
+    that they are not all resident in the GPU's caches."""
+    if norm:
+        x = torch.randn((M, K), device="cuda:0")
+        g = 1 + 0.1 * torch.randn(K, device="cuda:0")
+    else:
+        x = _rand_bf16((M, K))
+    ws_ = [_rand_bf16((N, K), 0.02) for _ in range(pool)]
     if epi == 2:
         out = torch.empty((M, N // 2), dtype=torch.int16, device="cuda:0")
         ldo = N // 2
     else:
         out = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
         ldo = N
+    nxt = torch.zeros(max(M, 1), dtype=torch.int32, device="cuda:0")
     ws = torch.zeros(max(256, lib.q3op_linear_workspace_bytes(kernel, epi, M, N, K)), dtype=torch.uint8,
                      device="cuda:0")
     sh = stream.cuda_stream
+    it = [0]
 
     def fn():
-        _lib.check(lib.q3op_linear(kernel, epi, x.data_ptr(), M, w.data_ptr(), N, K, out.data_ptr(), ldo, None,
-                                   ws.data_ptr(), ws.numel(), sh))
+        w = ws_[it[0] % pool]
+        it[0] += 1
+        nx = nxt.data_ptr() if (epi == 3 and kernel != 1) else None
+        if norm:
+            _lib.check(lib.q3op_norm_linear(kernel, epi, x.data_ptr(), M, g.data_ptr(), 1e-6, w.data_ptr(), N, K,
+                                            out.data_ptr(), ldo, nx, ws.data_ptr(), ws.numel(), sh))
+        else:
+            _lib.check(lib.q3op_linear(kernel, epi, x.data_ptr(), M, w.data_ptr(), N, K, out.data_ptr(), ldo, nx,
+                                       ws.data_ptr(), ws.numel(), sh))
     us = _time(fn, reps, stream)
-    if kernel == 1:
+    if kernel != 0:
         out_b = M * N * 4 if epi != 2 else M * (N // 2) * 2
-        byts = N * K * 2 + M * K * 2 + out_b + (M * N * 4 if epi == 1 else 0)
+        byts = N * K * 2 + M * K * (8 if norm else 2) + out_b + (M * N * 4 if epi == 1 else 0)
         return {"kernel": name, "M": M, "N": N, "K": K, "us": round(us, 2), "bytes": byts,
                 "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
     fl = 2 * M * N * K
@@ -101,6 +116,19 @@ def attention_case(lib, name, kernel, L, B, reps, stream):
 
 
 CASES = {
+    # batch-1 decode projections as the decode step runs them, weights cycled
+    # through 32 copies (beyond the GPU's last-level cache)
+    "row_qkv": lambda lib, r, s: linear_case(lib, "row_qkv", 0, 1, Q + 2 * KVW, H, r, s, kernel=4, norm=True, pool=32),
+    "row_o": lambda lib, r, s: linear_case(lib, "row_o", 1, 1, H, Q, r, s, kernel=4, pool=32),
+    "row_gate_up": lambda lib, r, s: linear_case(lib, "row_gate_up", 2, 1, 2 * I, H, r, s, kernel=4, norm=True,
+                                                 pool=32),
+    "row_down": lambda lib, r, s: linear_case(lib, "row_down", 1, 1, H, I, r, s, kernel=4, pool=32),
+    "row_lm_head": lambda lib, r, s: linear_case(lib, "row_lm_head", 3, 1, V, H, r, s, kernel=4, pool=2),
+    "sk_qkv": lambda lib, r, s: linear_case(lib, "sk_qkv", 0, 1, Q + 2 * KVW, H, r, s, kernel=1, norm=True, pool=32),
+    "sk_gate_up": lambda lib, r, s: linear_case(lib, "sk_gate_up", 2, 1, 2 * I, H, r, s, kernel=1, norm=True, pool=32),
+    "rd_o": lambda lib, r, s: linear_case(lib, "rd_o", 1, 1, H, Q, r, s, kernel=3, pool=32),
+    "rd_down": lambda lib, r, s: linear_case(lib, "rd_down", 1, 1, H, I, r, s, kernel=3, pool=32),
+    "sk_lm_head": lambda lib, r, s: linear_case(lib, "sk_lm_head", 3, 1, V, H, r, s, kernel=1, pool=2),
     "lm_head": lambda lib, r, s: linear_case(lib, "lm_head", 3, 1, V, H, r, s),
     "qkv": lambda lib, r, s: linear_case(lib, "qkv", 0, 1, Q + 2 * KVW, H, r, s),
     "o": lambda lib, r, s: linear_case(lib, "o", 1, 1, H, Q, r, s),
@@ -127,10 +155,12 @@ def main():
     ap.add_argument("--reps", type=int, default=50)
     ap.add_argument("--gemm-tiles", type=int, default=-1, help="prefill GEMM tile configuration (-1 automatic)")
     ap.add_argument("--flash-rows", type=int, default=-1, help="prefill attention rows per wavefront / 16")
+    ap.add_argument("--row-plan", type=int, default=-1, help="single-row GEMV: rows + 256 * wavefronts per block")
     args = ap.parse_args()
     lib = _lib.load()
     _lib.check(lib.q3op_tune(1, args.gemm_tiles))
     _lib.check(lib.q3op_tune(2, args.flash_rows))
+    _lib.check(lib.q3op_tune(3, args.row_plan))
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for k in args.kernels.split(","):

@@ -46,23 +46,28 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
  * kernel 2 = float32 GEMV (float32 model);
  * kernel 3 = bf16 row-per-wavefront GEMV (decode with M <= 4, epi 0 or 1,
- * K a multiple of 512).  bf16 kernels take bf16 X and W. */
+ * K a multiple of 512);
+ * kernel 4 = bf16 single-row GEMV (M = 1, epi 0-3, K = 512 * {1,2,4,6,8};
+ * SwiGLU needs N % 32 == 0; out is dense, ldo is ignored).
+ * bf16 kernels take bf16 X and W. */
 #define Q3OP_GEMM 0
 #define Q3OP_SKINNY 1
 #define Q3OP_GEMV_F32 2
 #define Q3OP_ROWDOT 3  /* bf16 row-per-wavefront GEMV (decode, M <= 4, epi 0-1) */
+#define Q3OP_ROWGEMV 4 /* bf16 single-row GEMV (decode batch 1, epi 0-3) */
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K);
 q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
                       int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
                       void* stream);
 
-/* Pasos 3 + 5: the weight-streaming kernel with RMSNorm fused into its
- * prologue (decode with M <= 8): X = bf16(x * rsqrt(mean(x^2) + eps) * g)
- * from float32 rows d_x [M][K] and float32 weight d_gnorm [K], then epilogue
- * `epi` as in q3op_linear.  Workspace: q3op_linear_workspace_bytes(1, ...). */
-q3_status q3op_norm_linear(int32_t epi, const float* d_x, int32_t M, const float* d_gnorm, float eps,
-                           const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo, int32_t* d_next,
-                           void* d_ws, size_t ws_bytes, void* stream);
+/* Pasos 3 + 5: a decode projection with RMSNorm fused into its prologue:
+ * X = bf16(x * rsqrt(mean(x^2) + eps) * g) from float32 rows d_x [M][K] and
+ * float32 weight d_gnorm [K], then epilogue `epi` as in q3op_linear.
+ * kernel 1 (weight-streaming, M <= 8, epi 0-3) or kernel 4 (single row,
+ * M = 1, epi 0 or 2).  Workspace: q3op_linear_workspace_bytes(kernel, ...). */
+q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_t M, const float* d_gnorm,
+                           float eps, const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo,
+                           int32_t* d_next, void* d_ws, size_t ws_bytes, void* stream);
 
 /* A one-layer KV arena for the attention ops: sequence b owns the elements
  * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):
@@ -113,9 +118,18 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,
  *   0..6 = fixed tile shapes (listed in k_gemm.hip).
  * Q3OP_TUNE_FLASH_ROWS: prefill attention query rows per wavefront / 16,
- *   -1 = automatic, or 1, 2, 4. */
+ *   -1 = automatic, or 1, 2, 4.
+ * Q3OP_TUNE_ROWGEMV: single-row GEMV shape, -1 = automatic, else
+ *   rows_per_wavefront (1, 2, 4, 8) + 256 * wavefronts_per_block (1..4);
+ *   SwiGLU needs an even rows_per_wavefront.
+ * Q3OP_TUNE_ATTN_SPLITS: upper bound on the key splits per (sequence, kv
+ *   head) of bf16 decode attention, -1 = none, else 1..64; it only lowers
+ *   the library's choice, so workspaces sized earlier stay large enough.
+ *   Decode graphs captured before the change keep their split count. */
 #define Q3OP_TUNE_GEMM_TILES 1
 #define Q3OP_TUNE_FLASH_ROWS 2
+#define Q3OP_TUNE_ROWGEMV 3
+#define Q3OP_TUNE_ATTN_SPLITS 4
 q3_status q3op_tune(int32_t key, int32_t value);
 
 #ifdef __cplusplus

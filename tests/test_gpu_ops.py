@@ -14,7 +14,7 @@ from oracle import attention_rows, rms_norm, rope_cos_sin, rope_rotate, silu, to
 pytestmark = pytest.mark.gpu
 
 EPI_STORE, EPI_RESADD, EPI_SWIGLU, EPI_ARGMAX = 0, 1, 2, 3
-GEMM, SKINNY, GEMV_F32 = 0, 1, 2
+GEMM, SKINNY, GEMV_F32, ROWDOT, ROWGEMV = 0, 1, 2, 3, 4
 BF16, F32 = 1, 0
 
 
@@ -83,7 +83,7 @@ def _linear(kernel, epi, X, W, out_init=None, ldo=None, want_next=False):
     mod, lib = ops()
     M, K = X.shape
     N = W.shape[0]
-    bf = kernel in (GEMM, SKINNY, 3)
+    bf = kernel in (GEMM, SKINNY, ROWDOT, ROWGEMV)
     dx = dev_bf16(X) if bf else dev_f32(X)
     dw = dev_bf16(W) if bf else dev_f32(W)
     if epi == EPI_SWIGLU:
@@ -106,7 +106,8 @@ def _rel(got, ref):
 
 
 @pytest.mark.parametrize("kernel,M", [(GEMM, 1), (GEMM, 5), (GEMM, 130), (GEMM, 257),
-                                      (SKINNY, 1), (SKINNY, 3), (SKINNY, 16), (SKINNY, 17), (SKINNY, 64)])
+                                      (SKINNY, 1), (SKINNY, 3), (SKINNY, 16), (SKINNY, 17), (SKINNY, 64),
+                                      (ROWGEMV, 1)])
 @pytest.mark.parametrize("N,K", [(4096, 1024), (1024, 2048), (1024, 3072)])
 def test_linear_store_and_residual(kernel, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
@@ -148,10 +149,55 @@ def test_tune_rejects_bad_values():
     _, lib = ops()
     assert lib.q3op_tune(1, 7) != 0
     assert lib.q3op_tune(2, 3) != 0
+    assert lib.q3op_tune(3, 3 + 256) != 0
+    assert lib.q3op_tune(3, 4 + 5 * 256) != 0
+    assert lib.q3op_tune(4, 0) != 0
+    assert lib.q3op_tune(4, 65) != 0
     assert lib.q3op_tune(99, 0) != 0
 
 
-@pytest.mark.parametrize("kernel,M", [(GEMM, 3), (GEMM, 200), (SKINNY, 1), (SKINNY, 40), (GEMV_F32, 6)])
+@pytest.mark.parametrize("rows", [1, 2, 4, 8])
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_rowgemv_shapes(rows, waves):
+    """Every single-row GEMV shape, with row counts that leave partial wavefronts and blocks."""
+    _, lib = ops()
+    call(lib.q3op_tune(3, rows + 256 * waves))
+    try:
+        rng = np.random.default_rng(rows * 10 + waves)
+        K = 2048
+        X = rand_bf16(rng, (1, K))
+        for N in (1040, 1041):
+            W = rand_bf16(rng, (N, K), 0.02)
+            ref = X.astype(np.float64) @ W.astype(np.float64).T
+            got, _ = _linear(ROWGEMV, EPI_STORE, X, W)
+            assert _rel(got, ref) < 2e-5, N
+            base = rng.standard_normal((1, N)).astype(np.float32)
+            got, _ = _linear(ROWGEMV, EPI_RESADD, X, W, out_init=base)
+            assert _rel(got - base, ref) < 2e-5, N
+            got, nxt = _linear(ROWGEMV, EPI_ARGMAX, X, W, want_next=True)
+            assert _rel(got, ref) < 2e-5, N
+            assert nxt[0] == int(np.argmax(got[0]))
+        if rows % 2 == 0:
+            N = 1088
+            G, U = rand_bf16(rng, (N // 2, K), 0.05), rand_bf16(rng, (N // 2, K), 0.05)
+            got, _ = _linear(ROWGEMV, EPI_SWIGLU, X, _pack_gate_up(G, U))
+            g = X.astype(np.float64) @ G.astype(np.float64).T
+            u = X.astype(np.float64) @ U.astype(np.float64).T
+            np.testing.assert_allclose(got, to_bf16(silu(g) * u), rtol=2 ** -7, atol=1e-6)
+        else:
+            mod, _ = ops()
+            x = torch.zeros(K, dtype=torch.int16, device="cuda:0")
+            w = torch.zeros((64, K), dtype=torch.int16, device="cuda:0")
+            o = torch.zeros(32, dtype=torch.int16, device="cuda:0")
+            st = lib.q3op_linear(ROWGEMV, EPI_SWIGLU, x.data_ptr(), 1, w.data_ptr(), 64, K, o.data_ptr(), 32, None,
+                                 None, 0, None)
+            assert st != 0, "odd rows per wavefront cannot pair gate and up rows"
+    finally:
+        call(lib.q3op_tune(3, -1))
+
+
+@pytest.mark.parametrize("kernel,M", [(GEMM, 3), (GEMM, 200), (SKINNY, 1), (SKINNY, 40), (GEMV_F32, 6),
+                                      (ROWGEMV, 1)])
 def test_linear_swiglu(kernel, M):
     rng = np.random.default_rng(M)
     I, H = 3072, 1024
@@ -184,7 +230,8 @@ def test_gemv_f32_store_and_residual(M):
     assert _rel(got - base, ref) < 1e-5
 
 
-@pytest.mark.parametrize("kernel,M", [(SKINNY, 1), (SKINNY, 7), (SKINNY, 64), (GEMM, 3), (GEMV_F32, 2)])
+@pytest.mark.parametrize("kernel,M", [(SKINNY, 1), (SKINNY, 7), (SKINNY, 64), (GEMM, 3), (GEMV_F32, 2),
+                                      (ROWGEMV, 1)])
 def test_logits_and_argmax(kernel, M):
     rng = np.random.default_rng(300 + M)
     V, H = 8192, 1024
@@ -402,9 +449,12 @@ def test_attention_f32(mode):
 
 
 @pytest.mark.parametrize("epi,M,N", [(EPI_STORE, 1, 4096), (EPI_SWIGLU, 3, 6144), (EPI_ARGMAX, 1, 8192),
-                                     (EPI_STORE, 8, 4096)])
-def test_norm_linear_fused_prologue(epi, M, N):
-    """RMSNorm folded into the weight-streaming kernel equals rmsnorm -> bf16 -> projection."""
+                                     (EPI_STORE, 8, 4096), (EPI_SWIGLU, 1, 6144)])
+@pytest.mark.parametrize("kernel", [SKINNY, ROWGEMV])
+def test_norm_linear_fused_prologue(kernel, epi, M, N):
+    """RMSNorm folded into a decode projection's prologue equals rmsnorm -> bf16 -> projection."""
+    if kernel == ROWGEMV and (M != 1 or epi not in (EPI_STORE, EPI_SWIGLU)):
+        pytest.skip("the single-row GEMV fuses the norm for one row and epilogues 0 and 2")
     mod, lib = ops()
     rng = np.random.default_rng(50 + M + epi)
     K = 1024
@@ -420,8 +470,8 @@ def test_norm_linear_fused_prologue(epi, M, N):
         out = torch.zeros((M, N), dtype=torch.float32, device="cuda:0")
         ldo = N
     nxt = torch.zeros(M, dtype=torch.int32, device="cuda:0")
-    ws = _ws(lib.q3op_linear_workspace_bytes(SKINNY, epi, M, N, K))
-    call(lib.q3op_norm_linear(epi, dx.data_ptr(), M, dg.data_ptr(), 1e-6, dw.data_ptr(), N, K, out.data_ptr(),
+    ws = _ws(lib.q3op_linear_workspace_bytes(kernel, epi, M, N, K))
+    call(lib.q3op_norm_linear(kernel, epi, dx.data_ptr(), M, dg.data_ptr(), 1e-6, dw.data_ptr(), N, K, out.data_ptr(),
                               ldo, nxt.data_ptr(), ws.data_ptr(), ws.numel(), None))
     _sync()
     if epi == EPI_SWIGLU:
