@@ -832,14 +832,19 @@ int g_attn_smax_cap = -1;  // upper bound on splits (q3op_tune); -1 = none
 }
 void decode_attn_set_split_cap(int cap) { g_attn_smax_cap = cap; }
 
-int fused_attn_smax(int B, int n_kv, int64_t max_ctx) {
+int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx) {
   // about 512 four-wavefront blocks, at least 128 keys each, at most 64 splits
   int64_t by_len = (max_ctx + 127) / 128;
   int64_t want = (512 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   int64_t sm = by_len < want ? by_len : want;
   if (sm > 64) sm = 64;
-  if (g_attn_smax_cap > 0 && sm > g_attn_smax_cap) sm = g_attn_smax_cap;
   return sm < 1 ? 1 : (int)sm;
+}
+
+int fused_attn_smax(int B, int n_kv, int64_t max_ctx) {
+  int sm = fused_attn_smax_max(B, n_kv, max_ctx);
+  if (g_attn_smax_cap > 0 && sm > g_attn_smax_cap) sm = g_attn_smax_cap;
+  return sm;
 }
 
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,

@@ -98,6 +98,7 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
 // B * n_q * smax * 130 floats and `counters` B * n_kv zeroed words (left
 // zeroed by the kernel).
 int fused_attn_smax(int B, int n_kv, int64_t max_ctx);
+int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx);  // ignoring the benchmark cap: for sizing
 void decode_attn_set_split_cap(int cap);  // -1 = no cap (benchmarks only)
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
                              int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,

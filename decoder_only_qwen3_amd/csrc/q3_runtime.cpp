@@ -117,7 +117,7 @@ int max_attn_splits_rows(const q3_config& c) {
   int best = 0;
   for (int B = 1; B <= Q3_MAX_BATCH; ++B) {
     best = std::max(best, B * decode_attn_splits(B, c.n_kv_heads, c.max_positions));
-    best = std::max(best, B * fused_attn_smax(B, c.n_kv_heads, c.max_positions));
+    best = std::max(best, B * fused_attn_smax_max(B, c.n_kv_heads, c.max_positions));
   }
   return best;
 }
