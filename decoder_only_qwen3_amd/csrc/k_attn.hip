@@ -451,9 +451,11 @@ struct FusedGeom {
   int cb;     // keys per split (multiple of 32)
 };
 
+template <int FW>
 Q3_DEV FusedGeom fused_geom(int ctx, int smax) {
+  constexpr int unit = 32 * FW;  // whole 32-key runs for each of the FW wavefronts
   int cb = (ctx + smax - 1) / smax;
-  cb = max(128, (cb + 127) & ~127);  // whole 32-key runs for each of the 4 wavefronts
+  cb = max(unit, (cb + unit - 1) / unit * unit);
   return FusedGeom{(ctx + cb - 1) / cb, cb};
 }
 
@@ -473,7 +475,6 @@ Q3_DEV void norm_rope_pair(float& a, float& c, const float* w, float eps, float 
   c = rc;
 }
 
-constexpr int FW = 4;  // wavefronts per fused decode block
 
 // One 32-key run of the cache in registers, in the MFMA operand layouts:
 // k[sbk][ks] = K[key(sbk)][ks*32 + fq*8 ..], key(sbk) = c0 + 8*(fr/4) + 4*sbk + fr%4
@@ -497,7 +498,8 @@ Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int cap, int 
   for (int d = 0; d < 8; ++d) r.v[d] = ld16(Vt + (int64_t)(d * 16 + fr) * cap + vkey0);
 }
 
-__global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
+template <int FW>
+__global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
     const float* __restrict__ qkv, SeqBatch sb, const SeqState* __restrict__ st, bf16_t* __restrict__ kv,
     int layer, int n_q, int n_kv, RopeArgs ra, int smax, float* __restrict__ part, uint32_t* __restrict__ cnt,
     bf16_t* __restrict__ o, float scale_log2) {
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(64 * FW) void decode_attn_fused_kernel(
   const int group = n_q / n_kv;
   const SeqState s = st[sb.slot[b]];
   const int pos = s.len, ctx = pos + 1;
-  const FusedGeom fg = fused_geom(ctx, smax);
+  const FusedGeom fg = fused_geom<FW>(ctx, smax);
   if (j >= fg.nact) return;
   const int k_begin = j * fg.cb, k_end = min(ctx, k_begin + fg.cb);
   const KvGeom geo{n_kv, layer};
@@ -833,9 +835,10 @@ int g_attn_smax_cap = -1;  // upper bound on splits (q3op_tune); -1 = none
 void decode_attn_set_split_cap(int cap) { g_attn_smax_cap = cap; }
 
 int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx) {
-  // about 512 four-wavefront blocks, at least 128 keys each, at most 64 splits
+  // about one block per CU (256), at least 128 keys each, at most 64 splits;
+  // measured on MI355X, more splits only add merge work once the CUs are busy
   int64_t by_len = (max_ctx + 127) / 128;
-  int64_t want = (512 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
+  int64_t want = (256 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   int64_t sm = by_len < want ? by_len : want;
   if (sm > 64) sm = 64;
   return sm < 1 ? 1 : (int)sm;
@@ -857,8 +860,10 @@ hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqStat
   const float scale_log2 = kLog2e / sqrtf(128.f);
   RopeArgs ra{qn, kn, cos_t, sin_t, eps};
   dim3 grid(smax, n_kv, sb.n);
-  decode_attn_fused_kernel<<<grid, 64 * FW, 0, s>>>(qkv, sb, st, kv, layer, n_q, n_kv, ra, smax, part, counters,
-                                                    o, scale_log2);
+  // Four wavefronts per block: eight measured slower at every batch and
+  // context tried (one CU's stream does not grow with more wavefronts).
+  decode_attn_fused_kernel<4><<<grid, 256, 0, s>>>(qkv, sb, st, kv, layer, n_q, n_kv, ra, smax, part, counters, o,
+                                                   scale_log2);
   return hipGetLastError();
 }
 

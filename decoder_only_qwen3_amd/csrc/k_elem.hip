@@ -92,7 +92,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     int layer, int n_q, int n_kv, const float* __restrict__ qn, const float* __restrict__ kn, float eps,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t, T* __restrict__ q_out,
     uint32_t* err) {
-  const int units = n_q + 2 * n_kv;
+  // Prefill handles the value heads in vt_append_kernel (tiled transpose).
+  const int units = sb.decode ? n_q + 2 * n_kv : n_q + n_kv;
+  const int stride_units = n_q + 2 * n_kv;
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wv >= T_ * units) return;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     if (lane == 0) atomicOr(err, 4u);
     return;
   }
-  const float* src = qkv + (int64_t)t * units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
+  const float* src = qkv + (int64_t)t * stride_units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
   float a = src[lane], c = src[lane + 64];
   const KvGeom g{n_kv, layer};
   if (u < n_q + n_kv) {
@@ -129,12 +131,68 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
   }
 }
 
+// Prefill values: block (64-token tile of one sequence, kv head g).  The
+// tile's 64 x 128 values are read as rows, transposed through LDS and
+// written as 64 consecutive positions of each of the 128 value rows of the
+// cache, so both sides move whole cache lines.  Prefill positions start at 0,
+// so a tile starts at a multiple of 64 within its sequence.
+constexpr int VT_TILE = 64;
+
+struct VtTiles {
+  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of 64-token tiles per sequence
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict__ qkv, SeqBatch sb, VtTiles tt,
+                                                        const SeqState* __restrict__ st, T* __restrict__ kv,
+                                                        int layer, int n_q, int n_kv) {
+  __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
+  const int tix = blockIdx.x, g = blockIdx.y;
+  int b = 0;
+  {
+    int lo = 0, hi = sb.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int L = sb.cu[b + 1] - sb.cu[b];
+  const int p0 = (tix - tt.tile_cu[b]) * VT_TILE;
+  const int n = min(VT_TILE, L - p0);
+  const int units = n_q + 2 * n_kv;
+  const float* src = qkv + (int64_t)(sb.cu[b] + p0) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
+  // read: thread -> (token r, 4 dims); 256 threads cover 8 tokens per pass
+  const int c4 = (threadIdx.x & 31) * 4, r0 = threadIdx.x >> 5;
+  for (int r = r0; r < n; r += 8) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)r * units * Q3_HEAD_DIM + c4);
+    st_f<T>(&tile[c4 + 0][r], v.x);
+    st_f<T>(&tile[c4 + 1][r], v.y);
+    st_f<T>(&tile[c4 + 2][r], v.z);
+    st_f<T>(&tile[c4 + 3][r], v.w);
+  }
+  __syncthreads();
+  const SeqState s = st[sb.slot[b]];
+  T* vt = kv_vt(kv, s, KvGeom{n_kv, layer}, g);
+  // write: thread -> (dim, 16-byte run of positions)
+  constexpr int RUN = 16 / sizeof(T), RUNS = VT_TILE / RUN;
+  for (int e = threadIdx.x; e < Q3_HEAD_DIM * RUNS; e += 256) {
+    const int d = e / RUNS, k0 = (e % RUNS) * RUN;
+    T* dst = vt + (int64_t)d * s.cap + p0 + k0;
+    if (k0 + RUN <= n) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
+    } else {
+      for (int k = k0; k < n; ++k) dst[k - k0] = tile[d][k];
+    }
+  }
+}
+
 hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
                        void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
                        float eps, const float* cos_t, const float* sin_t, void* q_out,
                        uint32_t* err, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int64_t waves = (int64_t)T * (n_q + 2 * n_kv);
+  const int64_t waves = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
   dim3 grid((unsigned)((waves + 3) / 4));
   if (dtype == BF16)
     rope_append_kernel<bf16_t><<<grid, 256, 0, s>>>(qkv, T, sb, st, (bf16_t*)kv, layer, n_q, n_kv, qn, kn,
@@ -142,6 +200,16 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
   else
     rope_append_kernel<float><<<grid, 256, 0, s>>>(qkv, T, sb, st, (float*)kv, layer, n_q, n_kv, qn, kn,
                                                    eps, cos_t, sin_t, (float*)q_out, err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sb.decode) return e;
+  VtTiles tt;
+  tt.tile_cu[0] = 0;
+  for (int b = 0; b < sb.n; ++b) tt.tile_cu[b + 1] = tt.tile_cu[b] + (sb.cu[b + 1] - sb.cu[b] + VT_TILE - 1) / VT_TILE;
+  dim3 vgrid((unsigned)tt.tile_cu[sb.n], n_kv);
+  if (dtype == BF16)
+    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv);
+  else
+    vt_append_kernel<float><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (float*)kv, layer, n_q, n_kv);
   return hipGetLastError();
 }
 

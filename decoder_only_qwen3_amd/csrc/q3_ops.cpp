@@ -48,6 +48,7 @@ q3_status upload_states(int n, const int64_t* base, const int32_t* cap, const in
   std::vector<SeqState> st(n);
   for (int b = 0; b < n; ++b) {
     if (cap[b] <= 0 || cap[b] % 64 != 0) return op_fail(Q3_E_ARG, "capacities must be positive multiples of 64");
+    if (base[b] < 0 || base[b] % 64 != 0) return op_fail(Q3_E_ARG, "bases must be non-negative multiples of 64");
     if (len[b] < 0 || len[b] > cap[b]) return op_fail(Q3_E_ARG, "length outside capacity");
     st[b] = SeqState{base[b], cap[b], len[b]};
   }

@@ -241,7 +241,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   if (decode && bf) {
     int64_t maxcap = 1;
     for (int b = 0; b < sb.n; ++b) maxcap = std::max(maxcap, m->slots[sb.slot[b]].cap);
-    smax = fused_attn_smax(sb.n, c.n_kv_heads, std::min<int64_t>(maxcap, c.max_positions));
+    maxcap = std::min<int64_t>(maxcap, c.max_positions);
+    smax = fused_attn_smax(sb.n, c.n_kv_heads, maxcap);
   }
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.

@@ -71,8 +71,8 @@ q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_
 
 /* A one-layer KV arena for the attention ops: sequence b owns the elements
  * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):
- * keys [n_kv][cap][128] then values transposed [n_kv][128][cap]; h_cap[b] is
- * a multiple of 64.  h_len[b] = tokens already cached before the call.
+ * keys [n_kv][cap][128] then values transposed [n_kv][128][cap]; h_cap[b] and
+ * h_base[b] are multiples of 64 and d_kv is 16-byte aligned.  h_len[b] = tokens already cached before the call.
  *
  * Pasos 4-5: per-head RMSNorm (q_norm / k_norm) then rotate-half RoPE at each
  * token's position, queries to d_q_out [T][n_q][128], keys and values into the

@@ -316,6 +316,8 @@ def test_rope_append(dtype, decode):
         for i, p in enumerate(pos):
             np.testing.assert_allclose(K[:, p, :], k_ref[i], **tol)
             np.testing.assert_array_equal(Vt[:, :, p], v_ref[i].astype(np.float32))
+        if not decode:  # nothing written past the sequence (the last value tile is partial)
+            assert not np.any(K[:, lens[b]:, :]) and not np.any(Vt[:, :, lens[b]:])
 
 
 # ---------------------------------------------------------------- Paso 5: attention
