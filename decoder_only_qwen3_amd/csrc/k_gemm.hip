@@ -8,100 +8,48 @@
 // en MLX" -- Paso 5 (q/k/v and o projections), Paso 6 (SwiGLU: gate, up,
 // silu(gate) * up, down), Paso 7 (residual adds).
 //
-// Tiling: block tile (16*WM*GM) x (16*WN*GN), K step 64; GM x GN wavefronts,
-// each owning a (16*WM) x (16*WN) sub-tile as 16x16 MFMA tiles.  Large
-// problems use 256x256 tiles on 16 wavefronts, small ones 64x64 on 4.
-// Global -> register prefetch of the next K step overlaps the MFMAs of the
-// current one; tiles are staged through LDS with 16-byte row padding.
+// Tiling: block tile (16*WM*GM) x (16*WN*GN); GM x GN wavefronts, each owning
+// a (16*WM) x (16*WN) sub-tile as 16x16 MFMA tiles.  Two K loops:
+//  - register-prefetched (K step 64): the next step's global loads go to
+//    registers while the MFMAs use the LDS copy of the current one;
+//  - LDS pipeline (32-wide K slices, 4 slices in LDS, loaded directly from
+//    global memory into LDS): three slices in flight behind the one in use.
+// Large problems use 256x256 tiles on 16 wavefronts with the pipeline,
+// small ones 64x64 tiles on 4 wavefronts.
 #include "kernels.h"
 
 namespace q3k {
 
 namespace {
-constexpr int BK = 64, LDK = BK + 8;
+constexpr int BK = 64;
+
+// LDS row layout of a 64-wide K slice: SW = 0 pads each row by 16 bytes;
+// SW = 1 / 2 store it unpadded with the 16-byte chunk index XORed with
+// (row & 7) / ((row >> 1) & 7).  Counters on MI355X: the padded layout has
+// about 0.6 bank conflicts per LDS access in this kernel, both XOR layouts
+// none (the kernels use SW = 1).
+template <int SW>
+Q3_DEV int lds_off(int row, int col) {
+  if constexpr (SW == 0) return row * (BK + 8) + col;
+  const int x = SW == 1 ? (row & 7) : ((row >> 1) & 7);
+  return row * BK + ((((col >> 3) ^ x) << 3) | (col & 7));
+}
 
 Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
-// Block tile (16*WM*GM) x (16*WN*GN): GM x GN wavefronts, each owning a
-// (16*WM) x (16*WN) sub-tile of 16x16 MFMA tiles.
-template <int EPI, int WM, int WN, int GM, int GN>
-__global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int M,
-                                                                const bf16_t* __restrict__ W, int N, int K,
-                                                                void* __restrict__ out, int64_t ldo) {
-  constexpr int NT = 64 * GM * GN;
-  constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
-  constexpr int RSTEP = NT / 8;                      // rows covered by one pass of 16-byte loads
-  constexpr int LA = BM / RSTEP, LW = BN / RSTEP;    // 16-byte chunks per thread per K step
-  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile rows must be a multiple of the load pass");
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[2][BN * LDK];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / GN, wn = wid % GN;
-  const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-
-  u32x4 ra[LA], rw[LW];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = lrow + RSTEP * i;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      ra[i] = (bm0 + r < M) ? ld16(A + (int64_t)(bm0 + r) * K + k0 + lcol) : z;
-    }
-#pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      const int r = lrow + RSTEP * i;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      rw[i] = (bn0 + r < N) ? ld16(W + (int64_t)(bn0 + r) * K + k0 + lcol) : z;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(&sA[buf][(lrow + RSTEP * i) * LDK + lcol]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LW; ++i) *reinterpret_cast<u32x4*>(&sW[buf][(lrow + RSTEP * i) * LDK + lcol]) = rw[i];
-  };
-
-  f32x4 acc[WM][WN];
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[WM], bw[WN];
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 16 * WM + i * 16 + fr) * LDK + ks * 32 + fk]);
-#pragma unroll
-      for (int j = 0; j < WN; ++j)
-        bw[j] = *reinterpret_cast<const bf16x8*>(&sW[buf][(wn * 16 * WN + j * 16 + fr) * LDK + ks * 32 + fk]);
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // C layout of a 16x16 MFMA tile: lane l holds rows (l/16)*4 + r, column l%16.
-  const int rbase = bm0 + wm * 16 * WM + (lane >> 4) * 4;
-  const int cbase = bn0 + wn * 16 * WN + (lane & 15);
+// C layout of a 16x16 MFMA tile: lane l holds rows (l/16)*4 + r, column l%16.
+// (r0, c0): first row and column of the wavefront's (16*WM) x (16*WN) tile.
+template <int EPI, int WM, int WN>
+Q3_DEV void gemm_epilogue(const f32x4 (&acc)[WM][WN], int r0, int c0, int M, int N, void* __restrict__ out,
+                          int64_t ldo) {
+  const int lane = threadIdx.x & 63;
+  const int rbase = r0 + (lane >> 4) * 4;
+  const int cbase = c0 + (lane & 15);
   if constexpr (EPI == EPI_SWIGLU) {
     // Packed rows: every 32 rows of W are 16 gate rows then the matching 16 up
     // rows, so tile j=2p is gate and j=2p+1 is up for the same output column.
     bf16_t* o = reinterpret_cast<bf16_t*>(out);
-    const int ocol0 = (bn0 + wn * 16 * WN) / 2 + (lane & 15);
+    const int ocol0 = c0 / 2 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -136,7 +84,83 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* _
   }
 }
 
-template <int WM, int WN, int GM, int GN>
+// Block tile (16*WM*GM) x (16*WN*GN): GM x GN wavefronts, each owning a
+// (16*WM) x (16*WN) sub-tile of 16x16 MFMA tiles.
+template <int EPI, int WM, int WN, int GM, int GN, int SW>
+__global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int M,
+                                                                const bf16_t* __restrict__ W, int N, int K,
+                                                                void* __restrict__ out, int64_t ldo) {
+  constexpr int NT = 64 * GM * GN;
+  constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
+  constexpr int RSTEP = NT / 8;                      // rows covered by one pass of 16-byte loads
+  constexpr int LA = BM / RSTEP, LW = BN / RSTEP;    // 16-byte chunks per thread per K step
+  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile rows must be a multiple of the load pass");
+  constexpr int LDK = SW == 0 ? BK + 8 : BK;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][BN * LDK];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / GN, wn = wid % GN;
+  const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+
+  u32x4 ra[LA], rw[LW];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int r = lrow + RSTEP * i;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      ra[i] = (bm0 + r < M) ? ld16(A + (int64_t)(bm0 + r) * K + k0 + lcol) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      const int r = lrow + RSTEP * i;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      rw[i] = (bn0 + r < N) ? ld16(W + (int64_t)(bn0 + r) * K + k0 + lcol) : z;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4*>(&sA[buf][lds_off<SW>(lrow + RSTEP * i, lcol)]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) *reinterpret_cast<u32x4*>(&sW[buf][lds_off<SW>(lrow + RSTEP * i, lcol)]) = rw[i];
+  };
+
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[WM], bw[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][lds_off<SW>(wm * 16 * WM + i * 16 + fr, ks * 32 + fk)]);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        bw[j] = *reinterpret_cast<const bf16x8*>(&sW[buf][lds_off<SW>(wn * 16 * WN + j * 16 + fr, ks * 32 + fk)]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
+}
+
+template <int WM, int WN, int GM, int GN, int SW>
 hipError_t gemm_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out, int64_t ldo,
                        hipStream_t s) {
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN, NT = 64 * GM * GN;
@@ -144,13 +168,139 @@ hipError_t gemm_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int N, 
   switch (epi) {
     case EPI_STORE:
     case EPI_ARGMAX:
-      gemm_bf16_kernel<EPI_STORE, WM, WN, GM, GN><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_STORE, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     case EPI_RESADD:
-      gemm_bf16_kernel<EPI_RESADD, WM, WN, GM, GN><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_RESADD, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     case EPI_SWIGLU:
-      gemm_bf16_kernel<EPI_SWIGLU, WM, WN, GM, GN><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_SWIGLU, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pipelined variant
+// Same tiling, but the K loop is an NS-stage pipeline of 32-wide K slices
+// loaded straight from global memory into LDS (global_load_lds_dwordx4, no
+// register staging): while the MFMAs work on slice kt, slices kt+1 ..
+// kt+NS-1 are in flight, which covers the L2/MALL latency that a single
+// register-prefetched step does not.  One block barrier per slice.
+//
+// LDS: each load instruction of a wavefront fills 1 KiB = 16 rows x 64 bytes
+// (lane i -> row i/4, 16-byte chunk i%4).  Chunks are stored XOR-swizzled by
+// (row >> 1) & 3, so the MFMA fragment reads (16 rows, one chunk) spread
+// over the LDS banks; the lane loads the global chunk that belongs at its
+// fixed LDS position.
+constexpr int DBK = 32;
+
+Q3_DEV int dswz(int row) { return (row >> 1) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+Q3_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int EPI, int WM, int WN, int GM, int GN, int NS>
+__global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __restrict__ A, int M,
+                                                               const bf16_t* __restrict__ W, int N, int K,
+                                                               void* __restrict__ out, int64_t ldo) {
+  constexpr int NW = GM * GN;
+  constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
+  constexpr int GA = BM / 16, GB = BN / 16;  // 1 KiB load groups per slice
+  static_assert((GA + GB) % NW == 0, "load groups must split evenly over the wavefronts");
+  constexpr int LPW = (GA + GB) / NW;        // load instructions per wavefront per slice
+  constexpr int STAGE = (BM + BN) * DBK;     // bf16 elements per slice
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NS * STAGE];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / GN, wn = wid % GN;
+  const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
+
+  // This lane's source pointer and its wavefront's LDS offset per load group.
+  const bf16_t* src[LPW];
+  int dst[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int g = wid * LPW + u;
+    const int rr = lane >> 2, sc = lane & 3;
+    if (g < GA) {
+      const int row = g * 16 + rr;
+      src[u] = A + (int64_t)min(bm0 + row, M - 1) * K + ((sc ^ dswz(row)) << 3);
+      dst[u] = g * 16 * DBK;
+    } else {
+      const int row = (g - GA) * 16 + rr;
+      src[u] = W + (int64_t)min(bn0 + row, N - 1) * K + ((sc ^ dswz(row)) << 3);
+      dst[u] = BM * DBK + (g - GA) * 16 * DBK;
+    }
+  }
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int u = 0; u < LPW; ++u)  // (non-const pointers: with a const source the host pass drops the kernel stub)
+      __builtin_amdgcn_global_load_lds((void*)(src[u] + kt * DBK), (void*)(lds + buf * STAGE + dst[u]), 16, 0, 0);
+  };
+
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / DBK;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st);
+  const int fr = lane & 15, fq = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt is complete once at most the later slices' loads are pending
+    if (kt + NS - 2 < nk) wait_vm<(NS - 2) * LPW>();
+    else wait_vm<0>();
+    // A bare barrier: __syncthreads() would also wait for every load still in
+    // flight (its fence), emptying the pipeline.  The waits above cover this
+    // wavefront's slice-kt loads; the memory clobber keeps the compiler from
+    // moving LDS accesses across the barrier.
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const bf16_t* sa = lds + (kt % NS) * STAGE;
+    const bf16_t* sb = sa + BM * DBK;
+    bf16x8 af[WM], bw[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int row = wm * 16 * WM + i * 16 + fr;
+      af[i] = *reinterpret_cast<const bf16x8*>(sa + row * DBK + ((fq ^ dswz(row)) << 3));
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int row = wn * 16 * WN + j * 16 + fr;
+      bw[j] = *reinterpret_cast<const bf16x8*>(sb + row * DBK + ((fq ^ dswz(row)) << 3));
+    }
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
+  }
+  gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
+}
+
+template <int WM, int WN, int GM, int GN, int NS>
+hipError_t gemm_dma_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out, int64_t ldo,
+                           hipStream_t s) {
+  constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN, NT = 64 * GM * GN;
+  if (K % DBK != 0) return hipErrorInvalidValue;
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  switch (epi) {
+    case EPI_STORE:
+    case EPI_ARGMAX:
+      gemm_dma_kernel<EPI_STORE, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    case EPI_RESADD:
+      gemm_dma_kernel<EPI_RESADD, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      break;
+    case EPI_SWIGLU:
+      gemm_dma_kernel<EPI_SWIGLU, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     default:
       return hipErrorInvalidValue;
@@ -171,19 +321,24 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
   int cfg = g_gemm_cfg;
   if (cfg < 0) {
     // The largest tile whose grid still gives each of the 256 CUs a block:
-    // 256 x 256 (16 wavefronts), else 128 x 128, else 64 x 64.
+    // 256 x 256 (4-slice LDS pipeline, 16 wavefronts), else 128 x 128, else
+    // 64 x 64.  Measured on MI355X at M = 32768: 700-900 TFLOP/s for the
+    // q/k/v, gate/up and down shapes with the pipeline, 3-5 % above the
+    // register-prefetched 256 x 256 kernel.
     const int64_t g256 = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
     const int64_t g128 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
-    cfg = g256 >= 256 ? 6 : (g128 >= 256 ? 1 : 0);
+    cfg = g256 >= 256 ? 7 : (g128 >= 256 ? 1 : 0);
   }
   switch (cfg) {
-    case 0: return gemm_launch<2, 2, 2, 2>(epi, A, M, W, N, K, out, ldo, s);   //  64 x  64, 4 waves
-    case 1: return gemm_launch<4, 4, 2, 2>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 128, 4 waves
-    case 2: return gemm_launch<4, 4, 4, 2>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 128, 8 waves
-    case 3: return gemm_launch<4, 4, 2, 4>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 256, 8 waves
-    case 4: return gemm_launch<4, 8, 2, 2>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 256, 4 waves
-    case 5: return gemm_launch<8, 4, 2, 2>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 128, 4 waves
-    case 6: return gemm_launch<4, 4, 4, 4>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 256, 16 waves
+    case 0: return gemm_launch<2, 2, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   //  64 x  64, 4 waves
+    case 1: return gemm_launch<4, 4, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 128, 4 waves
+    case 2: return gemm_launch<4, 4, 4, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 128, 8 waves
+    case 3: return gemm_launch<4, 4, 2, 4, 1>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 256, 8 waves
+    case 4: return gemm_launch<4, 8, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 256, 4 waves
+    case 5: return gemm_launch<8, 4, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 128, 4 waves
+    case 6: return gemm_launch<4, 4, 4, 4, 1>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 256, 16 waves
+    case 7: return gemm_dma_launch<4, 4, 4, 4, 4>(epi, A, M, W, N, K, out, ldo, s);  // 256 x 256, 4-slice pipeline
+    case 8: return gemm_dma_launch<4, 4, 2, 2, 4>(epi, A, M, W, N, K, out, ldo, s);  // 128 x 128, 4-slice pipeline
     default: return hipErrorInvalidValue;
   }
 }

@@ -116,7 +116,7 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
 /* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
  * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,
- *   0..6 = fixed tile shapes (listed in k_gemm.hip).
+ *   0..8 = fixed tile shapes (listed in k_gemm.hip).
  * Q3OP_TUNE_FLASH_ROWS: prefill attention query rows per wavefront / 16,
  *   -1 = automatic, or 1, 2, 4.
  * Q3OP_TUNE_ROWGEMV: single-row GEMV shape, -1 = automatic, else

@@ -121,7 +121,7 @@ def test_linear_store_and_residual(kernel, M, N, K):
     assert _rel(got - base, ref) < 2e-5
 
 
-@pytest.mark.parametrize("cfg", list(range(7)))
+@pytest.mark.parametrize("cfg", list(range(9)))
 def test_gemm_tile_configurations(cfg):
     """Every prefill GEMM tile shape, with ragged row and column tails."""
     _, lib = ops()
@@ -147,7 +147,7 @@ def test_gemm_tile_configurations(cfg):
 
 def test_tune_rejects_bad_values():
     _, lib = ops()
-    assert lib.q3op_tune(1, 7) != 0
+    assert lib.q3op_tune(1, 9) != 0
     assert lib.q3op_tune(2, 3) != 0
     assert lib.q3op_tune(3, 3 + 256) != 0
     assert lib.q3op_tune(3, 4 + 5 * 256) != 0
