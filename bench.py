@@ -27,6 +27,36 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+# rows per block of the single-row lm_head kernel (4 per wavefront x 4 wavefronts
+# for K = 1024): one (max, index) partial per block
+ROWGEMV_ARGMAX_ROWS_PER_BLOCK = 16
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_rowgemv_q06b_traffic.md")
+TRAFFIC_SOURCES = ["decoder_only_qwen3_amd/csrc/k_rowgemv.hip", "decoder_only_qwen3_amd/csrc/common.h"]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for p in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kname, M):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3
+    counter summary, or None when there is none for this kernel or its sources
+    have changed since the counters were taken."""
+    import re
+    if M != 1 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    dig = re.search(r"sources-sha256: ([0-9a-f]{64})", text)
+    byts = re.search(r"traffic-bytes-per-launch: ([0-9.e+]+)", text)
+    if not dig or not byts or dig.group(1) != sources_digest():
+        return None
+    return float(byts.group(1))
 
 
 def parse():
@@ -41,15 +71,18 @@ def parse():
     return ap.parse_args()
 
 
-def decode_bytes_per_step(d, ctx):
-    """Algorithmic HBM bytes of one batch-1 decode step at context `ctx` (new token included)."""
+def decode_bytes_per_step(d, ctxs):
+    """Algorithmic HBM bytes of one decode step of len(ctxs) sequences, sequence b
+    attending over ctxs[b] keys (its new token included): every weight once, each
+    sequence's cache read, the new keys/values written, one logits row each."""
     L, H, Q, KV, I, V = d.n_layers, d.hidden, d.n_q_heads * 128, d.n_kv_heads * 128, d.ffn, d.vocab
     e = 2 if d.dtype == "bf16" else 4
+    B = len(ctxs)
     weights = (L * (H * (Q + 2 * KV) + Q * H + 2 * I * H + I * H) + V * H) * e
     norms = (L * (2 * H + 256) + H) * 4
-    kv_read = ctx * L * 2 * KV * e
-    kv_write = L * 2 * KV * e
-    logits = V * 4
+    kv_read = sum(ctxs) * L * 2 * KV * e
+    kv_write = B * L * 2 * KV * e
+    logits = B * V * 4
     return weights + norms + kv_read + kv_write + logits
 
 
@@ -149,39 +182,38 @@ def main():
     prefill_tok_s = sum(lens) * args.steps / (sum(pre_ms) / 1e3)
     decode_tok_s = B * steps_dec * args.steps / (sum(dec_ms) / 1e3)
 
-    # Whole-step decode HBM fraction (batch-1 byte count, averaged over the contexts).
-    if B == 1:
-        byts = np.mean([decode_bytes_per_step(d, lens[0] + 1 + i) for i in range(steps_dec)])
-        dec_step_s = (sum(dec_ms) / 1e3) / (args.steps * steps_dec)
-        decode_hbm = {"bytes_per_step": float(byts), "achieved_GBs": byts / dec_step_s / 1e9,
-                      "frac": byts / dec_step_s / 1e9 / HBM_PEAK_GBS}
-    else:
-        decode_hbm = None
+    # Whole-step decode HBM fraction: algorithmic bytes averaged over the steps.
+    byts = np.mean([decode_bytes_per_step(d, [L + 1 + i for L in lens]) for i in range(steps_dec)])
+    dec_step_s = (sum(dec_ms) / 1e3) / (args.steps * steps_dec)
+    decode_hbm = {"bytes_per_step": float(byts), "achieved_GBs": byts / dec_step_s / 1e9,
+                  "frac": byts / dec_step_s / 1e9 / HBM_PEAK_GBS}
     pf = prefill_flops(d, lens)
     prefill_mfma = {"flops": pf, "achieved_TFLOPs": pf / (np.mean(pre_ms) / 1e3) / 1e12,
                     "frac": pf / (np.mean(pre_ms) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
-    # Dominant kernel: the tied lm_head weight stream (one launch per decode step,
-    # 151936 x 1024 bf16 = 311 MB), timed with HIP events on the model's stream
-    # over repeated launches of the same kernel on the model's own embedding table.
+    # Roofline kernel: the tied lm_head weight stream, the largest single transfer
+    # of a decode step (151936 x 1024 bf16 = 311 MB per launch), in the kernel the
+    # step itself uses (single-row GEMV for one sequence, the weight-streaming
+    # MFMA kernel for several).  Timed with HIP events on the model's stream over
+    # repeated launches on the model's own embedding table.
     lib = _lib.load()
     M = B
     N, K = d.vocab, d.hidden
+    kern = 4 if M == 1 else 1
     with torch.cuda.stream(m.stream):
         x = torch.zeros((M, K), dtype=torch.int16, device=dev)
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
-        nxt = torch.empty(M, dtype=torch.int32, device=dev)
-        wsb = lib.q3op_linear_workspace_bytes(1, 3, M, N, K)
+        wsb = lib.q3op_linear_workspace_bytes(kern, 3, M, N, K)
         ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)
     embed_ptr = m.bufs[0].data_ptr()  # the embedding table sits at offset 0 of the weight region
     # d_next = NULL: only the lm_head kernel itself (logits + per-block partials) is launched
     for _ in range(3):
-        _lib.check(lib.q3op_linear(1, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
+        _lib.check(lib.q3op_linear(kern, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
                                    ws.data_ptr(), ws.numel(), m.sh))
     k0, k1 = ev(), ev()
     k0.record(m.stream)
     for _ in range(args.kernel_reps):
-        _lib.check(lib.q3op_linear(1, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
+        _lib.check(lib.q3op_linear(kern, 3, x.data_ptr(), M, embed_ptr, N, K, out.data_ptr(), N, None,
                                    ws.data_ptr(), ws.numel(), m.sh))
     k1.record(m.stream)
     torch.cuda.synchronize()
@@ -194,8 +226,12 @@ def main():
         c_dst.copy_(c_src)
     torch.cuda.synchronize()
     del c_src, c_dst
-    alg_bytes = N * K * 2 + M * K * 2 + M * N * 4 + (N // 16) * M * 8
+    parts = ROWGEMV_ARGMAX_ROWS_PER_BLOCK if M == 1 else 16
+    alg_bytes = N * K * 2 + M * K * 2 + M * N * 4 + ((N + parts - 1) // parts) * M * 8
     achieved = alg_bytes / (per_launch_ms / 1e3) / 1e9
+    kname = ("rowgemv_kernel<EPI_ARGMAX> (lm_head + argmax partials, M=1)" if M == 1 else
+             "skinny_kernel<EPI_ARGMAX> (lm_head + argmax partials, M=%d)" % M)
+    traffic = measured_traffic(kname, M)
 
     line = {
         "metric": "decode tok/s + prefill tok/s (1 GPU) and % of HBM / bf16-MFMA roofline",
@@ -218,9 +254,9 @@ def main():
         "decode_ms_per_token_step": round(float(np.mean(dec_ms)) / steps_dec, 4),
         "decode_hbm": decode_hbm,
         "prefill_mfma": prefill_mfma,
-        "roofline": {"bound": "hbm", "kernel": "skinny_kernel<EPI_ARGMAX> (lm_head + argmax partials, M=%d)" % M,
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "per_launch_us": round(per_launch_ms * 1e3, 2), "alg_bytes": alg_bytes},
         "host_setup_s": round(t_gen, 1),
     }

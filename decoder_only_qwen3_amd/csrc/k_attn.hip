@@ -64,8 +64,11 @@ Q3_DEV u32x4 mask_keys(u32x4 v, int key0, int limit) {
 
 // ---------------------------------------------------------------- prefill
 constexpr int KT = 64;          // keys per tile
-constexpr int LDSK = 128 + 8;   // key tile row stride (elements)
-constexpr int LDSV = KT + 8;    // value^T tile row stride
+// LDS tiles are stored unpadded with the 16-byte chunk index of each row
+// XOR-swizzled by the row (keys: 16 chunks per row, values^T: 8), so the
+// MFMA fragment reads (16 rows, one chunk) do not collide in LDS banks.
+Q3_DEV int koff(int key, int col) { return key * 128 + ((((col >> 3) ^ (key & 15)) << 3) | (col & 7)); }
+Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ (dim & 7)) << 3) | (key & 7)); }
 
 struct TileTable {
   int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
     const bf16_t* __restrict__ kv, int layer, int n_q, int n_kv, int qt, bf16_t* __restrict__ o,
     float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * LDSK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * LDSV];  // fp16 bits
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * KT];  // fp16 bits
 
   const int total = tt.tile_cu[sb.n];
   const int tile = total - 1 - (int)blockIdx.x;  // late (long) tiles first
@@ -143,8 +146,8 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sK[buf][((tid >> 4) + 16 * i) * LDSK + (tid & 15) * 8]) = rk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][((tid >> 3) + 32 * i) * LDSV + (tid & 7) * 8]) = bf16x8_to_f16x8(rv[i]);
+      *reinterpret_cast<u32x4*>(&sK[buf][koff((tid >> 4) + 16 * i, (tid & 15) * 8)]) = rk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][voff((tid >> 3) + 32 * i, (tid & 7) * 8)]) = bf16x8_to_f16x8(rv[i]);
     }
   };
 
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
         const int krow = c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][krow * LDSK + ks * 32 + fq * 8]);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][koff(krow, ks * 32 + fq * 8)]);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf, qf[cb][ks], sacc[c][sbk][cb]);
         }
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
       }
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const f16x8 vf = *reinterpret_cast<const f16x8*>(&sV[buf][(d * 16 + fr) * LDSV + c * 32 + fq * 8]);
+        const f16x8 vf = *reinterpret_cast<const f16x8*>(&sV[buf][voff(d * 16 + fr, c * 32 + fq * 8)]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = mfma16_f16(vf, pf[cb], oacc[d][cb]);
       }

@@ -94,7 +94,7 @@ q3_status rowgemv_op(int epi, const void* X, const float* gnorm, float eps, cons
   float* av = epi == EPI_ARGMAX ? (float*)(ws + w.amax_val) : nullptr;
   int32_t* ai = epi == EPI_ARGMAX ? (int32_t*)(ws + w.amax_idx) : nullptr;
   OP_TRY(rowgemv_bf16(epi, X, (const bf16_t*)W, N, K, gnorm, eps, out, av, ai, s));
-  if (epi == EPI_ARGMAX) {
+  if (epi == EPI_ARGMAX && next) {
     SeqBatch none;
     std::memset(&none, 0, sizeof(none));
     OP_TRY(argmax_finish(av, ai, rowgemv_argmax_blocks(N, K), 1, next, none, nullptr, (uint32_t*)(ws + w.err), s));
@@ -153,7 +153,8 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   if (!d_x || !d_w || !d_out || M < 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
   if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
   if (epi == EPI_ARGMAX && M > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "logits epilogue needs M <= 64");
-  if (epi == EPI_ARGMAX && !d_next && kernel != Q3OP_SKINNY) return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
+  if (epi == EPI_ARGMAX && !d_next && kernel != Q3OP_SKINNY && kernel != Q3OP_ROWGEMV)
+    return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
   RowMap rows;
   rows.n = M;
   for (int i = 0; i < M && i < Q3_MAX_BATCH; ++i) rows.row[i] = i;

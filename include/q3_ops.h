@@ -40,8 +40,8 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  *   2 SwiGLU: W rows packed in runs of 16 gate rows then 16 up rows,
  *     out[m][j] = silu(gate_j) * up_j written in X's dtype (ldo >= N/2);
  *   3 logits: store float32 out[M][ldo] and d_next[m] = argmax (lowest index
- *     on ties).  With kernel 1 and d_next == NULL only the logits and the
- *     kernel's per-block (max, index) partials are produced (one launch).
+ *     on ties).  With kernel 1 or 4 and d_next == NULL only the logits and
+ *     the kernel's per-block (max, index) partials are produced (one launch).
  * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0);
  * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
  * kernel 2 = float32 GEMV (float32 model);
