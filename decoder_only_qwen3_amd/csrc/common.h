@@ -102,7 +102,8 @@ struct SeqState {
 };
 
 // KV arena addressing.  A slot's region holds, for each layer, the keys as
-// [kv_head][cap][128] followed by the values transposed as [kv_head][128][cap].
+// [kv_head][cap][128] followed by the values as [kv_head][cap/32][128][32]
+// (transposed within blocks of 32 keys).
 struct KvGeom {
   int32_t n_kv;
   int32_t layer;
@@ -111,6 +112,11 @@ template <typename T>
 Q3_DEV T* kv_k(T* arena, const SeqState& s, KvGeom g, int head) {
   return arena + s.base + ((int64_t)(g.layer * 2) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;
 }
+// Values are stored in blocks of 32 keys, each block [128 dims][32 keys]: a
+// 32-key run of every dim is one contiguous 8 KiB read, and a dim's 8-key
+// run is 16 contiguous bytes (the MFMA operand).  vt_off gives the element
+// of (key, dim) from the head's value base.
+Q3_DEV int64_t vt_off(int key, int dim) { return ((int64_t)(key >> 5) * Q3_HEAD_DIM + dim) * 32 + (key & 31); }
 template <typename T>
 Q3_DEV T* kv_vt(T* arena, const SeqState& s, KvGeom g, int head) {
   return arena + s.base + ((int64_t)(g.layer * 2 + 1) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;

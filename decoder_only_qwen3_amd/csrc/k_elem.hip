@@ -126,15 +126,16 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     st_f<T>(dst + lane + 64, rc);
   } else {
     T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
-    st_f<T>(dst + (int64_t)lane * s.cap + pos, a);
-    st_f<T>(dst + (int64_t)(lane + 64) * s.cap + pos, c);
+    st_f<T>(dst + vt_off(pos, lane), a);
+    st_f<T>(dst + vt_off(pos, lane + 64), c);
   }
 }
 
 // Prefill values: block (64-token tile of one sequence, kv head g).  The
 // tile's 64 x 128 values are read as rows, transposed through LDS and
-// written as 64 consecutive positions of each of the 128 value rows of the
-// cache, so both sides move whole cache lines.  Prefill positions start at 0,
+// written as 16-byte runs of consecutive positions into the cache's value
+// blocks ([128 dims][32 keys] per 32 positions), so both sides move whole
+// cache lines.  Prefill positions start at 0,
 // so a tile starts at a multiple of 64 within its sequence.
 constexpr int VT_TILE = 64;
 
@@ -178,11 +179,10 @@ __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict_
   constexpr int RUN = 16 / sizeof(T), RUNS = VT_TILE / RUN;
   for (int e = threadIdx.x; e < Q3_HEAD_DIM * RUNS; e += 256) {
     const int d = e / RUNS, k0 = (e % RUNS) * RUN;
-    T* dst = vt + (int64_t)d * s.cap + p0 + k0;
-    if (k0 + RUN <= n) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
+    if (k0 + RUN <= n) {  // a run never crosses a 32-key block (p0 is a multiple of 64)
+      *reinterpret_cast<u32x4*>(vt + vt_off(p0 + k0, d)) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
     } else {
-      for (int k = k0; k < n; ++k) dst[k - k0] = tile[d][k];
+      for (int k = k0; k < n; ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
     }
   }
 }

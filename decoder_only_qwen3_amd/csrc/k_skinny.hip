@@ -21,7 +21,7 @@
 //
 // NORM = true: X is not given; the prologue computes it from the float32
 // residual rows x and the norm weight g as bf16(x * rsqrt(mean(x^2)+eps) * g),
-// the same rounding point as the standalone RMSNorm kernel (decode, M <= 8).
+// the same rounding point as the standalone RMSNorm kernel (decode, M <= 64).
 #include "kernels.h"
 
 namespace q3k {
@@ -30,7 +30,7 @@ namespace {
 Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
 constexpr int kMaxWaves = 16;
-constexpr int kNormMaxM = 8;
+constexpr int kNormMaxM = 64;
 
 template <int EPI, int MT, int NST, bool NORM>
 __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ Xin, int M,
@@ -43,7 +43,9 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int k0 = wid * (NST * 32) + (lane >> 4) * 8;
+  // Split K (RESADD only): block (x, y) covers K slice y of gridDim.y.
+  const int nsplit = gridDim.y, sk = blockIdx.y;
+  const int k0 = sk * (K / nsplit) + wid * (NST * 32) + (lane >> 4) * 8;
   const int row0 = blockIdx.x * RG * 16;
 
   // Weight fragments first: they are the HBM stream.
@@ -58,31 +60,43 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
 
   float* red = smem;                                  // [nw][RG][MT][256]
   float* inv = smem + nw * RG * MT * 256;             // [kNormMaxM] (NORM only)
-  // NORM: this wavefront's slice of the float32 residual rows, loaded once;
-  // the row sums of squares are reduced from the slices across wavefronts.
-  float4 xs[NORM ? MT : 1][NORM ? NST : 1][2];
+  // NORM: the row sums of squares are reduced from the wavefronts' slices of
+  // the float32 residual rows.  One 16-row tile (M <= 16): the slice stays in
+  // registers; more rows: it is read again (from L2) when the bf16 operand is
+  // formed, rather than held in registers across the reduction.
+  constexpr bool XREG = NORM && MT == 1;
+  float4 xs[XREG ? NST : 1][2];
   if constexpr (NORM) {
     const float* x = reinterpret_cast<const float*>(Xin);
-    const int m = lane & 15;  // MT == 1 when NORM (M <= 8)
-    float ss = 0.f;
+    float ss[MT];
 #pragma unroll
-    for (int s2 = 0; s2 < NST; ++s2) {
-      if (m < M) {
-        const float* xp = x + (int64_t)m * K + k0 + s2 * 32;
-        xs[0][s2][0] = *reinterpret_cast<const float4*>(xp);
-        xs[0][s2][1] = *reinterpret_cast<const float4*>(xp + 4);
-      } else {
-        xs[0][s2][0] = xs[0][s2][1] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + (lane & 15);
+      ss[mt] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NST; ++s2) {
+        float4 a = float4{0.f, 0.f, 0.f, 0.f}, b = a;
+        if (m < M) {
+          const float* xp = x + (int64_t)m * K + k0 + s2 * 32;
+          a = *reinterpret_cast<const float4*>(xp);
+          b = *reinterpret_cast<const float4*>(xp + 4);
+        }
+        if constexpr (XREG) {
+          xs[s2][0] = a;
+          xs[s2][1] = b;
+        }
+        ss[mt] += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
       }
-      const float4 a = xs[0][s2][0], b = xs[0][s2][1];
-      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
+      // lanes m, m+16, m+32, m+48 hold row m's four K groups
+      ss[mt] += __shfl_xor(ss[mt], 16, 64);
+      ss[mt] += __shfl_xor(ss[mt], 32, 64);
     }
-    // lanes m, m+16, m+32, m+48 hold row m's four K groups
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (lane < kNormMaxM) red[wid * kNormMaxM + lane] = ss;
+    if (lane < 16) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[wid * kNormMaxM + mt * 16 + lane] = ss[mt];
+    }
     __syncthreads();
-    if (threadIdx.x < kNormMaxM) {
+    if (threadIdx.x < M) {
       float t = 0.f;
       for (int w = 0; w < nw; ++w) t += red[w * kNormMaxM + threadIdx.x];
       inv[threadIdx.x] = rsqrtf(t / (float)K + eps);
@@ -104,8 +118,15 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
       u32x4 xv = {0u, 0u, 0u, 0u};
       if constexpr (NORM) {
         if (live) {
-          const float4 a = xs[0][s][0];
-          const float4 b = xs[0][s][1];
+          float4 a, b;
+          if constexpr (XREG) {
+            a = xs[s][0];
+            b = xs[s][1];
+          } else {
+            const float* xp = reinterpret_cast<const float*>(Xin) + (int64_t)m * K + k0 + s * 32;
+            a = *reinterpret_cast<const float4*>(xp);
+            b = *reinterpret_cast<const float4*>(xp + 4);
+          }
           const float4 ga = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32);
           const float4 gb = *reinterpret_cast<const float4*>(gnorm + k0 + s * 32 + 4);
           const float r = inv[m];
@@ -182,11 +203,47 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
         bf16_t* o = reinterpret_cast<bf16_t*>(out);
         o[(int64_t)m * ldo + (row0 >> 1) + nl] = f2bf(silu_f(v0) * v1);
       } else if constexpr (EPI == EPI_RESADD) {
-        float* o = reinterpret_cast<float*>(out);
-        o[(int64_t)m * ldo + row0 + nl] += v0;
+        if (nsplit == 1) {
+          float* o = reinterpret_cast<float*>(out);
+          o[(int64_t)m * ldo + row0 + nl] += v0;
+        }
       } else {
         float* o = reinterpret_cast<float*>(out);
         o[(int64_t)m * ldo + row0 + nl] = v0;
+      }
+    }
+    if constexpr (EPI == EPI_RESADD) {
+      if (nsplit > 1) {
+        // Publish this slice's sums (agent scope: coherent across the L2
+        // slices), count the slices of this row group, and let the last one
+        // add them in slice order (deterministic) into the residual rows.
+        float* part = amax_val;                                  // [N/16][nsplit][MT*256]
+        uint32_t* cnt = reinterpret_cast<uint32_t*>(amax_idx);  // [N/16], zero between calls
+        float* mine = part + ((int64_t)blockIdx.x * nsplit + sk) * NE;
+        for (int e = threadIdx.x; e < NE; e += blockDim.x)
+          __hip_atomic_store(mine + e, red[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        __shared__ int last;
+        if (threadIdx.x == 0)
+          last = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(nsplit - 1);
+        __syncthreads();
+        if (last) {
+          const float* grp = part + (int64_t)blockIdx.x * nsplit * NE;
+          float* o = reinterpret_cast<float*>(out);
+          for (int e = threadIdx.x; e < NE; e += blockDim.x) {
+            const int mt = e >> 8, le = e & 255;
+            const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
+            const int nl = (le >> 2) & 15;
+            if (m >= M) continue;
+            float v = 0.f;
+            for (int j = 0; j < nsplit; ++j)
+              v += __hip_atomic_load(grp + (int64_t)j * NE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            o[(int64_t)m * ldo + row0 + nl] += v;
+          }
+          if (threadIdx.x == 0) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -229,30 +286,67 @@ hipError_t launch_norm(bool norm, const SkinnyPlan& p, int MT, dim3 grid, const 
 
 // Wavefronts per block and K steps per wavefront: 32-wide K steps in runs of
 // 4 (more wavefronts, more loads in flight per CU) unless that needs more than
-// 16 wavefronts or more than 48 KiB of LDS for the reduction.
+// 16 wavefronts or more than 96 KiB of LDS for the reduction (gfx950 gives a
+// block up to 160 KiB).
 SkinnyPlan skinny_plan(int epi, int M, int N, int K) {
   (void)N;
   const int rg = (epi == EPI_SWIGLU) ? 2 : 1;
   const int MT = (M + 15) / 16;
   SkinnyPlan p{4, K / 128};
-  if (p.waves > kMaxWaves || p.waves * rg * MT > 48) p = SkinnyPlan{8, K / 256};
+  if (p.waves > kMaxWaves || p.waves * rg * MT > 96) p = SkinnyPlan{8, K / 256};
   return p;
 }
 
 bool skinny_norm_ok(int M) { return M <= kNormMaxM; }
 
+// Whether a decode step should fold the RMSNorm into the projection: for one
+// 16-row tile the residual slice is read once into registers; beyond that
+// every block reads all rows of x twice, which on MI355X cost more (13 us at
+// 32 rows) than a separate RMSNorm kernel plus bf16 operands (5.5 + 6 us).
+bool skinny_norm_fuse(int M) { return M <= 16; }
+
+// Residual projections with few row groups (N/16 < 128, e.g. the 1024-wide o
+// and down projections: 64 blocks) split K over up to 4 block slices so that
+// the weight and activation streams spread over more CUs; slices of at least
+// 512 so each block keeps 4+ wavefronts.
+int skinny_splits(int epi, int M, int N, int K) {
+  (void)M;
+  if (epi != EPI_RESADD || N / 16 >= 128) return 1;
+  for (int sp = 4; sp >= 2; sp >>= 1)
+    if (K % (sp * 128) == 0 && K / sp >= 512) return sp;
+  return 1;
+}
+
+size_t skinny_split_floats(int M, int N, int K) {
+  const int sp = skinny_splits(EPI_RESADD, M, N, K);
+  if (sp <= 1) return 0;
+  return (size_t)(N / 16) * sp * ((M + 15) / 16) * 256;
+}
+
 int skinny_argmax_blocks(int N) { return N / 16; }
 
 hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
-                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s) {
+                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s,
+                       float* split_part, uint32_t* split_cnt) {
   if (M <= 0) return hipSuccess;
   if (M > 64) return hipErrorInvalidValue;
   const bool norm = gnorm != nullptr;
   if (norm && M > kNormMaxM) return hipErrorInvalidValue;
+  const int sp = (!norm && split_part && split_cnt) ? skinny_splits(epi, M, N, K) : 1;
+  if (sp > 1) {
+    // K slices: the kernel sees the slice length through its plan
+    const SkinnyPlan p = skinny_plan(epi, M, N, K / sp);
+    const int MT = (M + 15) / 16;
+    if (N % 16 != 0 || p.waves * p.nst * 32 * sp != K || p.waves > kMaxWaves || p.waves * MT > 96)
+      return hipErrorInvalidValue;
+    dim3 grid(N / 16, sp);
+    return launch_norm<EPI_RESADD>(false, p, MT, grid, X, M, W, N, K, nullptr, eps, out, ldo, split_part,
+                                   reinterpret_cast<int32_t*>(split_cnt), s);
+  }
   const SkinnyPlan p = skinny_plan(epi, M, N, K);
   const int rg = (epi == EPI_SWIGLU) ? 2 : 1;
   const int MT = (M + 15) / 16;
-  if (N % (16 * rg) != 0 || p.waves * p.nst * 32 != K || p.waves > kMaxWaves || p.waves * rg * MT > 48 ||
+  if (N % (16 * rg) != 0 || p.waves * p.nst * 32 != K || p.waves > kMaxWaves || p.waves * rg * MT > 96 ||
       (norm && K % 4 != 0))
     return hipErrorInvalidValue;
   dim3 grid(N / (16 * rg));

@@ -57,13 +57,21 @@ struct SkinnyPlan {
 };
 SkinnyPlan skinny_plan(int epi, int M, int N, int K);
 bool skinny_norm_ok(int M);
+bool skinny_norm_fuse(int M);  // decode steps fold RMSNorm in for M <= 16
 int skinny_argmax_blocks(int N);
 // M <= 64 rows times W[N,K]^T (bf16).  gnorm == nullptr: X is bf16 [M][K].
-// gnorm != nullptr (M <= 8): X is the float32 residual [M][K] and the kernel
+// gnorm != nullptr (M <= 64): X is the float32 residual [M][K] and the kernel
 // applies RMSNorm with weight gnorm and eps first.  EPI_ARGMAX also writes
 // per-block (max, index) partials, N/16 blocks x M.
 hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
-                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s);
+                       float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s,
+                       float* split_part = nullptr, uint32_t* split_cnt = nullptr);
+// Split-K for RESADD with few row groups: K slices per row group (1 = none)
+// and the float workspace the slices' partial sums need (split_part); the
+// split_cnt array holds N/16 counters that must be zero before the first call
+// (every call leaves them zero).
+int skinny_splits(int epi, int M, int N, int K);
+size_t skinny_split_floats(int M, int N, int K);
 // Row-parallel bf16 GEMV for decode with M <= 4 rows: one wavefront per
 // output row (EPI_STORE / EPI_RESADD), K a multiple of 512 up to 4096.
 bool rowdot_ok(int M, int K);

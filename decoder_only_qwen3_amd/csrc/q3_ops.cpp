@@ -30,15 +30,17 @@ q3_status op_hip(hipError_t e, const char* what) {
 size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
 struct SkinnyWs {
-  size_t err, amax_val, amax_idx, total;
+  size_t err, amax_val, amax_idx, split_part, split_cnt, total;
 };
-SkinnyWs skinny_ws(int M, int N) {
+SkinnyWs skinny_ws(int M, int N, int K) {
   SkinnyWs w;
   const size_t groups = (size_t)N / 16;
   w.err = 0;
   w.amax_val = al(16);
   w.amax_idx = w.amax_val + al(groups * M * 4);
-  w.total = w.amax_idx + al(groups * M * 4);
+  w.split_part = w.amax_idx + al(groups * M * 4);
+  w.split_cnt = w.split_part + al(skinny_split_floats(M, N, K) * 4);
+  w.total = w.split_cnt + al((groups + 1) * 4);
   return w;
 }
 
@@ -59,11 +61,13 @@ q3_status upload_states(int n, const int64_t* base, const int32_t* cap, const in
 
 q3_status skinny_op(int epi, const void* X, int M, const float* gnorm, float eps, const void* W, int N, int K,
                     void* out, int64_t ldo, int32_t* next, void* d_ws, size_t ws_bytes, hipStream_t s) {
-  SkinnyWs w = skinny_ws(M, N);
+  SkinnyWs w = skinny_ws(M, N, K);
   if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace too small");
   char* ws = (char*)d_ws;
+  uint32_t* cnt = (uint32_t*)(ws + w.split_cnt);
+  OP_TRY(fill_u32(cnt, 0u, (int64_t)N / 16 + 1, s));
   OP_TRY(skinny_bf16(epi, X, M, (const bf16_t*)W, N, K, gnorm, eps, out, ldo, (float*)(ws + w.amax_val),
-                     (int32_t*)(ws + w.amax_idx), s));
+                     (int32_t*)(ws + w.amax_idx), s, (float*)(ws + w.split_part), cnt));
   if (epi == EPI_ARGMAX && next) {
     SeqBatch none;
     std::memset(&none, 0, sizeof(none));
@@ -140,8 +144,7 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
 
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K) {
   (void)epi;
-  (void)K;
-  if (kernel == Q3OP_SKINNY) return skinny_ws(M, N).total;
+  if (kernel == Q3OP_SKINNY) return skinny_ws(M, N, K).total;
   if (kernel == Q3OP_ROWGEMV) return row_ws(N).total;
   return 256;
 }
@@ -208,7 +211,7 @@ q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_
     return rowgemv_op(epi, d_x, d_gnorm, eps, d_w, N, K, d_out, d_next, d_ws, ws_bytes, (hipStream_t)stream);
   }
   if (kernel != Q3OP_SKINNY) return op_fail(Q3_E_ARG, "the fused RMSNorm prologue exists in kernels 1 and 4");
-  if (!skinny_norm_ok(M)) return op_fail(Q3_E_UNSUPPORTED, "the fused RMSNorm prologue takes M <= 8");
+  if (!skinny_norm_ok(M)) return op_fail(Q3_E_UNSUPPORTED, "the fused RMSNorm prologue takes M <= 64");
   return skinny_op(epi, d_x, M, d_gnorm, eps, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, (hipStream_t)stream);
 }
 

@@ -51,7 +51,7 @@ struct WeightLayout {
 };
 
 struct WsLayout {
-  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, state, err, total;
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, state, err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
   int amax_blocks;
 };
@@ -141,6 +141,11 @@ WsLayout ws_layout(const q3_config& c) {
   W.amax_idx = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
   W.attn_part = take((size_t)max_attn_splits_rows(c) * c.n_q_heads * 130 * 4);
   W.attn_cnt = take((size_t)Q3_MAX_BATCH * c.n_kv_heads * 4);
+  // split-K partials of the batched-decode residual projections (o, down)
+  const int mb = std::min(c.max_slots, Q3_MAX_BATCH);
+  W.lin_part = take(std::max<size_t>(16, std::max(skinny_split_floats(mb, (int)H, (int)Q),
+                                                  skinny_split_floats(mb, (int)H, (int)I))) * 4);
+  W.lin_cnt = take((H / 16 + 1) * 4);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -255,7 +260,7 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     const LayerW& lw = m->wl.layers[l];
     // Paso 3 + Paso 5: normalised input, fused q/k/v projection.  Decode with
     // few rows folds the RMSNorm into the projection kernel's prologue.
-    const bool fuse_norm = bf && decode && (one_h || skinny_norm_ok(T));
+    const bool fuse_norm = bf && decode && (one_h || skinny_norm_fuse(T));
     if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
     if (!bf) {
       LAUNCH(gemv_f32(EPI_STORE, (const float*)h, T, m->W<float>(lw.qkv), NQKV, H, qkv, NQKV, s));
@@ -295,7 +300,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else if (rows_o) {
       LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s));
+      LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s,
+                         m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
       LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
     }
@@ -316,7 +322,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       else if (rows_d)
         LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
       else
-        LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s));
+        LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s,
+                           m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
       LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
@@ -451,6 +458,7 @@ q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, voi
   HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
   HIP_TRY(fill_u32(m->err(), 0u, 4, s));
   HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.attn_cnt), 0u, (int64_t)Q3_MAX_BATCH * c.n_kv_heads, s));
+  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.lin_cnt), 0u, (int64_t)c.hidden / 16 + 1, s));
   HIP_TRY(hipStreamSynchronize(s));
   m->bound = true;
   g_err.clear();

@@ -63,7 +63,7 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
 /* Pasos 3 + 5: a decode projection with RMSNorm fused into its prologue:
  * X = bf16(x * rsqrt(mean(x^2) + eps) * g) from float32 rows d_x [M][K] and
  * float32 weight d_gnorm [K], then epilogue `epi` as in q3op_linear.
- * kernel 1 (weight-streaming, M <= 8, epi 0-3) or kernel 4 (single row,
+ * kernel 1 (weight-streaming, M <= 64, epi 0-3) or kernel 4 (single row,
  * M = 1, epi 0 or 2).  Workspace: q3op_linear_workspace_bytes(kernel, ...). */
 q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_t M, const float* d_gnorm,
                            float eps, const void* d_w, int32_t N, int32_t K, void* d_out, int64_t ldo,
@@ -71,7 +71,8 @@ q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_
 
 /* A one-layer KV arena for the attention ops: sequence b owns the elements
  * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):
- * keys [n_kv][cap][128] then values transposed [n_kv][128][cap]; h_cap[b] and
+ * keys [n_kv][cap][128] then values [n_kv][cap/32][128][32] (32-key blocks,
+ * each transposed: value dim d of key t at ((t/32)*128 + d)*32 + t%32); h_cap[b] and
  * h_base[b] are multiples of 64 and d_kv is 16-byte aligned.  h_len[b] = tokens already cached before the call.
  *
  * Pasos 4-5: per-head RMSNorm (q_norm / k_norm) then rotate-half RoPE at each

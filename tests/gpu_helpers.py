@@ -28,6 +28,19 @@ def weights_for(dims: q3synth.ModelDims, seed: int):
     return q3synth.make_weights(dims, seed)
 
 
+# ---------------------------------------------------------------- KV cache value layout
+def vt_blocks(vt: np.ndarray) -> np.ndarray:
+    """Values as the kernels store them, from the logical transposed view
+    vt [n_kv][128][cap]: blocks of 32 keys, each [128 dims][32 keys]."""
+    n_kv, dim, cap = vt.shape
+    return np.ascontiguousarray(vt.reshape(n_kv, dim, cap // 32, 32).transpose(0, 2, 1, 3)).reshape(-1)
+
+
+def vt_logical(flat: np.ndarray, n_kv: int, cap: int) -> np.ndarray:
+    """Inverse of vt_blocks: [n_kv][128][cap] view of a stored value region."""
+    return flat.reshape(n_kv, cap // 32, 128, 32).transpose(0, 2, 1, 3).reshape(n_kv, 128, cap)
+
+
 # ---------------------------------------------------------------- device marshalling
 def dev_bf16(a: np.ndarray):
     """bf16-valued float32 array -> torch int16 tensor of its bit patterns on cuda:0."""

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import q3synth
-from gpu_helpers import call, dev_bf16, dev_f32, host_bf16, ops, rand_bf16
+from gpu_helpers import call, dev_bf16, dev_f32, host_bf16, ops, rand_bf16, vt_blocks, vt_logical
 from oracle import attention_rows, rms_norm, rope_cos_sin, rope_rotate, silu, to_bf16
 
 pytestmark = pytest.mark.gpu
@@ -312,7 +312,7 @@ def test_rope_append(dtype, decode):
         cap = caps[b]
         region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
         K = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
-        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        Vt = vt_logical(region[n_kv * cap * 128:], n_kv, cap)
         for i, p in enumerate(pos):
             np.testing.assert_allclose(K[:, p, :], k_ref[i], **tol)
             np.testing.assert_array_equal(Vt[:, :, p], v_ref[i].astype(np.float32))
@@ -351,9 +351,10 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
         cap = caps[b]
         region = np.zeros(2 * n_kv * cap * 128, np.float32)
         Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
-        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        Vt = np.zeros((n_kv, 128, cap), np.float32)
         Kc[:, :ctx[b], :] = K.transpose(1, 0, 2)
         Vt[:, :, :ctx[b]] = V.transpose(1, 2, 0)
+        region[n_kv * cap * 128:] = vt_blocks(Vt)
         arena[bases[b]:bases[b] + region.size] = region
     if bf:
         bits = q3synth.bf16_bits(arena)
@@ -362,9 +363,10 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
             cap = caps[b]
             reg = bits[bases[b]:bases[b] + 2 * n_kv * cap * 128]
             Kc = reg[:n_kv * cap * 128].reshape(n_kv, cap, 128)
-            Vt = reg[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+            Vt = vt_logical(reg[n_kv * cap * 128:], n_kv, cap).copy()
             Kc[:, ctx[b]:, :] = 0x7FC0
             Vt[:, :, ctx[b]:] = 0x7FC0
+            reg[n_kv * cap * 128:] = vt_blocks(Vt)
         dkv = torch.from_numpy(bits.view(np.int16)).to("cuda:0")
         dq = dev_bf16(q)
         out = torch.zeros((q.shape[0], n_q, 128), dtype=torch.int16, device="cuda:0")
@@ -451,7 +453,9 @@ def test_attention_f32(mode):
 
 
 @pytest.mark.parametrize("epi,M,N", [(EPI_STORE, 1, 4096), (EPI_SWIGLU, 3, 6144), (EPI_ARGMAX, 1, 8192),
-                                     (EPI_STORE, 8, 4096), (EPI_SWIGLU, 1, 6144)])
+                                     (EPI_STORE, 8, 4096), (EPI_SWIGLU, 1, 6144), (EPI_STORE, 17, 4096),
+                                     (EPI_SWIGLU, 32, 6144), (EPI_SWIGLU, 64, 6144), (EPI_STORE, 64, 4096),
+                                     (EPI_ARGMAX, 40, 8192)])
 @pytest.mark.parametrize("kernel", [SKINNY, ROWGEMV])
 def test_norm_linear_fused_prologue(kernel, epi, M, N):
     """RMSNorm folded into a decode projection's prologue equals rmsnorm -> bf16 -> projection."""
@@ -531,7 +535,9 @@ def test_decode_attention_fused_rope_append(prior, smax):
         cap = caps[b]
         region = np.zeros(2 * n_kv * cap * 128, np.float32)
         region[:n_kv * cap * 128].reshape(n_kv, cap, 128)[:, :prior[b], :] = K.transpose(1, 0, 2)
-        region[n_kv * cap * 128:].reshape(n_kv, 128, cap)[:, :, :prior[b]] = V.transpose(1, 2, 0)
+        vt = np.zeros((n_kv, 128, cap), np.float32)
+        vt[:, :, :prior[b]] = V.transpose(1, 2, 0)
+        region[n_kv * cap * 128:] = vt_blocks(vt)
         arena[bases[b]:bases[b] + region.size] = region
     qkv = rng.standard_normal((n, units * 128)).astype(np.float32)
     qn = q3synth.round_to_bf16((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
@@ -556,7 +562,7 @@ def test_decode_attention_fused_rope_append(prior, smax):
         cap = caps[b]
         region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
         Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
-        Vt = region[n_kv * cap * 128:].reshape(n_kv, 128, cap)
+        Vt = vt_logical(region[n_kv * cap * 128:], n_kv, cap)
         np.testing.assert_allclose(Kc[:, prior[b], :], k_new[0], rtol=2 ** -7, atol=1e-6)
         np.testing.assert_array_equal(Vt[:, :, prior[b]], v_new[0].astype(np.float32))
         keys = np.concatenate([old_k[b].astype(np.float64), k_new], axis=0)
