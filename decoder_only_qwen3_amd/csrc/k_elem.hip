@@ -79,13 +79,28 @@ hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, c
 }
 
 // ---------------------------------------------------------------- Pasos 4-5
-// One wavefront per (token, head unit); units are the n_q query heads, then
-// the n_kv key heads, then the n_kv value heads of the fused projection row.
-// Lane l owns dims l and l+64, which is exactly one RoPE pair.
+// Sixteen lanes per (token, head unit); units are the n_q query heads, then
+// the n_kv key heads, then (decode only) the n_kv value heads of the fused
+// projection row.  Lane j of a unit owns dims 4j..4j+3 and 64+4j..64+4j+3,
+// i.e. four whole RoPE pairs, read and written as 16-byte runs.
 //   query/key: per-head RMSNorm (weights q_norm / k_norm, same eps), then the
-//              pair rotation by pos * theta^(-l/64) read from the cos/sin table;
+//              pair rotation by pos * theta^(-i/64) read from the cos/sin table;
 //              queries go to q_out [T][n_q][128], keys to the cache row `pos`.
-//   value:     stored unchanged into the transposed value block at column pos.
+//   value:     (decode) stored unchanged into the cache's value block.
+template <typename T>
+Q3_DEV void store4(T* p, float a, float b, float c, float d);
+template <>
+Q3_DEV void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+}
+template <>
+Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  u32x2 w;
+  w[0] = pack_bf2(a, b);
+  w[1] = pack_bf2(c, d);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ qkv, int T_, SeqBatch sb, SeqState* __restrict__ st, T* __restrict__ kv,
@@ -95,39 +110,50 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
   // Prefill handles the value heads in vt_append_kernel (tiled transpose).
   const int units = sb.decode ? n_q + 2 * n_kv : n_q + n_kv;
   const int stride_units = n_q + 2 * n_kv;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wv >= T_ * units) return;
-  const int t = wv / units, u = wv - t * units;
+  const int64_t gu = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // unit index (uniform per 16 lanes)
+  const int j = threadIdx.x & 15;
+  if (gu >= (int64_t)T_ * units) return;
+  const int t = (int)(gu / units), u = (int)(gu - (int64_t)t * units);
   const int b = seq_of_token(sb, t);
   const SeqState s = st[sb.slot[b]];
   const int pos = sb.decode ? s.len : t - sb.cu[b];
   if (pos < 0 || pos >= s.cap) {  // host validation makes this unreachable
-    if (lane == 0) atomicOr(err, 4u);
+    if (j == 0) atomicOr(err, 4u);
     return;
   }
   const float* src = qkv + (int64_t)t * stride_units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
-  float a = src[lane], c = src[lane + 64];
+  float4 a = *reinterpret_cast<const float4*>(src + 4 * j);
+  float4 c = *reinterpret_cast<const float4*>(src + 64 + 4 * j);
   const KvGeom g{n_kv, layer};
   if (u < n_q + n_kv) {
     const float* w = u < n_q ? qn : kn;
-    const float ss = wave_sum(a * a + c * c);
+    float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
     const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
-    a = a * inv * w[lane];
-    c = c * inv * w[lane + 64];
-    const float cs = cos_t[(int64_t)pos * 64 + lane], sn = sin_t[(int64_t)pos * 64 + lane];
-    const float ra = a * cs - c * sn, rc = a * sn + c * cs;
+    const float4 wa = *reinterpret_cast<const float4*>(w + 4 * j);
+    const float4 wc = *reinterpret_cast<const float4*>(w + 64 + 4 * j);
+    a = float4{a.x * inv * wa.x, a.y * inv * wa.y, a.z * inv * wa.z, a.w * inv * wa.w};
+    c = float4{c.x * inv * wc.x, c.y * inv * wc.y, c.z * inv * wc.z, c.w * inv * wc.w};
+    const float4 cs = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * 64 + 4 * j);
+    const float4 sn = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * 64 + 4 * j);
     T* dst;
     if (u < n_q)
       dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
     else
       dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
-    st_f<T>(dst + lane, ra);
-    st_f<T>(dst + lane + 64, rc);
+    store4<T>(dst + 4 * j, a.x * cs.x - c.x * sn.x, a.y * cs.y - c.y * sn.y, a.z * cs.z - c.z * sn.z,
+              a.w * cs.w - c.w * sn.w);
+    store4<T>(dst + 64 + 4 * j, a.x * sn.x + c.x * cs.x, a.y * sn.y + c.y * cs.y, a.z * sn.z + c.z * cs.z,
+              a.w * sn.w + c.w * cs.w);
   } else {
     T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
-    st_f<T>(dst + vt_off(pos, lane), a);
-    st_f<T>(dst + vt_off(pos, lane + 64), c);
+    const float av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      st_f<T>(dst + vt_off(pos, 4 * j + k), av[k]);
+      st_f<T>(dst + vt_off(pos, 64 + 4 * j + k), cv[k]);
+    }
   }
 }
 
@@ -192,8 +218,8 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                        float eps, const float* cos_t, const float* sin_t, void* q_out,
                        uint32_t* err, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int64_t waves = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
-  dim3 grid((unsigned)((waves + 3) / 4));
+  const int64_t units = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
+  dim3 grid((unsigned)((units + 15) / 16));
   if (dtype == BF16)
     rope_append_kernel<bf16_t><<<grid, 256, 0, s>>>(qkv, T, sb, st, (bf16_t*)kv, layer, n_q, n_kv, qn, kn,
                                                     eps, cos_t, sin_t, (bf16_t*)q_out, err);
