@@ -84,6 +84,21 @@ Q3_DEV u32x4 bf16x8_to_f16x8(u32x4 v) {
 
 Q3_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Sixteen-byte accesses with the agent-scope cache policy (sc1: written through
+// to, and read back from, memory that every XCD's L2 sees), for partial results
+// that another block merges.  The four-byte agent-scope atomics carry the same
+// policy, but four times the transactions.
+constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc1
+Q3_DEV __amdgpu_buffer_rsrc_t agent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+Q3_DEV void st4_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCpolSc1);
+}
+Q3_DEV f32x4 ld4_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolSc1));
+}
+
 // Sequences of one call.  Prefill: token t of the call belongs to sequence b
 // with cu[b] <= t < cu[b+1] and sits at position t - cu[b].  Decode: token b
 // is the single new token of sequence b, at position = that slot's length.

@@ -86,10 +86,20 @@ Q3_DEV void gemm_epilogue(const f32x4 (&acc)[WM][WN], int r0, int c0, int M, int
 
 // Block tile (16*WM*GM) x (16*WN*GN): GM x GN wavefronts, each owning a
 // (16*WM) x (16*WN) sub-tile of 16x16 MFMA tiles.
+//
+// Split K (EPI_RESADD, gridDim.z > 1): block z accumulates the K slice z, publishes
+// its partial tile with agent-scope stores (coherent across the L2 slices),
+// and the last slice to finish a tile adds the partials in slice order
+// (deterministic) into the residual.  Small grids (M = 512 prefill) get four
+// times the blocks and a quarter of the dependent K steps.
+constexpr int kGemmMaxSplit = 4;
+
 template <int EPI, int WM, int WN, int GM, int GN, int SW>
 __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int M,
                                                                 const bf16_t* __restrict__ W, int N, int K,
-                                                                void* __restrict__ out, int64_t ldo) {
+                                                                void* __restrict__ out, int64_t ldo,
+                                                                float* __restrict__ part,
+                                                                uint32_t* __restrict__ cnt) {
   constexpr int NT = 64 * GM * GN;
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
   constexpr int RSTEP = NT / 8;                      // rows covered by one pass of 16-byte loads
@@ -102,6 +112,9 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* _
   const int wm = wid / GN, wn = wid % GN;
   const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
   const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+  const int nsplit = gridDim.z, ksl = K / nsplit;
+  A += (int64_t)blockIdx.z * ksl;  // this block's K slice (rows keep stride K)
+  W += (int64_t)blockIdx.z * ksl;
 
   u32x4 ra[LA], rw[LW];
   auto gload = [&](int k0) {
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* _
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = ksl / BK;
   gload(0);
   sstore(0);
   __syncthreads();
@@ -157,24 +170,70 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* _
     __syncthreads();
   }
 
+  if constexpr (EPI == EPI_RESADD) {
+    if (nsplit > 1) {
+      // partial tile of slice z: float4 v of thread t at ((tile*nsplit + z)*NA + v)*NT + t,
+      // so one store instruction covers a contiguous kilobyte
+      constexpr int NA = WM * WN;
+      const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+      const auto rs = agent_rsrc(part, (uint32_t)gridDim.x * gridDim.y * nsplit * NA * NT * 16);
+      const uint32_t tbase = ((uint32_t)tile * nsplit * NA * NT + tid) * 16;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          st4_agent(rs, tbase + ((blockIdx.z * NA + i * WN + j) * NT) * 16, acc[i][j]);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      __shared__ int last;
+      if (tid == 0)
+        last = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(nsplit - 1);
+      __syncthreads();
+      if (!last) return;
+      // all slices' partials (this block's own reads back what it stored), loaded
+      // together and summed in slice order; slices past nsplit re-read the last
+      // one and add nothing
+      f32x4 pz[kGemmMaxSplit][WM][WN];
+#pragma unroll
+      for (int z = 0; z < kGemmMaxSplit; ++z)
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            pz[z][i][j] = ld4_agent(rs, tbase + ((min(z, nsplit - 1) * NA + i * WN + j) * NT) * 16);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int z = 0; z < kGemmMaxSplit; ++z) t += z < nsplit ? pz[z][i][j] : f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[i][j] = t;
+        }
+      if (tid == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
 }
 
 template <int WM, int WN, int GM, int GN, int SW>
 hipError_t gemm_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out, int64_t ldo,
-                       hipStream_t s) {
+                       hipStream_t s, float* part = nullptr, uint32_t* cnt = nullptr, int nsplit = 1) {
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN, NT = 64 * GM * GN;
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  if (nsplit > 1 && (epi != EPI_RESADD || !part || !cnt || nsplit > kGemmMaxSplit || K % (nsplit * BK) != 0))
+    return hipErrorInvalidValue;
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, nsplit);
   switch (epi) {
     case EPI_STORE:
     case EPI_ARGMAX:
-      gemm_bf16_kernel<EPI_STORE, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_STORE, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, part, cnt);
       break;
     case EPI_RESADD:
-      gemm_bf16_kernel<EPI_RESADD, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_RESADD, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, part, cnt);
       break;
     case EPI_SWIGLU:
-      gemm_bf16_kernel<EPI_SWIGLU, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_bf16_kernel<EPI_SWIGLU, WM, WN, GM, GN, SW><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, part, cnt);
       break;
     default:
       return hipErrorInvalidValue;
@@ -313,11 +372,32 @@ int g_gemm_cfg = -1;  // tile configuration override (q3op_tune); -1 = automatic
 
 void gemm_set_config(int cfg) { g_gemm_cfg = cfg; }
 
+int gemm_splits(int epi, int M, int N, int K) {
+  // residual GEMMs whose 64 x 64 grid leaves CUs idle: up to 4 K slices of at
+  // least 512 (8 K steps), at most 1024 blocks
+  if (epi != EPI_RESADD) return 1;
+  const int64_t tiles = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
+  if (tiles >= 256) return 1;
+  for (int sp = kGemmMaxSplit; sp >= 2; sp >>= 1)
+    if (K % (sp * BK) == 0 && K / sp >= 512 && tiles * sp <= 1024) return sp;
+  return 1;
+}
+
+size_t gemm_split_floats(int M, int N, int K) {
+  const int sp = gemm_splits(EPI_RESADD, M, N, K);
+  if (sp <= 1) return 0;
+  return (size_t)((N + 63) / 64) * ((M + 63) / 64) * sp * 64 * 64;
+}
+
 hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
-                     int64_t ldo, hipStream_t s) {
+                     int64_t ldo, hipStream_t s, float* split_part, uint32_t* split_cnt) {
   if (M <= 0) return hipSuccess;
   if (K % BK != 0 || N % 16 != 0) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && N % 64 != 0) return hipErrorInvalidValue;
+  if (g_gemm_cfg < 0 && split_part && split_cnt) {
+    const int sp = gemm_splits(epi, M, N, K);
+    if (sp > 1) return gemm_launch<2, 2, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s, split_part, split_cnt, sp);
+  }
   int cfg = g_gemm_cfg;
   if (cfg < 0) {
     // The largest tile whose grid still gives each of the 256 CUs a block:

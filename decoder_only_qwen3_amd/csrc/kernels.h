@@ -46,7 +46,12 @@ hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 // ---------------------------------------------------------------- k_gemm.hip
 // C[M,N] = A[M,K] . W[N,K]^T with bf16 operands on MFMA; K % 64 == 0.
 hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
-                     int64_t ldo, hipStream_t s);
+                     int64_t ldo, hipStream_t s, float* split_part = nullptr, uint32_t* split_cnt = nullptr);
+// Split-K of residual GEMMs on small grids: slices (1 = none) and the float
+// workspace their partial tiles need; split_cnt holds one zeroed counter per
+// 64 x 64 output tile (every call leaves them zero).
+int gemm_splits(int epi, int M, int N, int K);
+size_t gemm_split_floats(int M, int N, int K);
 void gemm_set_config(int cfg);  // tile configuration override; -1 = automatic
 void flash_set_rows(int cb);    // prefill attention rows per wavefront / 16 (1, 2, 4); -1 = automatic
 

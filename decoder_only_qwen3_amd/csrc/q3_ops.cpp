@@ -2,6 +2,7 @@
 // pass on explicit buffers, for parity tests and kernel benchmarks.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -41,6 +42,20 @@ SkinnyWs skinny_ws(int M, int N, int K) {
   w.split_part = w.amax_idx + al(groups * M * 4);
   w.split_cnt = w.split_part + al(skinny_split_floats(M, N, K) * 4);
   w.total = w.split_cnt + al((groups + 1) * 4);
+  return w;
+}
+
+// Split-K partial tiles and per-tile counters of the residual GEMM.
+struct GemmWs {
+  size_t part, cnt, total;
+  int64_t tiles;
+};
+GemmWs gemm_ws(int M, int N, int K) {
+  GemmWs w;
+  w.tiles = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
+  w.part = 0;
+  w.cnt = al(gemm_split_floats(M, N, K) * 4);
+  w.total = std::max<size_t>(256, w.cnt + al(w.tiles * 4));
   return w;
 }
 
@@ -143,9 +158,9 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
 }
 
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K) {
-  (void)epi;
   if (kernel == Q3OP_SKINNY) return skinny_ws(M, N, K).total;
   if (kernel == Q3OP_ROWGEMV) return row_ws(N).total;
+  if (kernel == Q3OP_GEMM && epi == EPI_RESADD) return gemm_ws(M, N, K).total;
   return 256;
 }
 
@@ -163,7 +178,16 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   for (int i = 0; i < M && i < Q3_MAX_BATCH; ++i) rows.row[i] = i;
   uint32_t* no_err = nullptr;
   if (kernel == Q3OP_GEMM) {
-    OP_TRY(gemm_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, d_out, ldo, s));
+    float* part = nullptr;
+    uint32_t* cnt = nullptr;
+    if (epi == EPI_RESADD && gemm_split_floats(M, N, K) > 0) {
+      const GemmWs w = gemm_ws(M, N, K);
+      if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace smaller than q3op_linear_workspace_bytes");
+      part = (float*)((char*)d_ws + w.part);
+      cnt = (uint32_t*)((char*)d_ws + w.cnt);
+      OP_TRY(fill_u32(cnt, 0u, w.tiles, s));
+    }
+    OP_TRY(gemm_bf16(epi, (const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, d_out, ldo, s, part, cnt));
     if (epi == EPI_ARGMAX) {
       if (!d_ws || ws_bytes < 4) return op_fail(Q3_E_ARG, "logits epilogue needs 4 bytes of workspace");
       no_err = (uint32_t*)d_ws;

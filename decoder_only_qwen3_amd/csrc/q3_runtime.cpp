@@ -9,6 +9,7 @@
 // cache; the position of a new token is the number already cached).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -141,11 +142,16 @@ WsLayout ws_layout(const q3_config& c) {
   W.amax_idx = take((size_t)W.amax_blocks * Q3_MAX_BATCH * 4);
   W.attn_part = take((size_t)max_attn_splits_rows(c) * c.n_q_heads * 130 * 4);
   W.attn_cnt = take((size_t)Q3_MAX_BATCH * c.n_kv_heads * 4);
-  // split-K partials of the batched-decode residual projections (o, down)
+  // split-K partials of the residual projections (o, down): batched decode
+  // (weight-streaming kernel) and short prefills (tiled GEMM)
   const int mb = std::min(c.max_slots, Q3_MAX_BATCH);
-  W.lin_part = take(std::max<size_t>(16, std::max(skinny_split_floats(mb, (int)H, (int)Q),
-                                                  skinny_split_floats(mb, (int)H, (int)I))) * 4);
-  W.lin_cnt = take((H / 16 + 1) * 4);
+  size_t part = std::max(skinny_split_floats(mb, (int)H, (int)Q), skinny_split_floats(mb, (int)H, (int)I));
+  for (int64_t t = 64; t < R + 64; t += 64) {
+    const int tt = (int)std::min<int64_t>(t, R);
+    part = std::max({part, gemm_split_floats(tt, (int)H, (int)Q), gemm_split_floats(tt, (int)H, (int)I)});
+  }
+  W.lin_part = take(std::max<size_t>(16, part) * 4);
+  W.lin_cnt = take(std::max<size_t>(H / 16 + 1, 256) * 4);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -303,7 +309,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s,
                          m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
-      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s,
+                       m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     }
     // SwiGLU MLP + residual (Paso 6, Paso 7).
     if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.post_norm), H, c.rms_eps, h, s));
@@ -326,7 +333,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
                            m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
       LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
-      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s,
+                       m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     }
   }
   return Q3_OK;
@@ -458,7 +466,7 @@ q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, voi
   HIP_TRY(hipMemcpyAsync(m->state(), zero.data(), zero.size() * sizeof(SeqState), hipMemcpyHostToDevice, s));
   HIP_TRY(fill_u32(m->err(), 0u, 4, s));
   HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.attn_cnt), 0u, (int64_t)Q3_MAX_BATCH * c.n_kv_heads, s));
-  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.lin_cnt), 0u, (int64_t)c.hidden / 16 + 1, s));
+  HIP_TRY(fill_u32(m->WS<uint32_t>(m->wsl.lin_cnt), 0u, std::max<int64_t>((int64_t)c.hidden / 16 + 1, 256), s));
   HIP_TRY(hipStreamSynchronize(s));
   m->bound = true;
   g_err.clear();
