@@ -42,7 +42,10 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  *   3 logits: store float32 out[M][ldo] and d_next[m] = argmax (lowest index
  *     on ties).  With kernel 1 or 4 and d_next == NULL only the logits and
  *     the kernel's per-block (max, index) partials are produced (one launch).
- * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0);
+ * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0;
+ * the residual epilogue splits K over up to four blocks when the output has
+ * fewer than 256 tiles of 64 x 64, merging the slices in a fixed order, and
+ * then needs q3op_linear_workspace_bytes of workspace, else Q3_E_ARG);
  * kernel 1 = bf16 weight-streaming kernel (decode and lm_head; M <= 64);
  * kernel 2 = float32 GEMV (float32 model);
  * kernel 3 = bf16 row-per-wavefront GEMV (decode with M <= 4, epi 0 or 1,
