@@ -19,9 +19,13 @@ BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["k_elem.hip", "k_gemm.hip", "k_skinny.hip", "k_rowgemv.hip", "k_attn.hip", "q3_runtime.cpp", "q3_ops.cpp"]
 
 # Packed fp32 VALU forms are kept out of the device code on purpose.
+# MFMA accumulators live in ordinary VGPRs: in the accumulation-register form
+# the compiler copied every accumulator out and back around each conditional
+# rescale or epilogue (tens of extra VALU instructions per loop iteration).
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-result",
 ]
 

@@ -92,7 +92,7 @@ def load() -> C.CDLL:
         "q3op_rope_append": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP,
                                    C.c_float, C.c_double, I32, VP, VP, SZ, VP]),
         "q3op_tune": (I32, [I32, I32]),
-        "q3op_attention_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "q3op_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "q3op_decode_attn_fused_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "q3op_decode_attn_fused": (I32, [VP, I32, i64p, i32p, i32p, VP, I32, I32, VP, VP, C.c_float, C.c_double,
                                          I32, I32, VP, VP, SZ, VP]),

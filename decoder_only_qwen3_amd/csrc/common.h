@@ -137,6 +137,14 @@ Q3_DEV T* kv_vt(T* arena, const SeqState& s, KvGeom g, int head) {
   return arena + s.base + ((int64_t)(g.layer * 2 + 1) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;
 }
 
+// fp16 staging of a prefill call's values (the P.V operand of the flash
+// kernel): per kv head, the keys of sequence b from key vstage_start(sb, b)
+// on (a multiple of 64, keys padded to whole 64-key tiles with zeros), in the
+// value layout above.  vstage_keys(T, n) keys per head cover any call of T
+// tokens in n sequences.
+Q3_DEV int vstage_start(const SeqBatch& sb, int b) { return ((sb.cu[b] + 64 * b) >> 6) << 6; }
+inline int64_t vstage_keys(int64_t T, int n) { return (T + 64 * (int64_t)n + 127) / 64 * 64; }
+
 Q3_DEV int seq_of_token(const SeqBatch& sb, int t) {
   if (sb.decode) return t;
   int lo = 0, hi = sb.n - 1;

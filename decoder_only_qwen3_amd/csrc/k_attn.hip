@@ -19,10 +19,12 @@
 // P.V product.  No shuffles or LDS round trips are needed for P.
 //
 // Precision: S = Q.K^T takes the bf16 queries and keys as they are.  The P.V
-// product runs on fp16 operands: the softmax weights are rounded to fp16
-// (relative error 2^-11, eight times finer than bf16) and the bf16 values are
-// converted to fp16 exactly.  The softmax denominator sums the rounded
-// weights, so the output is a properly normalised average of the values.
+// product runs on fp16 MFMA operands: the bf16 values convert to fp16 exactly,
+// and each softmax weight enters as two fp16 terms (fp16(p) and the fp16 of
+// the remainder), about 22 significant bits.  A single fp16 weight (11 bits)
+// moved the attention output by ~2^-12 of its size, enough to flip many of
+// its bf16 roundings; downstream of those flips the logits of a two-layer
+// random-init model moved by up to 3e-2 of their RMS.
 #include <algorithm>
 
 #include "kernels.h"
@@ -34,21 +36,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 Q3_DEV float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Round eight softmax weights to fp16 in place (so the caller can sum the
-// rounded values) and pack them as an MFMA operand.
-Q3_DEV f16x8 pack_p(f32x4& a, f32x4& b) {
-  u32x4 u;
-  u[0] = pack_f16x2(a[0], a[1]);
-  u[1] = pack_f16x2(a[2], a[3]);
-  u[2] = pack_f16x2(b[0], b[1]);
-  u[3] = pack_f16x2(b[2], b[3]);
-  const f16x8 h = as_f16x8(u);
+// Eight softmax weights as two fp16 MFMA operands, hi = fp16(p) and
+// lo = fp16(p - hi): hi + lo carries about 22 significant bits, so the P.V
+// product keeps near-fp32 weights while running on fp16 MFMA.  The weights
+// (unrounded) are added to `sum`.
+struct PSplit {
+  f16x8 hi, lo;
+};
+Q3_DEV PSplit split_p(const f32x4& a, const f32x4& b, float& sum) {
+  const float p[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[i] = (float)h[i];
-    b[i] = (float)h[4 + i];
+    const f16x2 hh = __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, f16x2);
+    h[i] = __builtin_bit_cast(uint32_t, hh);
+    l[i] = pack_f16x2(p[2 * i] - (float)hh[0], p[2 * i + 1] - (float)hh[1]);
+    sum += p[2 * i] + p[2 * i + 1];
   }
-  return h;
+  return PSplit{as_f16x8(h), as_f16x8(l)};
 }
 
 // Zero the bf16 elements of an 8-key run whose key index is >= limit.
@@ -66,6 +71,7 @@ Q3_DEV u32x4 mask_keys(u32x4 v, int key0, int limit) {
 
 // ---------------------------------------------------------------- prefill
 constexpr int KT = 64;          // keys per tile
+constexpr float kLazyLog2 = 8.f;  // headroom of the stale reference maximum (log2 units)
 // LDS tiles are stored unpadded with the 16-byte chunk index of each row
 // XOR-swizzled by the row (keys: 16 chunks per row, values^T: 8), so the
 // MFMA fragment reads (16 rows, one chunk) do not collide in LDS banks.
@@ -82,10 +88,10 @@ struct TileTable {
 // keys are double-buffered in LDS and shared by the 4 wavefronts; more rows
 // per wavefront means fewer LDS reads per MFMA.
 template <int CB>
-__global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
+__global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
-    const bf16_t* __restrict__ kv, int layer, int n_q, int n_kv, int qt, bf16_t* __restrict__ o,
-    float scale_log2) {
+    const bf16_t* __restrict__ kv, const uint16_t* __restrict__ vstage, int64_t vh_keys, int layer, int n_q,
+    int n_kv, int qt, bf16_t* __restrict__ o, float scale_log2) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * 128];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * KT];  // fp16 bits
 
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
   const SeqState s = st[sb.slot[b]];
   const KvGeom geo{n_kv, layer};
   const bf16_t* Kc = kv_k(kv, s, geo, g);
-  const bf16_t* Vt = kv_vt(kv, s, geo, g);
+  const uint16_t* Vh = vstage + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;  // fp16, zero-padded
   const int group = n_q / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
@@ -142,14 +148,14 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
       rk[i] = ld16(Kc + (int64_t)key * 128 + (tid & 15) * 8);
       const int dim = (tid >> 3) + 32 * i;
       const int key0 = kt * KT + (tid & 7) * 8;
-      rv[i] = mask_keys(ld16(Vt + vt_off(key0, dim)), key0, L);
+      rv[i] = ld16(Vh + vt_off(key0, dim));
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *reinterpret_cast<u32x4*>(&sK[buf][koff((tid >> 4) + 16 * i, (tid & 15) * 8)]) = rk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][voff((tid >> 3) + 32 * i, (tid & 7) * 8)]) = bf16x8_to_f16x8(rv[i]);
+      *reinterpret_cast<u32x4*>(&sV[buf][voff((tid >> 3) + 32 * i, (tid & 7) * 8)]) = rv[i];
     }
   };
 
@@ -158,10 +164,10 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
   for (int d = 0; d < 8; ++d)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun[CB], lrun[CB];
+  float mref[CB], lrun[CB];  // reference maximum (scaled, log2 units) and weight sum per row
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    mrun[cb] = -INFINITY;
+    mref[cb] = -INFINITY;
     lrun[cb] = 0.f;
   }
 
@@ -173,74 +179,114 @@ __global__ __launch_bounds__(256, 1) void flash_prefill_kernel(
     if (kt + 1 < ntiles) gload(kt + 1);
 
     // S^T for the tile: sacc[c][sb][cb], keys kt*64 + c*32 + 8*fq + 4*sb + r.
-    f32x4 sacc[2][2][CB];
+    // All sixteen key fragments are read from LDS first, then the products run
+    // with the four accumulators interleaved.
+    bf16x8 kf[2][2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int sbk = 0; sbk < 2; ++sbk) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int krow = c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][koff(krow, ks * 32 + fq * 8)]);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf, qf[cb][ks], sacc[c][sbk][cb]);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+          kf[c][sbk][ks] = *reinterpret_cast<const bf16x8*>(&sK[buf][koff(krow, ks * 32 + fq * 8)]);
       }
+    f32x4 sacc[2][2][CB];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf[c][sbk][ks], qf[cb][ks], sacc[c][sbk][cb]);
 
-    const bool diag = kt * KT + KT - 1 > q0 || kt * KT + KT > L;
+    // Keys after a row's position (the diagonal tile) or past the sequence end
+    // (its last tile) score -inf.
+    if (kt * KT + KT - 1 > q0 || kt * KT + KT > L) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = kt * KT + c * 32 + 8 * fq + 4 * sbk + r;
+              if (key > qpos[cb] || key >= L) sacc[c][sbk][cb][r] = -INFINITY;
+            }
+    }
+    // Row maxima of the raw scores (the scale is positive, so it commutes with max).
+    float mx[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      float mx = -INFINITY;
+      mx[cb] = -INFINITY;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = sacc[c][sbk][cb][r] * scale_log2;
-            if (diag) {
-              const int key = kt * KT + c * 32 + 8 * fq + 4 * sbk + r;
-              if (key > qpos[cb] || key >= L) v = -INFINITY;
-            }
-            sacc[c][sbk][cb][r] = v;
-            mx = fmaxf(mx, v);
-          }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun[cb], mx);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2_f(mrun[cb] - mref);
-      mrun[cb] = mnew;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int sbk = 0; sbk < 2; ++sbk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sacc[c][sbk][cb][r] = exp2_f(sacc[c][sbk][cb][r] - mref);
-      lrun[cb] *= alpha;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) oacc[d][cb] *= alpha;
+          for (int r = 0; r < 4; ++r) mx[cb] = fmaxf(mx[cb], sacc[c][sbk][cb][r]);
+      mx[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 16, 64));
+      mx[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 32, 64));
+      mx[cb] *= scale_log2;
     }
-
-    // O^T += V^T . P^T  (fp16 operands)
+    // The reference maximum of a row moves only when the tile's maximum passes
+    // it by more than kLazyLog2 (then for every row of the wavefront, a uniform
+    // branch): weights stay <= 2^kLazyLog2, well inside fp16, and most tiles of
+    // a long row skip the rescale of its accumulators.
+    bool grow = false;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f16x8 pf[CB];
+    for (int cb = 0; cb < CB; ++cb) grow |= mx[cb] > mref[cb] + kLazyLog2;
+    if (__ballot(grow)) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        pf[cb] = pack_p(sacc[c][0][cb], sacc[c][1][cb]);
-        float ls = 0.f;
+        const float mnew = fmaxf(mref[cb], mx[cb]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2_f(mref[cb] - mnew);
+        mref[cb] = mnew;
+        lrun[cb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ls += sacc[c][0][cb][r] + sacc[c][1][cb][r];
-        lrun[cb] += ls;
+        for (int d = 0; d < 8; ++d) oacc[d][cb] *= alpha;
       }
+    }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const f16x8 vf = *reinterpret_cast<const f16x8*>(&sV[buf][voff(d * 16 + fr, c * 32 + fq * 8)]);
+    for (int cb = 0; cb < CB; ++cb) {
+      const float mu = (mref[cb] == -INFINITY) ? 0.f : mref[cb];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = mfma16_f16(vf, pf[cb], oacc[d][cb]);
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[c][sbk][cb][r] = exp2_f(fmaf(sacc[c][sbk][cb][r], scale_log2, -mu));
+    }
+
+    // O^T += V^T . P^T  (fp16 operands), four dim blocks at a time: hi products
+    // then lo, so no MFMA waits on the one before it
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      PSplit pf[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) pf[cb] = split_p(sacc[c][0][cb], sacc[c][1][cb], lrun[cb]);
+#pragma unroll
+      for (int dh = 0; dh < 8; dh += 4) {
+        f16x8 vf[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          vf[d] = *reinterpret_cast<const f16x8*>(&sV[buf][voff((dh + d) * 16 + fr, c * 32 + fq * 8)]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[cb].hi, oacc[dh + d][cb]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[cb].lo, oacc[dh + d][cb]);
       }
     }
 
@@ -360,13 +406,14 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restric
     for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sacc[sbk][r] = exp2_f(sacc[sbk][r] - mnew);
-    const f16x8 pf = pack_p(sacc[0], sacc[1]);
     float ls = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ls += sacc[0][r] + sacc[1][r];
+    const PSplit pf = split_p(sacc[0], sacc[1], ls);
     lrun = lrun * alpha + ls;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(vraw[d])), pf, oacc[d] * alpha);
+    for (int d = 0; d < 8; ++d) {
+      const f16x8 vf = as_f16x8(bf16x8_to_f16x8(vraw[d]));
+      oacc[d] = mfma16_f16(vf, pf.lo, mfma16_f16(vf, pf.hi, oacc[d] * alpha));
+    }
   }
   lrun += __shfl_xor(lrun, 16, 64);
   lrun += __shfl_xor(lrun, 32, 64);
@@ -603,15 +650,15 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
     for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sacc[sbk][rr] = exp2_f(sacc[sbk][rr] - mnew);
-    const f16x8 pf = pack_p(sacc[0], sacc[1]);
     float ls = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ls += sacc[0][rr] + sacc[1][rr];
+    const PSplit pf = split_p(sacc[0], sacc[1], ls);
     lrun = lrun * alpha + ls;
     const int vkey0 = c0 + fq * 8;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-      oacc[d] = mfma16_f16(as_f16x8(bf16x8_to_f16x8(mask_keys(r.v[d], vkey0, cend))), pf, oacc[d] * alpha);
+    for (int d = 0; d < 8; ++d) {
+      const f16x8 vf = as_f16x8(bf16x8_to_f16x8(mask_keys(r.v[d], vkey0, cend)));
+      oacc[d] = mfma16_f16(vf, pf.lo, mfma16_f16(vf, pf.hi, oacc[d] * alpha));
+    }
   };
   // Two register buffers, used in turn: the next run loads while one is used.
   for (int c0 = w0; c0 < cend; c0 += 64) {
@@ -779,14 +826,21 @@ int g_flash_cb = -1;  // rows-per-wavefront override (q3op_tune); -1 = automatic
 void flash_set_rows(int cb) { g_flash_cb = cb; }
 
 hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
-                         const bf16_t* kv, int layer, int n_q, int n_kv, bf16_t* o, hipStream_t s) {
+                         const bf16_t* kv, const uint16_t* vstage, int layer, int n_q, int n_kv, bf16_t* o,
+                         hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int group = n_q / n_kv;
   if (group < 1 || group > 8 || 128 % group != 0) return hipErrorInvalidValue;
-  // Rows per wavefront (16*CB).  CB = 1 keeps the kernel within 256 registers
-  // per lane, so two blocks share a CU; on gfx950 that beat the larger
-  // register tiles at every length measured (512 to 32768 keys).
-  const int CB = g_flash_cb < 0 ? 1 : g_flash_cb;
+  // Rows per wavefront (16*CB).  CB = 2 halves the LDS reads per MFMA and still
+  // fits two blocks per CU (238 registers per lane); CB = 4 (one block per CU)
+  // measured slower on gfx950.  Short prefills keep CB = 1 for more blocks.
+  int CB = g_flash_cb;
+  if (CB < 0) {
+    // 32 rows per wavefront when that still gives every CU two blocks, else 16
+    int64_t tiles2 = 0;
+    for (int b = 0; b < sb.n; ++b) tiles2 += (sb.cu[b + 1] - sb.cu[b] + 128 / group - 1) / (128 / group);
+    CB = tiles2 * n_kv >= 512 ? 2 : 1;
+  }
   const int qt = 64 * CB / group;
   TileTable tt;
   tt.tile_cu[0] = 0;
@@ -798,15 +852,19 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   if (total <= 0) return hipSuccess;
   dim3 grid(total, n_kv);
   const float scale_log2 = kLog2e / sqrtf(128.f);
+  const int64_t vh_keys = vstage_keys(T, sb.n);
   switch (CB) {
     case 4:
-      flash_prefill_kernel<4><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      flash_prefill_kernel<4><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
+                                                        scale_log2);
       break;
     case 2:
-      flash_prefill_kernel<2><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      flash_prefill_kernel<2><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
+                                                        scale_log2);
       break;
     case 1:
-      flash_prefill_kernel<1><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, layer, n_q, n_kv, qt, o, scale_log2);
+      flash_prefill_kernel<1><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
+                                                        scale_log2);
       break;
     default:
       return hipErrorInvalidValue;

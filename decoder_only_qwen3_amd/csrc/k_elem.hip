@@ -172,7 +172,8 @@ struct VtTiles {
 template <typename T>
 __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict__ qkv, SeqBatch sb, VtTiles tt,
                                                         const SeqState* __restrict__ st, T* __restrict__ kv,
-                                                        int layer, int n_q, int n_kv) {
+                                                        int layer, int n_q, int n_kv, uint16_t* __restrict__ vh,
+                                                        int64_t vh_keys) {
   __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
   const int tix = blockIdx.x, g = blockIdx.y;
   int b = 0;
@@ -211,12 +212,73 @@ __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict_
       for (int k = k0; k < n; ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
     }
   }
+  if constexpr (sizeof(T) == 2) {
+    // fp16 staging copy of the stored bf16 values for the flash kernel, the
+    // tile's keys past the sequence end zero
+    if (vh) {
+      uint16_t* dst = vh + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;
+      for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
+        const int d = e >> 3, k0 = (e & 7) * 8;
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = k0 + 2 * w < n ? tile[d][k0 + 2 * w] : 0u;
+          const uint32_t hi = k0 + 2 * w + 1 < n ? tile[d][k0 + 2 * w + 1] : 0u;
+          v[w] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + vt_off(p0 + k0, d)) = bf16x8_to_f16x8(v);
+      }
+    }
+  }
+}
+
+// fp16 staging of values already in the cache (the standalone flash entry
+// point): block (64-key tile of one sequence, kv head g).
+__global__ __launch_bounds__(256) void vstage_kernel(SeqBatch sb, VtTiles tt, const SeqState* __restrict__ st,
+                                                     const bf16_t* __restrict__ kv, int layer, int n_kv,
+                                                     uint16_t* __restrict__ vh, int64_t vh_keys) {
+  const int tix = blockIdx.x, g = blockIdx.y;
+  int b = 0;
+  {
+    int lo = 0, hi = sb.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int L = sb.cu[b + 1] - sb.cu[b];
+  const int p0 = (tix - tt.tile_cu[b]) * VT_TILE;
+  const bf16_t* vt = kv_vt(kv, st[sb.slot[b]], KvGeom{n_kv, layer}, g);
+  uint16_t* dst = vh + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;
+  for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
+    const int d = e >> 3, k0 = p0 + (e & 7) * 8;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (k0 + 8 <= L) {
+      v = ld16(vt + vt_off(k0, d));
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = k0 + 2 * w < L ? vt[vt_off(k0 + 2 * w, d)] : 0u;
+        const uint32_t hi = k0 + 2 * w + 1 < L ? vt[vt_off(k0 + 2 * w + 1, d)] : 0u;
+        v[w] = lo | (hi << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(dst + vt_off(k0, d)) = bf16x8_to_f16x8(v);
+  }
+}
+
+VtTiles vt_tiles(const SeqBatch& sb) {
+  VtTiles tt;
+  tt.tile_cu[0] = 0;
+  for (int b = 0; b < sb.n; ++b) tt.tile_cu[b + 1] = tt.tile_cu[b] + (sb.cu[b + 1] - sb.cu[b] + VT_TILE - 1) / VT_TILE;
+  return tt;
 }
 
 hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
                        void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
                        float eps, const float* cos_t, const float* sin_t, void* q_out,
-                       uint32_t* err, hipStream_t s) {
+                       uint32_t* err, hipStream_t s, uint16_t* vstage) {
   if (T <= 0) return hipSuccess;
   const int64_t units = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
   dim3 grid((unsigned)((units + 15) / 16));
@@ -228,14 +290,22 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                                                    eps, cos_t, sin_t, (float*)q_out, err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sb.decode) return e;
-  VtTiles tt;
-  tt.tile_cu[0] = 0;
-  for (int b = 0; b < sb.n; ++b) tt.tile_cu[b + 1] = tt.tile_cu[b] + (sb.cu[b + 1] - sb.cu[b] + VT_TILE - 1) / VT_TILE;
+  const VtTiles tt = vt_tiles(sb);
   dim3 vgrid((unsigned)tt.tile_cu[sb.n], n_kv);
+  const int64_t vh_keys = vstage_keys(T, sb.n);
   if (dtype == BF16)
-    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv);
+    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv, vstage, vh_keys);
   else
-    vt_append_kernel<float><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (float*)kv, layer, n_q, n_kv);
+    vt_append_kernel<float><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (float*)kv, layer, n_q, n_kv, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
+                             uint16_t* vstage, hipStream_t s) {
+  if (T <= 0 || sb.decode) return hipSuccess;
+  const VtTiles tt = vt_tiles(sb);
+  dim3 grid((unsigned)tt.tile_cu[sb.n], n_kv);
+  vstage_kernel<<<grid, 256, 0, s>>>(sb, tt, st, kv, layer, n_kv, vstage, vstage_keys(T, sb.n));
   return hipGetLastError();
 }
 

@@ -31,7 +31,11 @@ hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, c
 hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
                        void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
                        float eps, const float* cos_t, const float* sin_t, void* q_out,
-                       uint32_t* err, hipStream_t s);
+                       uint32_t* err, hipStream_t s, uint16_t* vstage = nullptr);
+// fp16 staging of a bf16 prefill call's values from the cache (vstage_keys(T, n)
+// keys per kv head); rope_append writes the same staging when given one.
+hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
+                             uint16_t* vstage, hipStream_t s);
 hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
                        uint32_t* err, hipStream_t s);
 // Reduce per-block (max, index) partials of EPI_ARGMAX into next[m], then
@@ -99,7 +103,7 @@ hipError_t gemv_f32(int epi, const float* X, int M, const float* W, int N, int K
 
 // ---------------------------------------------------------------- k_attn.hip
 hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
-                         const bf16_t* kv, int layer, int n_q, int n_kv, bf16_t* o,
+                         const bf16_t* kv, const uint16_t* vstage, int layer, int n_q, int n_kv, bf16_t* o,
                          hipStream_t s);
 int decode_attn_splits(int B, int n_kv, int64_t max_ctx);
 hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, const bf16_t* kv,

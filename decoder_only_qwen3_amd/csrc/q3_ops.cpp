@@ -281,9 +281,11 @@ q3_status q3op_rope_append(int32_t dtype, const float* d_qkv, int32_t n, const i
   return Q3_OK;
 }
 
-size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t n_q, int32_t splits) {
+size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t total_tokens, int32_t n_q,
+                                      int32_t n_kv, int32_t splits) {
   size_t b = al(n_seqs * sizeof(SeqState));
   if (kernel == Q3OP_ATTN_DECODE) b += al((size_t)n_seqs * n_q * (splits > 0 ? splits : 2048) * 130 * 4);
+  if (kernel == Q3OP_ATTN_FLASH) b += al((size_t)vstage_keys(std::max(total_tokens, 0), n_seqs) * n_kv * 128 * 2);
   return b;
 }
 
@@ -308,15 +310,18 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
     for (int b = 0; b < n; ++b) mc = std::max<int64_t>(mc, h_cap[b]);
     splits = decode_attn_splits(n, n_kv, mc);
   }
-  if (!d_ws || ws_bytes < q3op_attention_workspace_bytes(kernel, n, n_q, splits))
+  const int T = sb.cu[n];
+  if (!d_ws || ws_bytes < q3op_attention_workspace_bytes(kernel, n, T, n_q, n_kv, splits))
     return op_fail(Q3_E_ARG, "workspace too small");
   char* ws = (char*)d_ws;
   st = upload_states(n, h_base, h_cap, h_len, ws, s);
   if (st != Q3_OK) return st;
   const SeqState* sst = (const SeqState*)ws;
-  const int T = sb.cu[n];
   if (kernel == Q3OP_ATTN_FLASH) {
-    OP_TRY(flash_prefill((const bf16_t*)d_q, T, sb, sst, (const bf16_t*)d_kv, 0, n_q, n_kv, (bf16_t*)d_out, s));
+    uint16_t* vstage = (uint16_t*)(ws + al(n * sizeof(SeqState)));
+    OP_TRY(vstage_from_cache(T, sb, sst, (const bf16_t*)d_kv, 0, n_kv, vstage, s));
+    OP_TRY(flash_prefill((const bf16_t*)d_q, T, sb, sst, (const bf16_t*)d_kv, vstage, 0, n_q, n_kv,
+                         (bf16_t*)d_out, s));
   } else if (kernel == Q3OP_ATTN_DECODE) {
     float* part = (float*)(ws + al(n * sizeof(SeqState)));
     OP_TRY(decode_attn((const bf16_t*)d_q, sb, sst, (const bf16_t*)d_kv, 0, n_q, n_kv, splits, part,

@@ -52,7 +52,8 @@ struct WeightLayout {
 };
 
 struct WsLayout {
-  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, state, err, total;
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, vstage, state,
+      err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
   int amax_blocks;
 };
@@ -152,6 +153,8 @@ WsLayout ws_layout(const q3_config& c) {
   }
   W.lin_part = take(std::max<size_t>(16, part) * 4);
   W.lin_cnt = take(std::max<size_t>(H / 16 + 1, 256) * 4);
+  // fp16 values of a bf16 prefill call for the flash kernel
+  W.vstage = take(c.dtype == BF16 ? (size_t)vstage_keys(R, Q3_MAX_BATCH) * c.n_kv_heads * 128 * 2 : 16);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -287,7 +290,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
                                m->WS<float>(L.attn_part), m->WS<uint32_t>(L.attn_cnt), (bf16_t*)ob, s));
     } else {
       LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
-                         m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s));
+                         m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s,
+                         bf ? m->WS<uint16_t>(L.vstage) : nullptr));
     }
     if (!bf) {
       LAUNCH(attn_f32((const float*)qb, T, sb, m->state(), (const float*)m->kv, l, c.n_q_heads, c.n_kv_heads,
@@ -295,8 +299,8 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else if (decode) {
       // done above
     } else {
-      LAUNCH(flash_prefill((const bf16_t*)qb, T, sb, m->state(), (const bf16_t*)m->kv, l, c.n_q_heads,
-                           c.n_kv_heads, (bf16_t*)ob, s));
+      LAUNCH(flash_prefill((const bf16_t*)qb, T, sb, m->state(), (const bf16_t*)m->kv, m->WS<uint16_t>(L.vstage), l,
+                           c.n_q_heads, c.n_kv_heads, (bf16_t*)ob, s));
     }
     // Output projection + residual (Paso 5 end, Paso 7).
     if (!bf) {

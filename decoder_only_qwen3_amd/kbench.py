@@ -97,8 +97,8 @@ def attention_case(lib, name, kernel, L, B, reps, stream):
         q = _rand_bf16((B, n_q, 128))
         out = torch.empty_like(q)
         lens, decode = [L] * B, 1
-    ws = torch.zeros(max(256, lib.q3op_attention_workspace_bytes(kernel, B, n_q, 0)), dtype=torch.uint8,
-                     device="cuda:0")
+    ws_bytes = lib.q3op_attention_workspace_bytes(kernel, B, int(cu[-1]), n_q, n_kv, 0)
+    ws = torch.zeros(max(256, ws_bytes), dtype=torch.uint8, device="cuda:0")
     sh = stream.cuda_stream
     a_cu, a_b, a_c, a_l = _lib.i32_array(cu), _lib.i64_array(bases), _lib.i32_array([cap] * B), _lib.i32_array(lens)
 

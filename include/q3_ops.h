@@ -92,14 +92,16 @@ q3_status q3op_rope_append(int32_t dtype, const float* d_qkv, int32_t n_seqs, co
 
 /* Paso 5 attention over the arena above, output [T][n_q][128] in dtype.
  * kernel 0 = bf16 flash prefill (decode must be 0: query t of sequence b at
- * position t - h_cu[b], keys 0..L_b-1 of that sequence);
+ * position t - h_cu[b], keys 0..L_b-1 of that sequence; the call first stages
+ * the values as fp16 in the workspace, total_tokens = h_cu[n_seqs]);
  * kernel 1 = bf16 split-K decode (decode must be 1: query b at position
  * h_len[b], keys 0..h_len[b]); `splits` <= 0 picks the library's choice;
  * kernel 2 = float32 (either mode). */
 #define Q3OP_ATTN_FLASH 0
 #define Q3OP_ATTN_DECODE 1
 #define Q3OP_ATTN_F32 2
-size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t n_q, int32_t splits);
+size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t total_tokens, int32_t n_q,
+                                      int32_t n_kv, int32_t splits);
 q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n_seqs, const int32_t* h_cu, int32_t decode,
                          const int64_t* h_base, const int32_t* h_cap, const int32_t* h_len, const void* d_kv,
                          int32_t n_q, int32_t n_kv, int32_t splits, void* d_out, void* d_ws, size_t ws_bytes,

@@ -390,7 +390,7 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
         dkv = dev_f32(arena)
         dq = dev_f32(q)
         out = torch.zeros((q.shape[0], n_q, 128), dtype=torch.float32, device="cuda:0")
-    ws = _ws(lib.q3op_attention_workspace_bytes(kernel, n, n_q, splits))
+    ws = _ws(lib.q3op_attention_workspace_bytes(kernel, n, int(cu[-1]), n_q, n_kv, splits))
     call(lib.q3op_attention(kernel, dq.data_ptr(), n, mod.i32_array(cu), 1 if decode else 0,
                             mod.i64_array(bases), mod.i32_array(caps), mod.i32_array(prior), dkv.data_ptr(),
                             n_q, n_kv, splits, out.data_ptr(), ws.data_ptr(), ws.numel(), None))
