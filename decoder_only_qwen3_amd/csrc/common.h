@@ -84,6 +84,18 @@ Q3_DEV u32x4 bf16x8_to_f16x8(u32x4 v) {
 
 Q3_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+Q3_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier without the fence of __syncthreads(), whose wait for every
+// outstanding vector-memory operation would drain a load pipeline; the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+Q3_DEV void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Sixteen-byte accesses with the agent-scope cache policy (sc1: written through
 // to, and read back from, memory that every XCD's L2 sees), for partial results
 // that another block merges.  The four-byte agent-scope atomics carry the same

@@ -43,14 +43,26 @@ Q3_DEV float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 struct PSplit {
   f16x8 hi, lo;
 };
+// p - (float)half (the half being the low or high fp16 of `h`), in one
+// mixed-precision FMA: -half * 1 + p.
+Q3_DEV float minus_half_lo(uint32_t h, float p) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
+  return r;
+}
+Q3_DEV float minus_half_hi(uint32_t h, float p) {
+  float r;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
+  return r;
+}
 Q3_DEV PSplit split_p(const f32x4& a, const f32x4& b, float& sum) {
   const float p[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   u32x4 h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16x2 hh = __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, f16x2);
-    h[i] = __builtin_bit_cast(uint32_t, hh);
-    l[i] = pack_f16x2(p[2 * i] - (float)hh[0], p[2 * i + 1] - (float)hh[1]);
+    h[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
+    const uint32_t hi = h[i];
+    l[i] = pack_f16x2(minus_half_lo(hi, p[2 * i]), minus_half_hi(hi, p[2 * i + 1]));
     sum += p[2 * i] + p[2 * i + 1];
   }
   return PSplit{as_f16x8(h), as_f16x8(l)};
@@ -74,9 +86,16 @@ constexpr int KT = 64;          // keys per tile
 constexpr float kLazyLog2 = 8.f;  // headroom of the stale reference maximum (log2 units)
 // LDS tiles are stored unpadded with the 16-byte chunk index of each row
 // XOR-swizzled by the row (keys: 16 chunks per row, values^T: 8), so the
-// MFMA fragment reads (16 rows, one chunk) do not collide in LDS banks.
-Q3_DEV int koff(int key, int col) { return key * 128 + ((((col >> 3) ^ (key & 15)) << 3) | (col & 7)); }
-Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ (dim & 7)) << 3) | (key & 7)); }
+// MFMA fragment reads (16 rows, one chunk) do not collide in LDS banks.  The
+// key fragment's 16 rows differ in key bits 0, 1, 3 and 4 (the permuted key
+// order below), and the key swizzle takes exactly those bits.  Both choices
+// were checked with the LDS bank-conflict counter on gfx950 (zero conflict
+// cycles; swizzling keys by their low four bits instead cost one conflict
+// cycle per read).
+Q3_DEV int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
+Q3_DEV int vswz(int dim) { return dim & 7; }
+Q3_DEV int koff(int key, int col) { return key * 128 + ((((col >> 3) ^ kswz(key)) << 3) | (col & 7)); }
+Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ vswz(dim)) << 3) | (key & 7)); }
 
 struct TileTable {
   int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
@@ -84,9 +103,16 @@ struct TileTable {
 
 // Block: one kv head and one query tile of `qt` tokens of one sequence; its
 // 64*CB query rows are the group's query heads x qt tokens (row r -> head
-// r / qt, token r % qt).  4 wavefronts x 16*CB rows.  K and V^T tiles of 64
-// keys are double-buffered in LDS and shared by the 4 wavefronts; more rows
-// per wavefront means fewer LDS reads per MFMA.
+// r / qt, token r % qt).  4 wavefronts x 16*CB rows.  K tiles (bf16) and V^T
+// tiles (fp16 staging) of 64 keys are double-buffered in LDS, filled by
+// direct global-to-LDS loads (each lane fetches the global chunk that belongs
+// at its fixed LDS position under the swizzle) and shared by the 4 wavefronts.
+//
+// The loop is rotated so each iteration holds independent MFMA and VALU work:
+// iteration j runs P(j-1).V(j-1) while taking the row maxima of S(j), then
+// S(j+1) = K(j+1).Q^T while exponentiating S(j).  LDS: K(t) in sK[t & 1],
+// V(t) in sV[t & 1]; iteration j reads V(j-1) and K(j+1) and loads V(j) and
+// K(j+2) over the buffers of V(j-2) and K(j), used up in iteration j-1.
 template <int CB>
 __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
@@ -117,6 +143,9 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
 
+  // V(-1) is all zeros (the first iteration's P.V adds nothing).
+  for (int i = tid; i < 128 * KT / 8; i += 256) reinterpret_cast<u32x4*>(sV[1])[i] = u32x4{0u, 0u, 0u, 0u};
+
   // Query fragments (B operand of S^T) for this wavefront's 16-row blocks.
   bf16x8 qf[CB][4];
   int qpos[CB], qhead[CB];
@@ -139,23 +168,54 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
   const int kend = min(L, q0 + qt);
   const int ntiles = (kend + KT - 1) / KT;
 
-  // Staging assignment: K tile 64 keys x 16 chunks; V^T tile 128 dims x 8 chunks.
-  u32x4 rk[4], rv[4];
-  auto gload = [&](int kt) {
+  // Load i of wavefront w fills LDS chunks (4i + w)*64 + lane of a tile: the
+  // K chunk (key, j) holds global chunk j ^ kswz(key) of that key's row; the
+  // V^T chunk (dim, j) holds keys 8 (j ^ vswz(dim)) .. +7 of that dim.
+  int ksrc[4], vsrc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt * KT + (tid >> 4) + 16 * i;
-      rk[i] = ld16(Kc + (int64_t)key * 128 + (tid & 15) * 8);
-      const int dim = (tid >> 3) + 32 * i;
-      const int key0 = kt * KT + (tid & 7) * 8;
-      rv[i] = ld16(Vh + vt_off(key0, dim));
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int p = (4 * i + wid) * 64 + lane;
+    const int key = p >> 4, dim = p >> 3;
+    ksrc[i] = key * 128 + (((p & 15) ^ kswz(key)) << 3);
+    vsrc[i] = (int)vt_off(((p & 7) ^ vswz(dim)) << 3, dim);
+  }
+  auto issue_k = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // (non-const pointers: with a const source the host pass drops the kernel stub)
+      __builtin_amdgcn_global_load_lds((void*)(Kc + (int64_t)t * KT * 128 + ksrc[i]),
+                                       (void*)(&sK[t & 1][(4 * i + wid) * 512]), 16, 0, 0);
   };
-  auto sstore = [&](int buf) {
+  auto issue_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sK[buf][koff((tid >> 4) + 16 * i, (tid & 15) * 8)]) = rk[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][voff((tid >> 3) + 32 * i, (tid & 7) * 8)]) = rv[i];
+    for (int i = 0; i < 4; ++i)  // a 64-key tile is two 32-key value blocks: 64 * 128 elements
+      __builtin_amdgcn_global_load_lds((void*)(Vh + (int64_t)t * KT * 128 + vsrc[i]),
+                                       (void*)(&sV[t & 1][(4 * i + wid) * 512]), 16, 0, 0);
+  };
+
+  // S^T of tile t: sacc[c][sb][cb], keys t*64 + c*32 + 8*fq + 4*sb + r.
+  auto scores = [&](int t, f32x4 (&sacc)[2][2][CB]) {
+    const bf16_t* kb = sK[t & 1];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 kf[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+          kf[c][sbk] = *reinterpret_cast<const bf16x8*>(
+              &kb[koff(c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), ks * 32 + fq * 8)]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf[c][sbk], qf[cb][ks], sacc[c][sbk][cb]);
     }
   };
 
@@ -164,52 +224,62 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
   for (int d = 0; d < 8; ++d)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) oacc[d][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // O^T += V^T(t) . P^T (fp16 operands) over the keys of half c of the tile,
+  // four dim blocks at a time: hi products then lo, so no MFMA waits on the
+  // one before it.
+  auto accumulate = [&](int t, const PSplit (&pf)[2][CB], int c) {
+    const uint16_t* vb = sV[t & 1];
+#pragma unroll
+    for (int dh = 0; dh < 8; dh += 4) {
+      f16x8 vf[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        vf[d] = *reinterpret_cast<const f16x8*>(&vb[voff((dh + d) * 16 + fr, c * 32 + fq * 8)]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[c][cb].hi, oacc[dh + d][cb]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[c][cb].lo, oacc[dh + d][cb]);
+    }
+  };
+
   float mref[CB], lrun[CB];  // reference maximum (scaled, log2 units) and weight sum per row
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     mref[cb] = -INFINITY;
     lrun[cb] = 0.f;
   }
+  PSplit pf[2][CB];  // weights of the previous tile (zero before the first)
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      pf[c][cb].hi = as_f16x8(u32x4{0u, 0u, 0u, 0u});
+      pf[c][cb].lo = pf[c][cb].hi;
+    }
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+  // Prologue: K(0) then K(1); S(0) once K(0) has landed (K(1) may still fly).
+  issue_k(0);
+  if (ntiles > 1) {
+    issue_k(1);
+    wait_vm<4>();
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();  // also orders the zeroing of sV[1]
+  // Iteration j: sacc holds S(j) on entry; S(j+1) goes to snext.
+  auto step = [&](int j, f32x4 (&sacc)[2][2][CB], f32x4 (&snext)[2][2][CB]) {
+    // K(j+1) and V(j-1) (loaded during the previous iteration) have landed.
+    wait_vm<0>();
+    bare_barrier();
+    issue_v(j);
+    if (j + 2 < ntiles) issue_k(j + 2);
 
-    // S^T for the tile: sacc[c][sb][cb], keys kt*64 + c*32 + 8*fq + 4*sb + r.
-    // All sixteen key fragments are read from LDS first, then the products run
-    // with the four accumulators interleaved.
-    bf16x8 kf[2][2][4];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int sbk = 0; sbk < 2; ++sbk) {
-        const int krow = c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[c][sbk][ks] = *reinterpret_cast<const bf16x8*>(&sK[buf][koff(krow, ks * 32 + fq * 8)]);
-      }
-    f32x4 sacc[2][2][CB];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int sbk = 0; sbk < 2; ++sbk)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int sbk = 0; sbk < 2; ++sbk)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) sacc[c][sbk][cb] = mfma16(kf[c][sbk][ks], qf[cb][ks], sacc[c][sbk][cb]);
-
-    // Keys after a row's position (the diagonal tile) or past the sequence end
-    // (its last tile) score -inf.
-    if (kt * KT + KT - 1 > q0 || kt * KT + KT > L) {
+    if (j * KT + KT - 1 > q0 || j * KT + KT > L) {
+      // keys after a row's position (the diagonal tile) or past the sequence end
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -218,10 +288,13 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
           for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int key = kt * KT + c * 32 + 8 * fq + 4 * sbk + r;
+              const int key = j * KT + c * 32 + 8 * fq + 4 * sbk + r;
               if (key > qpos[cb] || key >= L) sacc[c][sbk][cb][r] = -INFINITY;
             }
     }
+    // P(j-1).V(j-1) (buffer (j - 1) & 1), the row maxima of S(j) beside it.
+    accumulate(j + 1, pf, 0);
+    accumulate(j + 1, pf, 1);
     // Row maxima of the raw scores (the scale is positive, so it commutes with max).
     float mx[CB];
 #pragma unroll
@@ -255,6 +328,10 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
         for (int d = 0; d < 8; ++d) oacc[d][cb] *= alpha;
       }
     }
+
+    // S(j+1) on the MFMA pipe while the VALU turns S(j) into split weights.
+    // (Past the last tile the product reads a stale buffer and is discarded.)
+    scores(j + 1, snext);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const float mu = (mref[cb] == -INFINITY) ? 0.f : mref[cb];
@@ -265,34 +342,26 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) sacc[c][sbk][cb][r] = exp2_f(fmaf(sacc[c][sbk][cb][r], scale_log2, -mu));
     }
-
-    // O^T += V^T . P^T  (fp16 operands), four dim blocks at a time: hi products
-    // then lo, so no MFMA waits on the one before it
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      PSplit pf[CB];
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) pf[cb] = split_p(sacc[c][0][cb], sacc[c][1][cb], lrun[cb]);
-#pragma unroll
-      for (int dh = 0; dh < 8; dh += 4) {
-        f16x8 vf[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          vf[d] = *reinterpret_cast<const f16x8*>(&sV[buf][voff((dh + d) * 16 + fr, c * 32 + fq * 8)]);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[cb].hi, oacc[dh + d][cb]);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[dh + d][cb] = mfma16_f16(vf[d], pf[cb].lo, oacc[dh + d][cb]);
-      }
-    }
-
-    if (kt + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
+      for (int cb = 0; cb < CB; ++cb) pf[c][cb] = split_p(sacc[c][0][cb], sacc[c][1][cb], lrun[cb]);
+  };
+  // Unrolled by two so the score buffers swap roles instead of being copied.
+  f32x4 sA[2][2][CB], sB[2][2][CB];
+  scores(0, sA);
+  for (int j = 0;;) {
+    step(j, sA, sB);
+    if (++j >= ntiles) break;
+    step(j, sB, sA);
+    if (++j >= ntiles) break;
   }
+
+  // The last tile's P.V.
+  wait_vm<0>();
+  bare_barrier();
+  accumulate(ntiles - 1, pf, 0);
+  accumulate(ntiles - 1, pf, 1);
 
   // Normalise and store: lane holds dims d*16 + fq*4 + r of row (cb, fr).
 #pragma unroll

@@ -257,13 +257,6 @@ constexpr int DBK = 32;
 
 Q3_DEV int dswz(int row) { return (row >> 1) & 3; }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-Q3_DEV void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int EPI, int WM, int WN, int GM, int GN, int NS>
 __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __restrict__ A, int M,
                                                                const bf16_t* __restrict__ W, int N, int K,
@@ -321,7 +314,7 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
     // flight (its fence), emptying the pipeline.  The waits above cover this
     // wavefront's slice-kt loads; the memory clobber keeps the compiler from
     // moving LDS accesses across the barrier.
-    asm volatile("s_barrier" ::: "memory");
+    bare_barrier();
     if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
     const bf16_t* sa = lds + (kt % NS) * STAGE;
     const bf16_t* sb = sa + BM * DBK;
