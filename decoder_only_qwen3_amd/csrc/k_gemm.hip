@@ -15,7 +15,8 @@
 //  - LDS pipeline (32-wide K slices, 4 slices in LDS, loaded directly from
 //    global memory into LDS): three slices in flight behind the one in use.
 // Large problems use 256x256 tiles on 16 wavefronts with the pipeline,
-// small ones 64x64 tiles on 4 wavefronts.
+// small ones 64x64 tiles on 4 wavefronts.  The products run as C^T = W . A^T
+// so that each lane writes four consecutive outputs (one 16-byte store).
 #include "kernels.h"
 
 namespace q3k {
@@ -37,50 +38,53 @@ Q3_DEV int lds_off(int row, int col) {
 
 Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
-// C layout of a 16x16 MFMA tile: lane l holds rows (l/16)*4 + r, column l%16.
-// (r0, c0): first row and column of the wavefront's (16*WM) x (16*WN) tile.
+// The products run as C^T = W . A^T (the W fragment is the MFMA's A operand),
+// so in a 16x16 tile lane l holds output row l%16 and the four consecutive
+// output columns (l/16)*4 + r: one 16-byte store per lane and tile (8 bytes
+// for the bf16 SwiGLU output).  acc[i][j] covers A rows i*16.. and W rows j*16..
+// of the wavefront's tile; (r0, c0) = its first output row and column.
 template <int EPI, int WM, int WN>
 Q3_DEV void gemm_epilogue(const f32x4 (&acc)[WM][WN], int r0, int c0, int M, int N, void* __restrict__ out,
                           int64_t ldo) {
   const int lane = threadIdx.x & 63;
-  const int rbase = r0 + (lane >> 4) * 4;
-  const int cbase = c0 + (lane & 15);
+  const int row0 = r0 + (lane & 15);
+  const int cq = (lane >> 4) * 4;
   if constexpr (EPI == EPI_SWIGLU) {
     // Packed rows: every 32 rows of W are 16 gate rows then the matching 16 up
-    // rows, so tile j=2p is gate and j=2p+1 is up for the same output column.
+    // rows, so tile j=2p is gate and j=2p+1 is up for the same output columns.
     bf16_t* o = reinterpret_cast<bf16_t*>(out);
-    const int ocol0 = c0 / 2 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < WM; ++i) {
+      const int row = row0 + i * 16;
+      if (row >= M) continue;
 #pragma unroll
-      for (int p = 0; p < WN / 2; ++p)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + i * 16 + r;
-          const int col = ocol0 + p * 16;
-          if (row < M && 2 * col < N) {
-            const float g = acc[i][2 * p][r], u = acc[i][2 * p + 1][r];
-            o[(int64_t)row * ldo + col] = f2bf(silu_f(g) * u);
-          }
-        }
+      for (int p = 0; p < WN / 2; ++p) {
+        const int col = c0 / 2 + p * 16 + cq;
+        if (2 * col >= N) continue;
+        const f32x4 g = acc[i][2 * p], u = acc[i][2 * p + 1];
+        u32x2 w;
+        w[0] = pack_bf2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+        w[1] = pack_bf2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+        *reinterpret_cast<u32x2*>(o + (int64_t)row * ldo + col) = w;
+      }
+    }
   } else {
     float* o = reinterpret_cast<float*>(out);
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < WM; ++i) {
+      const int row = row0 + i * 16;
+      if (row >= M) continue;
 #pragma unroll
-      for (int j = 0; j < WN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + i * 16 + r;
-          const int col = cbase + j * 16;
-          if (row < M && col < N) {
-            float* p = o + (int64_t)row * ldo + col;
-            if constexpr (EPI == EPI_RESADD)
-              *p += acc[i][j][r];
-            else
-              *p = acc[i][j][r];
-          }
-        }
+      for (int j = 0; j < WN; ++j) {
+        const int col = c0 + j * 16 + cq;
+        if (col >= N) continue;
+        f32x4* p = reinterpret_cast<f32x4*>(o + (int64_t)row * ldo + col);
+        if constexpr (EPI == EPI_RESADD)
+          *p = *p + acc[i][j];
+        else
+          *p = acc[i][j];
+      }
+    }
   }
 }
 
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_bf16_kernel(const bf16_t* _
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(bw[j], af[i], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
@@ -257,7 +261,25 @@ constexpr int DBK = 32;
 
 Q3_DEV int dswz(int row) { return (row >> 1) & 3; }
 
-template <int EPI, int WM, int WN, int GM, int GN, int NS>
+// Blocks are dealt to the eight XCDs round robin (block b runs on XCD b % 8),
+// each XCD with an L2 of its own.  Tile t of the TM x TN output grid goes to
+// the block that makes every XCD work through one contiguous run of tiles,
+// taken in groups of kGroupM tile rows with the tile columns outer, so the
+// blocks an XCD runs together share A and W tiles in its L2 instead of every
+// XCD fetching every A tile.
+constexpr int kGroupM = 4;
+Q3_DEV void xcd_tile(int TM, int TN, int& tm, int& tn) {
+  const int T = TM * TN, b = blockIdx.x;
+  const int x = b & 7, slot = b >> 3;
+  const int per = T >> 3, extra = T & 7;  // XCD x runs per + (x < extra) tiles
+  const int t = x * per + min(x, extra) + slot;
+  const int g = t / (kGroupM * TN), r = t - g * (kGroupM * TN);
+  const int rows = min(kGroupM, TM - g * kGroupM);
+  tm = g * kGroupM + r % rows;
+  tn = r / rows;
+}
+
+template <int EPI, int WM, int WN, int GM, int GN, int NS, bool DB>
 __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __restrict__ A, int M,
                                                                const bf16_t* __restrict__ W, int N, int K,
                                                                void* __restrict__ out, int64_t ldo) {
@@ -270,7 +292,9 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
   __shared__ __attribute__((aligned(16))) bf16_t lds[NS * STAGE];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / GN, wn = wid % GN;
-  const int bn0 = blockIdx.x * BN, bm0 = blockIdx.y * BM;
+  int tm, tn;
+  xcd_tile((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int bn0 = tn * BN, bm0 = tm * BM;
 
   // This lane's source pointer and its wavefront's LDS offset per load group.
   const bf16_t* src[LPW];
@@ -306,19 +330,9 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st, st);
   const int fr = lane & 15, fq = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt is complete once at most the later slices' loads are pending
-    if (kt + NS - 2 < nk) wait_vm<(NS - 2) * LPW>();
-    else wait_vm<0>();
-    // A bare barrier: __syncthreads() would also wait for every load still in
-    // flight (its fence), emptying the pipeline.  The waits above cover this
-    // wavefront's slice-kt loads; the memory clobber keeps the compiler from
-    // moving LDS accesses across the barrier.
-    bare_barrier();
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+  auto read_frags = [&](int kt, bf16x8 (&af)[WM], bf16x8 (&bw)[WN]) {
     const bf16_t* sa = lds + (kt % NS) * STAGE;
     const bf16_t* sb = sa + BM * DBK;
-    bf16x8 af[WM], bw[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       const int row = wm * 16 * WM + i * 16 + fr;
@@ -329,30 +343,73 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
       const int row = wn * 16 * WN + j * 16 + fr;
       bw[j] = *reinterpret_cast<const bf16x8*>(sb + row * DBK + ((fq ^ dswz(row)) << 3));
     }
+  };
+  if constexpr (!DB) {
+    for (int kt = 0; kt < nk; ++kt) {
+      // slice kt is complete once at most the later slices' loads are pending
+      if (kt + NS - 2 < nk) wait_vm<(NS - 2) * LPW>();
+      else wait_vm<0>();
+      bare_barrier();
+      if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+      bf16x8 af[WM], bw[WN];
+      read_frags(kt, af, bw);
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(af[i], bw[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(bw[j], af[i], acc[i][j]);
+    }
+  } else {
+    // Slice 0 complete once at most slices 1 .. NS-2 are pending.
+    if (NS - 2 < nk) wait_vm<(NS - 2) * LPW>();
+    else wait_vm<0>();
+    bare_barrier();
+    // Step kt: the MFMAs of slice kt run on fragments read during step kt-1,
+    // while the fragments of slice kt+1 are read.  Before the reads, slice kt+1
+    // must be complete (at most slices kt+2 .. kt+NS-2 pending) and every
+    // wavefront past step kt-1, so the load of slice kt+NS-1 may reuse the
+    // buffer of slice kt-1.  (A bare barrier: __syncthreads() would also wait
+    // for every load in flight, emptying the pipeline.)
+    auto step = [&](int kt, const bf16x8 (&af)[WM], const bf16x8 (&bw)[WN], bf16x8 (&an)[WM], bf16x8 (&bn)[WN]) {
+      if (kt + 1 < nk) {
+        if (kt + NS - 2 < nk) wait_vm<(NS - 3) * LPW>();
+        else wait_vm<0>();
+        bare_barrier();
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+        read_frags(kt + 1, an, bn);
+      }
+  #pragma unroll
+      for (int i = 0; i < WM; ++i)
+  #pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma16(bw[j], af[i], acc[i][j]);
+    };
+    bf16x8 a0[WM], b0[WN], a1[WM], b1[WN];
+    read_frags(0, a0, b0);
+    for (int kt = 0;;) {  // unrolled by two so the fragment buffers swap roles
+      step(kt, a0, b0, a1, b1);
+      if (++kt >= nk) break;
+      step(kt, a1, b1, a0, b0);
+      if (++kt >= nk) break;
+    }
   }
   gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
 }
 
-template <int WM, int WN, int GM, int GN, int NS>
+template <int WM, int WN, int GM, int GN, int NS, bool DB>
 hipError_t gemm_dma_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out, int64_t ldo,
                            hipStream_t s) {
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN, NT = 64 * GM * GN;
   if (K % DBK != 0) return hipErrorInvalidValue;
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM)));
   switch (epi) {
     case EPI_STORE:
     case EPI_ARGMAX:
-      gemm_dma_kernel<EPI_STORE, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_STORE, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     case EPI_RESADD:
-      gemm_dma_kernel<EPI_RESADD, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_RESADD, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     case EPI_SWIGLU:
-      gemm_dma_kernel<EPI_SWIGLU, WM, WN, GM, GN, NS><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_SWIGLU, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
       break;
     default:
       return hipErrorInvalidValue;
@@ -387,6 +444,8 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
   if (M <= 0) return hipSuccess;
   if (K % BK != 0 || N % 16 != 0) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && N % 64 != 0) return hipErrorInvalidValue;
+  // the epilogue writes four consecutive outputs per lane (16 / 8 bytes)
+  if (ldo % 4 != 0 || reinterpret_cast<uintptr_t>(out) % (epi == EPI_SWIGLU ? 8 : 16) != 0) return hipErrorInvalidValue;
   if (g_gemm_cfg < 0 && split_part && split_cnt) {
     const int sp = gemm_splits(epi, M, N, K);
     if (sp > 1) return gemm_launch<2, 2, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s, split_part, split_cnt, sp);
@@ -395,9 +454,10 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
   if (cfg < 0) {
     // The largest tile whose grid still gives each of the 256 CUs a block:
     // 256 x 256 (4-slice LDS pipeline, 16 wavefronts), else 128 x 128, else
-    // 64 x 64.  Measured on MI355X at M = 32768: 700-900 TFLOP/s for the
-    // q/k/v, gate/up and down shapes with the pipeline, 3-5 % above the
-    // register-prefetched 256 x 256 kernel.
+    // 64 x 64.  Measured on MI355X at M = 32768: 790, 970 and 950 TFLOP/s for
+    // the q/k/v, gate/up and down shapes with the pipeline; the other
+    // configurations (8-wavefront tiles, two blocks per CU, two LDS slices,
+    // fragment double-buffering) measured 5-25 % below it.
     const int64_t g256 = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
     const int64_t g128 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
     cfg = g256 >= 256 ? 7 : (g128 >= 256 ? 1 : 0);
@@ -410,8 +470,11 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
     case 4: return gemm_launch<4, 8, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 128 x 256, 4 waves
     case 5: return gemm_launch<8, 4, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 128, 4 waves
     case 6: return gemm_launch<4, 4, 4, 4, 1>(epi, A, M, W, N, K, out, ldo, s);   // 256 x 256, 16 waves
-    case 7: return gemm_dma_launch<4, 4, 4, 4, 4>(epi, A, M, W, N, K, out, ldo, s);  // 256 x 256, 4-slice pipeline
-    case 8: return gemm_dma_launch<4, 4, 2, 2, 4>(epi, A, M, W, N, K, out, ldo, s);  // 128 x 128, 4-slice pipeline
+    case 7: return gemm_dma_launch<4, 4, 4, 4, 4, false>(epi, A, M, W, N, K, out, ldo, s);  // 256 x 256, 4-slice pipeline
+    case 8: return gemm_dma_launch<4, 4, 2, 2, 4, true>(epi, A, M, W, N, K, out, ldo, s);  // 128 x 128, 4-slice pipeline
+    case 9: return gemm_dma_launch<4, 4, 4, 2, 3, false>(epi, A, M, W, N, K, out, ldo, s); // 256 x 128, 3 slices, 2 blocks/CU
+    case 10: return gemm_dma_launch<4, 4, 2, 4, 3, false>(epi, A, M, W, N, K, out, ldo, s); // 128 x 256, 3 slices, 2 blocks/CU
+    case 11: return gemm_dma_launch<4, 4, 4, 4, 2, false>(epi, A, M, W, N, K, out, ldo, s); // 256 x 256, 2 slices
     default: return hipErrorInvalidValue;
   }
 }

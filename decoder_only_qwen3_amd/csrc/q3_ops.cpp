@@ -383,7 +383,7 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h
 
 q3_status q3op_tune(int32_t key, int32_t value) {
   if (key == Q3OP_TUNE_GEMM_TILES) {
-    if (value < -1 || value > 8) return op_fail(Q3_E_ARG, "tile configuration out of range");
+    if (value < -1 || value > 11) return op_fail(Q3_E_ARG, "tile configuration out of range");
     gemm_set_config(value);
     return Q3_OK;
   }

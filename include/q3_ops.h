@@ -43,6 +43,7 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  *     on ties).  With kernel 1 or 4 and d_next == NULL only the logits and
  *     the kernel's per-block (max, index) partials are produced (one launch).
  * kernel 0 = bf16 MFMA tiled GEMM (prefill; epi 0-2; any M; K % 64 == 0;
+ * ldo % 4 == 0 and d_out 16-byte aligned (8 for SwiGLU);
  * the residual epilogue splits K over up to four blocks when the output has
  * fewer than 256 tiles of 64 x 64, merging the slices in a fixed order, and
  * then needs q3op_linear_workspace_bytes of workspace, else Q3_E_ARG);
@@ -122,7 +123,7 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
 /* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
  * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,
- *   0..8 = fixed tile shapes (listed in k_gemm.hip).
+ *   0..11 = fixed tile shapes (listed in k_gemm.hip).
  * Q3OP_TUNE_FLASH_ROWS: prefill attention query rows per wavefront / 16,
  *   -1 = automatic, or 1, 2, 4.
  * Q3OP_TUNE_ROWGEMV: single-row GEMV shape, -1 = automatic, else

@@ -137,7 +137,7 @@ def test_gemm_split_k_residual(M, N, K):
     assert np.array_equal(got1, got2)
 
 
-@pytest.mark.parametrize("cfg", list(range(9)))
+@pytest.mark.parametrize("cfg", list(range(12)))
 def test_gemm_tile_configurations(cfg):
     """Every prefill GEMM tile shape, with ragged row and column tails."""
     _, lib = ops()
@@ -163,7 +163,7 @@ def test_gemm_tile_configurations(cfg):
 
 def test_tune_rejects_bad_values():
     _, lib = ops()
-    assert lib.q3op_tune(1, 9) != 0
+    assert lib.q3op_tune(1, 12) != 0
     assert lib.q3op_tune(2, 3) != 0
     assert lib.q3op_tune(3, 3 + 256) != 0
     assert lib.q3op_tune(3, 4 + 5 * 256) != 0
