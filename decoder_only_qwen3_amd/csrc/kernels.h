@@ -114,7 +114,8 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
 // (sequence, kv head) at most (fused_attn_smax); partials need
 // B * n_q * smax * 130 floats and `counters` B * n_kv zeroed words (left
 // zeroed by the kernel).
-int fused_attn_smax(int B, int n_kv, int64_t max_ctx);
+// ragged: the batch's longest context is at least twice its shortest.
+int fused_attn_smax(int B, int n_kv, int64_t max_cap, bool ragged);
 int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx);  // ignoring the benchmark cap: for sizing
 void decode_attn_set_split_cap(int cap);  // -1 = no cap (benchmarks only)
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,

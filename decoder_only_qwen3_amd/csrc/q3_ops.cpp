@@ -350,12 +350,14 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h
   if (!d_qkv || !d_kv || !d_qn || !d_kn || !d_out || !h_base || !h_cap || !h_len || max_pos <= 0)
     return op_fail(Q3_E_ARG, "bad argument");
   if (n_kv <= 0 || n_q % n_kv != 0 || n_q / n_kv > 8) return op_fail(Q3_E_UNSUPPORTED, "head grouping");
-  int64_t mc = 1;
+  int64_t mc = 1, lmax = 1, lmin = INT64_MAX;
   for (int b = 0; b < n; ++b) {
     if (h_len[b] + 1 > h_cap[b] || h_len[b] + 1 > max_pos) return op_fail(Q3_E_CAPACITY, "position beyond capacity");
     mc = std::max<int64_t>(mc, h_cap[b]);
+    lmax = std::max<int64_t>(lmax, h_len[b] + 1);
+    lmin = std::min<int64_t>(lmin, h_len[b] + 1);
   }
-  if (smax <= 0) smax = fused_attn_smax(n, n_kv, mc);
+  if (smax <= 0) smax = fused_attn_smax(n, n_kv, mc, lmax >= 2 * lmin);
   if (smax > 64) return op_fail(Q3_E_ARG, "smax must be <= 64");
   if (!d_ws || ws_bytes < q3op_decode_attn_fused_workspace_bytes(n, n_q, smax, max_pos))
     return op_fail(Q3_E_ARG, "workspace too small");

@@ -253,10 +253,16 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   const bool bf = c.dtype == Q3_BF16;
   int smax = 1;
   if (decode && bf) {
-    int64_t maxcap = 1;
-    for (int b = 0; b < sb.n; ++b) maxcap = std::max(maxcap, m->slots[sb.slot[b]].cap);
-    maxcap = std::min<int64_t>(maxcap, c.max_positions);
-    smax = fused_attn_smax(sb.n, c.n_kv_heads, maxcap);
+    // (the contexts at this call; a recorded graph keeps the split count it
+    // was recorded with, which only matters for speed)
+    int64_t maxcap = 1, maxctx = 1, minctx = INT64_MAX;
+    for (int b = 0; b < sb.n; ++b) {
+      const auto& hs = m->slots[sb.slot[b]];
+      maxcap = std::max<int64_t>(maxcap, std::min<int64_t>(hs.cap, c.max_positions));
+      maxctx = std::max<int64_t>(maxctx, hs.len + 1);
+      minctx = std::min<int64_t>(minctx, hs.len + 1);
+    }
+    smax = fused_attn_smax(sb.n, c.n_kv_heads, maxcap, maxctx >= 2 * minctx);
   }
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.

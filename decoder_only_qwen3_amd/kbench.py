@@ -115,6 +115,44 @@ def attention_case(lib, name, kernel, L, B, reps, stream):
             "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
 
 
+def fused_attn_case(lib, name, lens, reps, stream, smax):
+    """Fused decode attention (QK-Norm, RoPE, append, split attention) over
+    sequences with contexts `lens` (+1 new key each); bytes = cache read."""
+    n_q, n_kv = 16, 8
+    B = len(lens)
+    caps = [(L + 1 + 63) // 64 * 64 for L in lens]
+    regions = [2 * n_kv * c * 128 for c in caps]
+    bases = [0]
+    for r in regions[:-1]:
+        bases.append(bases[-1] + r)
+    kv = _rand_bf16((sum(regions),))
+    qkv = torch.randn((B, (n_q + 2 * n_kv) * 128), dtype=torch.float32, device="cuda:0")
+    qn = torch.ones(128, dtype=torch.float32, device="cuda:0")
+    out = torch.empty((B, n_q, 128), dtype=torch.int16, device="cuda:0")
+    max_pos = max(caps)
+    ws_bytes = lib.q3op_decode_attn_fused_workspace_bytes(B, n_q, smax, max_pos)
+    ws = torch.zeros(max(256, ws_bytes), dtype=torch.uint8, device="cuda:0")
+    a_b, a_c, a_l = _lib.i64_array(bases), _lib.i32_array(caps), _lib.i32_array(lens)
+
+    def fn():
+        _lib.check(lib.q3op_decode_attn_fused(qkv.data_ptr(), B, a_b, a_c, a_l, kv.data_ptr(), n_q, n_kv,
+                                              qn.data_ptr(), qn.data_ptr(), 1e-6, 1e6, max_pos, smax,
+                                              out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream))
+    us = _time(fn, reps, stream)  # includes the op's host-side table upload; use a kernel trace for the kernel
+    byts = sum(L + 1 for L in lens) * n_kv * 128 * 2 * 2
+    return {"kernel": name, "B": B, "keys": sum(L + 1 for L in lens), "smax": smax, "us_call": round(us, 2),
+            "bytes": byts}
+
+
+class ARGS:  # command-line settings the cases read
+    attn_smax = 0
+
+
+def _ragged(n, lo, hi, seed):
+    g = torch.Generator().manual_seed(seed)
+    return [int(v) for v in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
 CASES = {
     # batch-1 decode projections as the decode step runs them, weights cycled
     # through 32 copies (beyond the GPU's last-level cache)
@@ -146,6 +184,12 @@ CASES = {
     "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
     "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),
     "decode_attn_b64_8k": lambda lib, r, s: attention_case(lib, "decode_attn_b64_8k", 1, 8191, 64, r, s),
+    # fused decode attention at batched shapes; --attn-smax sets the split count
+    "fused_b64_ragged": lambda lib, r, s: fused_attn_case(lib, "fused_b64_ragged", _ragged(64, 128, 8192, 7), r, s,
+                                                          ARGS.attn_smax),
+    "fused_b64_uniform": lambda lib, r, s: fused_attn_case(lib, "fused_b64_uniform", [4160] * 64, r, s,
+                                                           ARGS.attn_smax),
+    "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax),
 }
 
 
@@ -156,7 +200,9 @@ def main():
     ap.add_argument("--gemm-tiles", type=int, default=-1, help="prefill GEMM tile configuration (-1 automatic)")
     ap.add_argument("--flash-rows", type=int, default=-1, help="prefill attention rows per wavefront / 16")
     ap.add_argument("--row-plan", type=int, default=-1, help="single-row GEMV: rows + 256 * wavefronts per block")
+    ap.add_argument("--attn-smax", type=int, default=0, help="fused decode attention splits (0 = library choice)")
     args = ap.parse_args()
+    ARGS.attn_smax = args.attn_smax
     lib = _lib.load()
     _lib.check(lib.q3op_tune(1, args.gemm_tiles))
     _lib.check(lib.q3op_tune(2, args.flash_rows))
