@@ -274,6 +274,28 @@ def test_kv_cache_decode_equals_full_recompute(contract):
     np.testing.assert_allclose(forced[0], first, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("contract", [False, True])
+def test_chunked_prefill_equals_single_prefill(contract):
+    """A prompt fed in chunks (each chunk at the positions after the cached
+    ones, attending to them) gives the rows of one call over the whole prompt,
+    and those rows match the scalar brute force on the concatenation."""
+    d, w = _tiny_model(dtype="bf16" if contract else "f32")
+    if contract:
+        w = {k: q3synth.round_to_bf16(v) for k, v in w.items()}
+    m = OracleModel(d, w, contract=contract)
+    ids = [10, 20, 30, 40, 50, 60, 70, 80, 90, 5, 6]
+    whole = m.forward(ids, m.new_cache(len(ids)), logit_rows=range(len(ids)))
+    cache = m.new_cache(len(ids))
+    parts = []
+    for a, b in [(0, 4), (4, 5), (5, 9), (9, 11)]:
+        parts.append(m.forward(ids[a:b], cache, logit_rows=range(b - a)))
+        assert cache.length == b
+    np.testing.assert_allclose(np.concatenate(parts), whole, rtol=1e-12, atol=1e-14)
+    if not contract:
+        ref = np.array(scalar_forward_all(d, w, ids))
+        np.testing.assert_allclose(np.concatenate(parts), ref, rtol=1e-11, atol=1e-13)
+
+
 def test_prefix_logits_unchanged_by_later_tokens():
     d, w = _tiny_model()
     m = OracleModel(d, w)
