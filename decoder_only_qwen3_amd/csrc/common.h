@@ -112,13 +112,16 @@ Q3_DEV f32x4 ld4_agent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
 }
 
 // Sequences of one call.  Prefill: token t of the call belongs to sequence b
-// with cu[b] <= t < cu[b+1] and sits at position t - cu[b].  Decode: token b
-// is the single new token of sequence b, at position = that slot's length.
+// with cu[b] <= t < cu[b+1] and sits at position prior[b] + t - cu[b], where
+// prior[b] tokens of that sequence are already cached (0 for a fresh prompt;
+// a continuation attends to them too).  Decode: token b is the single new
+// token of sequence b, at position = that slot's length.
 struct SeqBatch {
   int32_t n;
   int32_t decode;
   int32_t slot[Q3_MAX_BATCH];
   int32_t cu[Q3_MAX_BATCH + 1];
+  int32_t prior[Q3_MAX_BATCH];
 };
 
 // Per-slot KV placement and length, resident on the device.
@@ -150,12 +153,16 @@ Q3_DEV T* kv_vt(T* arena, const SeqState& s, KvGeom g, int head) {
 }
 
 // fp16 staging of a prefill call's values (the P.V operand of the flash
-// kernel): per kv head, the keys of sequence b from key vstage_start(sb, b)
-// on (a multiple of 64, keys padded to whole 64-key tiles with zeros), in the
-// value layout above.  vstage_keys(T, n) keys per head cover any call of T
-// tokens in n sequences.
-Q3_DEV int vstage_start(const SeqBatch& sb, int b) { return ((sb.cu[b] + 64 * b) >> 6) << 6; }
-inline int64_t vstage_keys(int64_t T, int n) { return (T + 64 * (int64_t)n + 127) / 64 * 64; }
+// kernel): per kv head, all keys 0 .. prior + L - 1 of sequence b from key
+// vstage_start(sb, b) on (whole 64-key tiles, the tail zero), in the value
+// layout above; vstage_keys(sb) keys per head.  Host side: the kernels get
+// the starts in their tile tables.
+inline int vstage_start(const SeqBatch& sb, int b) {
+  int s = 0;
+  for (int i = 0; i < b; ++i) s += ((sb.prior[i] + sb.cu[i + 1] - sb.cu[i] + 63) >> 6) << 6;
+  return s;
+}
+inline int64_t vstage_keys(const SeqBatch& sb) { return (int64_t)vstage_start(sb, sb.n) + 64; }
 
 Q3_DEV int seq_of_token(const SeqBatch& sb, int t) {
   if (sb.decode) return t;

@@ -99,11 +99,13 @@ Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ vswz(dim))
 
 struct TileTable {
   int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
+  int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
 };
 
 // Block: one kv head and one query tile of `qt` tokens of one sequence; its
 // 64*CB query rows are the group's query heads x qt tokens (row r -> head
-// r / qt, token r % qt).  4 wavefronts x 16*CB rows.  K tiles (bf16) and V^T
+// r / qt, token r % qt).  Token i of the sequence's call sits at position
+// prior + i and sees keys 0 .. prior + i (the prior ones already cached).  4 wavefronts x 16*CB rows.  K tiles (bf16) and V^T
 // tiles (fp16 staging) of 64 keys are double-buffered in LDS, filled by
 // direct global-to-LDS loads (each lane fetches the global chunk that belongs
 // at its fixed LDS position under the swizzle) and shared by the 4 wavefronts.
@@ -133,12 +135,12 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
     }
     b = lo;
   }
-  const int L = sb.cu[b + 1] - sb.cu[b];
+  const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
   const int q0 = (tile - tt.tile_cu[b]) * qt;
   const SeqState s = st[sb.slot[b]];
   const KvGeom geo{n_kv, layer};
   const bf16_t* Kc = kv_k(kv, s, geo, g);
-  const uint16_t* Vh = vstage + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;  // fp16, zero-padded
+  const uint16_t* Vh = vstage + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;  // fp16, zero-padded
   const int group = n_q / n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
     }
   }
 
-  const int kend = min(L, q0 + qt);
+  const int kend = P + min(L, q0 + qt);  // keys of the tile's last row, + 1
   const int ntiles = (kend + KT - 1) / KT;
 
   // Load i of wavefront w fills LDS chunks (4i + w)*64 + lane of a tile: the
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
     issue_v(j);
     if (j + 2 < ntiles) issue_k(j + 2);
 
-    if (j * KT + KT - 1 > q0 || j * KT + KT > L) {
+    if (j * KT + KT - 1 > P + q0 || j * KT + KT > P + L) {
       // keys after a row's position (the diagonal tile) or past the sequence end
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int key = j * KT + c * 32 + 8 * fq + 4 * sbk + r;
-              if (key > qpos[cb] || key >= L) sacc[c][sbk][cb][r] = -INFINITY;
+              if (key > P + qpos[cb] || key >= P + L) sacc[c][sbk][cb][r] = -INFINITY;
             }
     }
     // P(j-1).V(j-1) (buffer (j - 1) & 1), the row maxima of S(j) beside it.
@@ -857,7 +859,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
   const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int b = seq_of_token(sb, t);
   const SeqState s = st[sb.slot[b]];
-  const int pos = sb.decode ? s.len : t - sb.cu[b];
+  const int pos = sb.decode ? s.len : sb.prior[b] + t - sb.cu[b];
   const int ctx = min(pos + 1, F32_MAX_CTX);
   const int g = h / (n_q / n_kv);
   const KvGeom geo{n_kv, layer};
@@ -921,12 +923,13 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   for (int b = 0; b < sb.n; ++b) {
     const int L = sb.cu[b + 1] - sb.cu[b];
     tt.tile_cu[b + 1] = tt.tile_cu[b] + (L + qt - 1) / qt;
+    tt.vstart[b] = vstage_start(sb, b);
   }
   const int total = tt.tile_cu[sb.n];
   if (total <= 0) return hipSuccess;
   dim3 grid(total, n_kv);
   const float scale_log2 = kLog2e / sqrtf(128.f);
-  const int64_t vh_keys = vstage_keys(T, sb.n);
+  const int64_t vh_keys = vstage_keys(sb);
   switch (CB) {
     case 4:
       flash_prefill_kernel<4><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,

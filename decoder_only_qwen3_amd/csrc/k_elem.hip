@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
   const int t = (int)(gu / units), u = (int)(gu - (int64_t)t * units);
   const int b = seq_of_token(sb, t);
   const SeqState s = st[sb.slot[b]];
-  const int pos = sb.decode ? s.len : t - sb.cu[b];
+  const int pos = sb.decode ? s.len : sb.prior[b] + t - sb.cu[b];
   if (pos < 0 || pos >= s.cap) {  // host validation makes this unreachable
     if (j == 0) atomicOr(err, 4u);
     return;
@@ -157,17 +157,28 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
   }
 }
 
-// Prefill values: block (64-token tile of one sequence, kv head g).  The
-// tile's 64 x 128 values are read as rows, transposed through LDS and
-// written as 16-byte runs of consecutive positions into the cache's value
-// blocks ([128 dims][32 keys] per 32 positions), so both sides move whole
-// cache lines.  Prefill positions start at 0,
-// so a tile starts at a multiple of 64 within its sequence.
+// Prefill values: block (64-position tile of one sequence, kv head g).  Tiles
+// are aligned to positions (tile i covers positions 64i .. 64i + 63), so a
+// continuation's first and last tiles may be partial.  The tile's values are
+// read as rows, transposed through LDS and written as 16-byte runs of
+// consecutive positions into the cache's value blocks ([128 dims][32 keys]
+// per 32 positions), so both sides move whole cache lines.
 constexpr int VT_TILE = 64;
 
 struct VtTiles {
-  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of 64-token tiles per sequence
+  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of tiles per sequence
+  int32_t first[Q3_MAX_BATCH];        // position tile index of each sequence's first tile
+  int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
 };
+
+Q3_DEV int vt_seq(const VtTiles& tt, int n, int tix) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict__ qkv, SeqBatch sb, VtTiles tt,
@@ -176,23 +187,16 @@ __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict_
                                                         int64_t vh_keys) {
   __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
   const int tix = blockIdx.x, g = blockIdx.y;
-  int b = 0;
-  {
-    int lo = 0, hi = sb.n - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
-  const int L = sb.cu[b + 1] - sb.cu[b];
-  const int p0 = (tix - tt.tile_cu[b]) * VT_TILE;
-  const int n = min(VT_TILE, L - p0);
+  const int b = vt_seq(tt, sb.n, tix);
+  const int P = sb.prior[b], L = sb.cu[b + 1] - sb.cu[b];
+  const int p0 = (tt.first[b] + tix - tt.tile_cu[b]) * VT_TILE;  // first position of the tile
+  // new positions in the tile: p0 + lo .. p0 + n - 1
+  const int lo = max(P - p0, 0), n = min(VT_TILE, P + L - p0);
   const int units = n_q + 2 * n_kv;
-  const float* src = qkv + (int64_t)(sb.cu[b] + p0) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
+  const float* src = qkv + (int64_t)(sb.cu[b] + p0 - P) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
   // read: thread -> (token r, 4 dims); 256 threads cover 8 tokens per pass
   const int c4 = (threadIdx.x & 31) * 4, r0 = threadIdx.x >> 5;
-  for (int r = r0; r < n; r += 8) {
+  for (int r = lo + r0; r < n; r += 8) {
     const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)r * units * Q3_HEAD_DIM + c4);
     st_f<T>(&tile[c4 + 0][r], v.x);
     st_f<T>(&tile[c4 + 1][r], v.y);
@@ -206,17 +210,18 @@ __global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict_
   constexpr int RUN = 16 / sizeof(T), RUNS = VT_TILE / RUN;
   for (int e = threadIdx.x; e < Q3_HEAD_DIM * RUNS; e += 256) {
     const int d = e / RUNS, k0 = (e % RUNS) * RUN;
-    if (k0 + RUN <= n) {  // a run never crosses a 32-key block (p0 is a multiple of 64)
+    if (k0 >= lo && k0 + RUN <= n) {  // a run never crosses a 32-key block (p0 is a multiple of 64)
       *reinterpret_cast<u32x4*>(vt + vt_off(p0 + k0, d)) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
     } else {
-      for (int k = k0; k < n; ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
+      for (int k = max(k0, lo); k < min(k0 + RUN, n); ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
     }
   }
   if constexpr (sizeof(T) == 2) {
     // fp16 staging copy of the stored bf16 values for the flash kernel, the
-    // tile's keys past the sequence end zero
+    // tile's keys past the sequence end zero (only for calls without cached
+    // tokens: then the tile holds every key of its positions)
     if (vh) {
-      uint16_t* dst = vh + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;
+      uint16_t* dst = vh + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;
       for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
         const int d = e >> 3, k0 = (e & 7) * 8;
         u32x4 v;
@@ -238,19 +243,11 @@ __global__ __launch_bounds__(256) void vstage_kernel(SeqBatch sb, VtTiles tt, co
                                                      const bf16_t* __restrict__ kv, int layer, int n_kv,
                                                      uint16_t* __restrict__ vh, int64_t vh_keys) {
   const int tix = blockIdx.x, g = blockIdx.y;
-  int b = 0;
-  {
-    int lo = 0, hi = sb.n - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
-  const int L = sb.cu[b + 1] - sb.cu[b];
-  const int p0 = (tix - tt.tile_cu[b]) * VT_TILE;
+  const int b = vt_seq(tt, sb.n, tix);
+  const int L = sb.prior[b] + sb.cu[b + 1] - sb.cu[b];  // every key of the sequence after the call
+  const int p0 = (tt.first[b] + tix - tt.tile_cu[b]) * VT_TILE;
   const bf16_t* vt = kv_vt(kv, st[sb.slot[b]], KvGeom{n_kv, layer}, g);
-  uint16_t* dst = vh + ((int64_t)g * vh_keys + vstage_start(sb, b)) * Q3_HEAD_DIM;
+  uint16_t* dst = vh + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;
   for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
     const int d = e >> 3, k0 = p0 + (e & 7) * 8;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -268,11 +265,25 @@ __global__ __launch_bounds__(256) void vstage_kernel(SeqBatch sb, VtTiles tt, co
   }
 }
 
-VtTiles vt_tiles(const SeqBatch& sb) {
+// Tiles of each sequence's new positions (all = false) or of all its
+// positions 0 .. prior + L - 1 (all = true).
+VtTiles vt_tiles(const SeqBatch& sb, bool all) {
   VtTiles tt;
   tt.tile_cu[0] = 0;
-  for (int b = 0; b < sb.n; ++b) tt.tile_cu[b + 1] = tt.tile_cu[b] + (sb.cu[b + 1] - sb.cu[b] + VT_TILE - 1) / VT_TILE;
+  for (int b = 0; b < sb.n; ++b) {
+    const int P = sb.prior[b], end = P + sb.cu[b + 1] - sb.cu[b];
+    tt.first[b] = all ? 0 : P / VT_TILE;
+    tt.vstart[b] = vstage_start(sb, b);
+    tt.tile_cu[b + 1] = tt.tile_cu[b] + (end + VT_TILE - 1) / VT_TILE - tt.first[b];
+  }
   return tt;
+}
+
+bool has_prior(const SeqBatch& sb) {
+  if (sb.decode) return false;
+  for (int b = 0; b < sb.n; ++b)
+    if (sb.prior[b] != 0) return true;
+  return false;
 }
 
 hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, SeqState* st,
@@ -290,22 +301,28 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                                                    eps, cos_t, sin_t, (float*)q_out, err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sb.decode) return e;
-  const VtTiles tt = vt_tiles(sb);
+  const VtTiles tt = vt_tiles(sb, false);
   dim3 vgrid((unsigned)tt.tile_cu[sb.n], n_kv);
-  const int64_t vh_keys = vstage_keys(T, sb.n);
+  // A continuation stages all of its sequences' values from the cache once
+  // the new ones are in; a fresh prompt stages them here, as they pass.
+  const bool cont = has_prior(sb);
+  const int64_t vh_keys = vstage_keys(sb);
   if (dtype == BF16)
-    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv, vstage, vh_keys);
+    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv,
+                                                   cont ? nullptr : vstage, vh_keys);
   else
     vt_append_kernel<float><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (float*)kv, layer, n_q, n_kv, nullptr, 0);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !cont || !vstage || dtype != BF16) return e;
+  return vstage_from_cache(T, sb, st, (const bf16_t*)kv, layer, n_kv, vstage, s);
 }
 
 hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
                              uint16_t* vstage, hipStream_t s) {
   if (T <= 0 || sb.decode) return hipSuccess;
-  const VtTiles tt = vt_tiles(sb);
+  const VtTiles tt = vt_tiles(sb, true);
   dim3 grid((unsigned)tt.tile_cu[sb.n], n_kv);
-  vstage_kernel<<<grid, 256, 0, s>>>(sb, tt, st, kv, layer, n_kv, vstage, vstage_keys(T, sb.n));
+  vstage_kernel<<<grid, 256, 0, s>>>(sb, tt, st, kv, layer, n_kv, vstage, vstage_keys(sb));
   return hipGetLastError();
 }
 
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(1024) void argmax_finish_kernel(const float* __rest
     next[m] = bi == 0x7fffffff ? 0 : bi;
     if (m < sb.n) {
       SeqState* s = st + sb.slot[m];
-      s->len = sb.decode ? s->len + 1 : sb.cu[m + 1] - sb.cu[m];
+      s->len = sb.decode ? s->len + 1 : sb.prior[m] + sb.cu[m + 1] - sb.cu[m];
     }
   }
 }
@@ -414,7 +431,7 @@ __global__ void seq_advance_kernel(SeqBatch sb, SeqState* st) {
   const int b = threadIdx.x;
   if (b < sb.n) {
     SeqState* s = st + sb.slot[b];
-    s->len = sb.decode ? s->len + 1 : sb.cu[b + 1] - sb.cu[b];
+    s->len = sb.decode ? s->len + 1 : sb.prior[b] + sb.cu[b + 1] - sb.cu[b];
   }
 }
 

@@ -32,14 +32,15 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                        void* kv, int layer, int n_q, int n_kv, const float* qn, const float* kn,
                        float eps, const float* cos_t, const float* sin_t, void* q_out,
                        uint32_t* err, hipStream_t s, uint16_t* vstage = nullptr);
-// fp16 staging of a bf16 prefill call's values from the cache (vstage_keys(T, n)
-// keys per kv head); rope_append writes the same staging when given one.
+// fp16 staging of a bf16 prefill call's values from the cache (vstage_keys(sb)
+// keys per kv head: every key 0 .. prior + L - 1 of each sequence);
+// rope_append writes the same staging when given one.
 hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
                              uint16_t* vstage, hipStream_t s);
 hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
                        uint32_t* err, hipStream_t s);
 // Reduce per-block (max, index) partials of EPI_ARGMAX into next[m], then
-// advance the lengths of the sequences of `sb` (decode: +1; prefill: = length).
+// advance the lengths of the sequences of `sb` (decode: +1; prefill: = prior + length).
 hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
                          const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s);
 hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s);

@@ -121,7 +121,8 @@ q3_status rowgemv_op(int epi, const void* X, const float* gnorm, float eps, cons
   return Q3_OK;
 }
 
-q3_status make_batch(int n, const int32_t* cu, int decode, SeqBatch* sb) {
+// Prefill: sequence b continues after prior[b] cached tokens (NULL: none).
+q3_status make_batch(int n, const int32_t* cu, int decode, SeqBatch* sb, const int32_t* prior = nullptr) {
   if (n < 1 || n > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "n_seqs must be in [1, 64]");
   std::memset(sb, 0, sizeof(*sb));
   sb->n = n;
@@ -134,6 +135,11 @@ q3_status make_batch(int n, const int32_t* cu, int decode, SeqBatch* sb) {
     for (int b = 0; b <= n; ++b) sb->cu[b] = cu[b];
     for (int b = 0; b < n; ++b)
       if (cu[b + 1] <= cu[b]) return op_fail(Q3_E_ARG, "empty sequence");
+    if (prior)
+      for (int b = 0; b < n; ++b) {
+        if (prior[b] < 0) return op_fail(Q3_E_ARG, "negative cached length");
+        sb->prior[b] = prior[b];
+      }
   }
   return Q3_OK;
 }
@@ -249,14 +255,14 @@ q3_status q3op_rope_append(int32_t dtype, const float* d_qkv, int32_t n, const i
                            double theta, int32_t max_pos, void* d_q_out, void* d_ws, size_t ws_bytes,
                            void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  SeqBatch sb;
-  q3_status st = make_batch(n, h_cu, decode, &sb);
-  if (st != Q3_OK) return st;
   if (!d_qkv || !d_kv || !d_qn || !d_kn || !d_q_out || !h_base || !h_cap || !h_len || max_pos <= 0)
     return op_fail(Q3_E_ARG, "bad argument");
+  SeqBatch sb;
+  q3_status st = make_batch(n, h_cu, decode, &sb, h_len);
+  if (st != Q3_OK) return st;
   if (!d_ws || ws_bytes < q3op_rope_workspace_bytes(n, max_pos)) return op_fail(Q3_E_ARG, "workspace too small");
   for (int b = 0; b < n; ++b) {
-    const int last = decode ? h_len[b] : (sb.cu[b + 1] - sb.cu[b] - 1);
+    const int last = decode ? h_len[b] : (h_len[b] + sb.cu[b + 1] - sb.cu[b] - 1);
     if (last >= h_cap[b] || last >= max_pos) return op_fail(Q3_E_CAPACITY, "position beyond capacity");
   }
   char* ws = (char*)d_ws;
@@ -285,7 +291,9 @@ size_t q3op_attention_workspace_bytes(int32_t kernel, int32_t n_seqs, int32_t to
                                       int32_t n_kv, int32_t splits) {
   size_t b = al(n_seqs * sizeof(SeqState));
   if (kernel == Q3OP_ATTN_DECODE) b += al((size_t)n_seqs * n_q * (splits > 0 ? splits : 2048) * 130 * 4);
-  if (kernel == Q3OP_ATTN_FLASH) b += al((size_t)vstage_keys(std::max(total_tokens, 0), n_seqs) * n_kv * 128 * 2);
+  // every sequence's keys rounded up to 64, plus one tile
+  if (kernel == Q3OP_ATTN_FLASH)
+    b += al(((size_t)std::max(total_tokens, 0) + 64 * (size_t)std::max(n_seqs, 0) + 64) * n_kv * 128 * 2);
   return b;
 }
 
@@ -294,15 +302,15 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
                          int32_t n_q, int32_t n_kv, int32_t splits, void* d_out, void* d_ws, size_t ws_bytes,
                          void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  SeqBatch sb;
-  q3_status st = make_batch(n, h_cu, decode, &sb);
-  if (st != Q3_OK) return st;
   if (!d_q || !d_kv || !d_out || !h_base || !h_cap || !h_len) return op_fail(Q3_E_ARG, "bad argument");
+  SeqBatch sb;
+  q3_status st = make_batch(n, h_cu, decode, &sb, h_len);
+  if (st != Q3_OK) return st;
   if (n_kv <= 0 || n_q % n_kv != 0 || n_q / n_kv > 8) return op_fail(Q3_E_UNSUPPORTED, "head grouping");
   if (kernel == Q3OP_ATTN_FLASH && decode) return op_fail(Q3_E_ARG, "flash kernel is the prefill kernel");
   if (kernel == Q3OP_ATTN_DECODE && !decode) return op_fail(Q3_E_ARG, "decode kernel needs decode = 1");
   for (int b = 0; b < n; ++b) {
-    const int ctx = decode ? h_len[b] + 1 : sb.cu[b + 1] - sb.cu[b];
+    const int ctx = decode ? h_len[b] + 1 : h_len[b] + sb.cu[b + 1] - sb.cu[b];
     if (ctx > h_cap[b]) return op_fail(Q3_E_CAPACITY, "context beyond capacity");
   }
   if (kernel == Q3OP_ATTN_DECODE && splits <= 0) {
@@ -311,7 +319,10 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
     splits = decode_attn_splits(n, n_kv, mc);
   }
   const int T = sb.cu[n];
-  if (!d_ws || ws_bytes < q3op_attention_workspace_bytes(kernel, n, T, n_q, n_kv, splits))
+  int64_t keys = 0;  // keys of the call: cached + new
+  for (int b = 0; b < n; ++b) keys += (decode ? 0 : h_len[b]) + sb.cu[b + 1] - sb.cu[b];
+  if (keys > INT32_MAX) return op_fail(Q3_E_CAPACITY, "too many keys");
+  if (!d_ws || ws_bytes < q3op_attention_workspace_bytes(kernel, n, (int32_t)keys, n_q, n_kv, splits))
     return op_fail(Q3_E_ARG, "workspace too small");
   char* ws = (char*)d_ws;
   st = upload_states(n, h_base, h_cap, h_len, ws, s);

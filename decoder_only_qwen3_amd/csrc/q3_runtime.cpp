@@ -55,6 +55,7 @@ struct WsLayout {
   size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, vstage, state,
       err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
+  int64_t vstage_cap;  // keys per kv head of the fp16 value staging
   int amax_blocks;
 };
 
@@ -153,8 +154,11 @@ WsLayout ws_layout(const q3_config& c) {
   }
   W.lin_part = take(std::max<size_t>(16, part) * 4);
   W.lin_cnt = take(std::max<size_t>(H / 16 + 1, 256) * 4);
-  // fp16 values of a bf16 prefill call for the flash kernel
-  W.vstage = take(c.dtype == BF16 ? (size_t)vstage_keys(R, Q3_MAX_BATCH) * c.n_kv_heads * 128 * 2 : 16);
+  // fp16 values of a bf16 prefill call for the flash kernel: every call of
+  // fresh prompts fits (sum of L rounded up to 64, plus one tile), and so does
+  // one continued sequence of up to max_positions
+  W.vstage_cap = std::max<int64_t>(R, c.max_positions) + 64 * Q3_MAX_BATCH + 64;
+  W.vstage = take(c.dtype == BF16 ? (size_t)W.vstage_cap * c.n_kv_heads * 128 * 2 : 16);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -689,9 +693,8 @@ q3_status q3_prefill(q3_model* m, int32_t n, const int32_t* h_slots, const int32
     const int64_t L = (int64_t)h_cu[b + 1] - h_cu[b];
     if (L < 1) return fail(Q3_E_ARG, "every sequence needs at least one token");
     const HostSlot& hs = m->slots[h_slots[b]];
-    if (hs.len != 0) return fail(Q3_E_STATE, "prefill needs an empty slot");
-    if (L > hs.cap) return fail(Q3_E_CAPACITY, "KV cache full: prompt longer than the slot");
-    if (L > m->cfg.max_positions) return fail(Q3_E_CAPACITY, "prompt longer than max_positions");
+    if (hs.len + L > hs.cap) return fail(Q3_E_CAPACITY, "KV cache full: prompt longer than the slot");
+    if (hs.len + L > m->cfg.max_positions) return fail(Q3_E_CAPACITY, "sequence longer than max_positions");
   }
   const int64_t T = h_cu[n];
   if (T > m->cfg.max_prefill_tokens) return fail(Q3_E_CAPACITY, "more tokens than max_prefill_tokens");
@@ -703,6 +706,9 @@ q3_status q3_prefill(q3_model* m, int32_t n, const int32_t* h_slots, const int32
   sb.decode = 0;
   for (int b = 0; b < n; ++b) sb.slot[b] = h_slots[b];
   for (int b = 0; b <= n; ++b) sb.cu[b] = h_cu[b];
+  for (int b = 0; b < n; ++b) sb.prior[b] = (int32_t)m->slots[h_slots[b]].len;
+  if (c.dtype == Q3_BF16 && vstage_keys(sb) > m->wsl.vstage_cap)
+    return fail(Q3_E_CAPACITY, "continued sequences too long for one call: split it");
 
   LAUNCH(embed(c.dtype, d_tokens, (int)T, m->W(m->wl.embed), c.vocab, c.hidden, m->WS<float>(m->wsl.x), m->err(), s));
   st = enqueue_layers(m, (int)T, sb, false, s);
@@ -729,7 +735,7 @@ q3_status q3_prefill(q3_model* m, int32_t n, const int32_t* h_slots, const int32
     LAUNCH(argmax_rows(d_logits, c.vocab, last, c.vocab, d_next, m->err(), s));
     LAUNCH(seq_advance(sb, m->state(), s));
   }
-  for (int b = 0; b < n; ++b) m->slots[h_slots[b]].len = h_cu[b + 1] - h_cu[b];
+  for (int b = 0; b < n; ++b) m->slots[h_slots[b]].len += h_cu[b + 1] - h_cu[b];
   g_err.clear();
   return Q3_OK;
 }

@@ -122,7 +122,8 @@ class Q3Model:
                                       d_next.data_ptr(), self.sh))
 
     def prefill(self, slots: Sequence[int], prompts: Sequence[Sequence[int]], all_logits: bool = False):
-        """Prefill several empty slots; returns (logits, next) device tensors."""
+        """Prefill several slots (a slot holding tokens already is continued after
+        them); returns (logits, next) device tensors."""
         lens = [len(p) for p in prompts]
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         flat = np.concatenate([np.asarray(p, dtype=np.int32) for p in prompts])

@@ -133,10 +133,14 @@ q3_status q3_seq_length(const q3_model* m, int32_t slot, int64_t* out);
 /* Prefill flags. */
 #define Q3_PREFILL_ALL_LOGITS 1u  /* d_logits receives [T, vocab]: every position */
 
-/* Prefill n_seqs empty sequences at once (Paso 9's first forward call, packed
- * as one variable-length batch).  Sequence b consists of tokens
- * d_tokens[h_cu_seqlens[b] .. h_cu_seqlens[b+1]) at positions 0.., uses slot
- * h_slots[b], and attends causally to its own tokens only.
+/* Prefill n_seqs sequences at once (Paso 9's first forward call, packed as
+ * one variable-length batch).  Sequence b consists of tokens
+ * d_tokens[h_cu_seqlens[b] .. h_cu_seqlens[b+1]), uses slot h_slots[b] and
+ * attends causally to its own tokens.  A slot that already holds P_b tokens
+ * (an earlier prefill or decode) is continued: the new tokens sit at
+ * positions P_b, P_b + 1, .. and also attend to the cached ones, so a prompt
+ * fed in chunks gives what one prefill of the whole prompt gives, up to
+ * rounding (chunked prefill).  An empty slot starts at position 0.
  *   h_cu_seqlens: n_seqs+1 non-decreasing offsets, [0] = 0, each length >= 1,
  *                 total T <= max_prefill_tokens.
  *   d_tokens:     int32 [T].  IDs outside [0, vocab) are not checked on the
@@ -147,8 +151,11 @@ q3_status q3_seq_length(const q3_model* m, int32_t slot, int64_t* out);
  *                 that flag.
  *   d_next:       int32 [n_seqs] greedy next token (largest logit, lowest
  *                 index on ties; Paso 8).
- * Errors: Q3_E_STATE if a slot is not empty or unallocated;
- * Q3_E_CAPACITY if a sequence exceeds its slot or max_positions. */
+ * Errors: Q3_E_STATE if a slot is unallocated; Q3_E_CAPACITY if P_b + L_b
+ * exceeds the slot or max_positions, or (bf16 model, some P_b > 0) if the
+ * sum over the call of roundup(P_b + L_b, 64) exceeds
+ * max(max_prefill_tokens, max_positions) + 64 * 64: the fp16 staging of the
+ * values every key of the call needs (split such a call). */
 q3_status q3_prefill(q3_model* m, int32_t n_seqs, const int32_t* h_slots,
                      const int32_t* h_cu_seqlens, const int32_t* d_tokens, float* d_logits,
                      int32_t* d_next, uint32_t flags, void* stream);

@@ -279,10 +279,11 @@ def _arena(lens_cap, n_kv, esz):
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32])
-@pytest.mark.parametrize("decode", [0, 1])
-def test_rope_append(dtype, decode):
+@pytest.mark.parametrize("mode", ["prefill", "decode", "continue"])
+def test_rope_append(dtype, mode):
     mod, lib = ops()
-    rng = np.random.default_rng(5 + decode)
+    decode = 1 if mode == "decode" else 0
+    rng = np.random.default_rng(5 + decode + 7 * (mode == "continue"))
     n_q, n_kv = 16, 8
     if decode:
         lens = [1, 1, 1]
@@ -291,7 +292,9 @@ def test_rope_append(dtype, decode):
     else:
         lens = [3, 64, 130]
         cu = list(np.concatenate([[0], np.cumsum(lens)]))
-        prior = [0, 0, 0]
+        # continuation: new positions start inside a 32-key value block, on a
+        # 64-position tile boundary, and mid-tile with a partial tail
+        prior = [0, 0, 0] if mode == "prefill" else [5, 64, 3001]
     caps = [4096, 128, 4096]
     T = cu[-1]
     units = n_q + 2 * n_kv
@@ -318,7 +321,7 @@ def test_rope_append(dtype, decode):
     tol = dict(rtol=2 ** -7, atol=1e-6) if dtype == BF16 else dict(rtol=1e-5, atol=1e-6)
     for b in range(len(lens)):
         rows = slice(cu[b], cu[b + 1])
-        pos = (np.arange(lens[b]) if not decode else np.array([prior[b]]))
+        pos = prior[b] + np.arange(lens[b])
         x = qkv[rows].astype(np.float64).reshape(-1, units, 128)
         c, s = rope_cos_sin(pos, 128, 1e6)
         q_ref = rnd(rope_rotate(rms_norm(x[:, :n_q], qn, 1e-6), c, s))
@@ -332,12 +335,17 @@ def test_rope_append(dtype, decode):
         for i, p in enumerate(pos):
             np.testing.assert_allclose(K[:, p, :], k_ref[i], **tol)
             np.testing.assert_array_equal(Vt[:, :, p], v_ref[i].astype(np.float32))
-        if not decode:  # nothing written past the sequence (the last value tile is partial)
-            assert not np.any(K[:, lens[b]:, :]) and not np.any(Vt[:, :, lens[b]:])
+        if not decode:  # nothing written outside the new positions (partial value tiles)
+            end = prior[b] + lens[b]
+            assert not np.any(K[:, end:, :]) and not np.any(Vt[:, :, end:])
+            assert not np.any(K[:, :prior[b], :]) and not np.any(Vt[:, :, :prior[b]])
 
 
 # ---------------------------------------------------------------- Paso 5: attention
-def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0):
+def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0, cached=None):
+    """decode: query b at position prior[b] over keys 0..prior[b].  Prefill:
+    token i of sequence b at position cached[b] + i (cached[b] = 0 by default)
+    over keys 0..cached[b] + i."""
     mod, lib = ops()
     rng = np.random.default_rng(seed)
     decode = kernel == 1 or (kernel == 2 and prior is not None)
@@ -349,8 +357,8 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
         cu = list(range(n + 1))
         q = mk((n, n_q, 128))
     else:
-        ctx = list(lens)
-        prior = [0] * n
+        prior = list(cached) if cached is not None else [0] * n
+        ctx = [p + L for p, L in zip(prior, lens)]
         cu = list(np.concatenate([[0], np.cumsum(lens)]))
         q = mk((cu[-1], n_q, 128))
     bases, total = _arena(caps, n_kv, 2 if bf else 4)
@@ -390,7 +398,8 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
         dkv = dev_f32(arena)
         dq = dev_f32(q)
         out = torch.zeros((q.shape[0], n_q, 128), dtype=torch.float32, device="cuda:0")
-    ws = _ws(lib.q3op_attention_workspace_bytes(kernel, n, int(cu[-1]), n_q, n_kv, splits))
+    keys = int(cu[-1]) if decode else int(sum(ctx))
+    ws = _ws(lib.q3op_attention_workspace_bytes(kernel, n, keys, n_q, n_kv, splits))
     call(lib.q3op_attention(kernel, dq.data_ptr(), n, mod.i32_array(cu), 1 if decode else 0,
                             mod.i64_array(bases), mod.i32_array(caps), mod.i32_array(prior), dkv.data_ptr(),
                             n_q, n_kv, splits, out.data_ptr(), ws.data_ptr(), ws.numel(), None))
@@ -406,8 +415,9 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0)
             g = got[b:b + 1]
         else:
             qb = q[cu[b]:cu[b + 1]].astype(np.float64)
-            pos = np.arange(lens[b])
-            ref = attention_rows(qb, Ks[b].astype(np.float64), Vs[b].astype(np.float64), pos, pos)
+            pos = prior[b] + np.arange(lens[b])
+            ref = attention_rows(qb, Ks[b].astype(np.float64), Vs[b].astype(np.float64), pos,
+                                 np.arange(ctx[b]))
             g = got[cu[b]:cu[b + 1]]
         assert np.all(np.isfinite(g)), f"seq {b}: non-finite output"
         # Error in units of the allowed bound.  bf16 output: half an ulp of the
@@ -438,6 +448,37 @@ def test_flash_prefill_rows_per_wavefront(rows):
             assert worst < 1.0, (rows, n_q, n_kv, worst)
     finally:
         call(lib.q3op_tune(2, -1))
+
+
+@pytest.mark.parametrize("lens,cached", [
+    ([1], [1]), ([5], [64]), ([64], [37]), ([130, 1, 63, 200], [0, 500, 1, 64]),
+    ([600, 3, 130, 1100], [2000, 0, 127, 31]), ([1], [8191])])
+def test_flash_prefill_attention_continues_cache(lens, cached):
+    """Prefill into a cache that already holds `cached` keys per sequence:
+    queries at positions cached + i see every cached key and the new ones."""
+    caps = [((c + L + 63) // 64) * 64 for L, c in zip(lens, cached)]
+    worst = _attention_case(0, lens, None, caps, seed=3 * len(lens) + cached[0], cached=cached)
+    assert worst < 1.0, worst
+
+
+@pytest.mark.parametrize("rows", [1, 2])
+def test_flash_prefill_continues_cache_rows_per_wavefront(rows):
+    _, lib = ops()
+    call(lib.q3op_tune(2, rows))
+    try:
+        lens, cached = [300, 3, 130], [70, 1000, 0]
+        caps = [((c + L + 63) // 64) * 64 for L, c in zip(lens, cached)]
+        worst = _attention_case(0, lens, None, caps, seed=rows + 50, cached=cached)
+        assert worst < 1.0, (rows, worst)
+    finally:
+        call(lib.q3op_tune(2, -1))
+
+
+def test_f32_prefill_attention_continues_cache():
+    lens, cached = [5, 70], [3, 130]
+    caps = [((c + L + 63) // 64) * 64 for L, c in zip(lens, cached)]
+    worst = _attention_case(2, lens, None, caps, seed=9, cached=cached)
+    assert worst < 1.0, worst
 
 
 def test_flash_prefill_gqa_groups():

@@ -151,3 +151,121 @@ def test_bf16_varlen_all_logits_matches_oracle(bf16_two_layer):
         assert margin_ok(ref[-1], int(nxt[i].item()), TOL_BF16 * float(np.sqrt(np.mean(ref[-1] ** 2))))
         row += len(p)
     assert m.error_flags() == 0
+
+
+# ---------------------------------------------------------------- chunked prefill
+def _check_rows(got, ref, tol, what):
+    for r in range(len(ref)):
+        e = rel_err(got[r], ref[r])
+        assert e <= tol, f"{what} row {r}: {e:.3e} > {tol}"
+
+
+def test_bf16_chunked_prefill_matches_single_prefill_oracle(bf16_two_layer):
+    """A 200-token prompt fed as four prefill calls into one slot (chunks that
+    start on and off 64-token tiles), then forced decode steps: every row
+    matches the oracle's one-call prefill of the whole prompt."""
+    d, w = bf16_two_layer
+    prompt = q3synth.make_tokens(200, d.vocab, 11).tolist()
+    forced = q3synth.make_tokens(6, d.vocab, 12).tolist()
+    o = OracleModel(d, w)
+    ref = o.forward(prompt + forced, o.new_cache(206), logit_rows=range(206))
+    m = _model(d, max_slots=2, max_positions=256, max_prefill_tokens=128, kv_tokens=512)
+    m.load_weights(w)
+    m.seq_alloc(1, 256)
+    row = 0
+    for a, b in [(0, 64), (64, 65), (65, 150), (150, 200)]:
+        logits, nxt = m.prefill([1], [prompt[a:b]], all_logits=True)
+        m.synchronize()
+        assert m.seq_length(1) == b
+        _check_rows(logits.cpu().numpy(), ref[a:b], TOL_BF16, f"chunk {a}:{b}")
+        rms = float(np.sqrt(np.mean(ref[b - 1] ** 2)))
+        assert margin_ok(ref[b - 1], int(nxt[0].item()), TOL_BF16 * rms), f"chunk {a}:{b} next token"
+    dev = m.device
+    with torch.cuda.stream(m.stream):
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        lg = torch.empty((1, d.vocab), dtype=torch.float32, device=dev)
+        nx = torch.empty(1, dtype=torch.int32, device=dev)
+    for i, t in enumerate(forced):
+        with torch.cuda.stream(m.stream):
+            tok.fill_(int(t))
+        m.decode_raw([1], tok, lg, nx)
+        m.synchronize()
+        _check_rows(lg.cpu().numpy(), ref[200 + i:201 + i], TOL_BF16, f"decode {i}")
+    assert m.error_flags() == 0
+
+
+def test_bf16_chunked_prefill_mixed_batch(bf16_two_layer):
+    """One call continuing two slots (after 70 and after 1 cached tokens) and
+    starting a fresh one, then a decode step for all three."""
+    d, w = bf16_two_layer
+    full = [q3synth.make_tokens(L, d.vocab, 60 + i).tolist() for i, L in enumerate([150, 40, 90])]
+    first = {0: 70, 2: 1}
+    o = OracleModel(d, w)
+    m = _model(d, max_slots=4, max_positions=256, max_prefill_tokens=256, kv_tokens=1024)
+    m.load_weights(w)
+    slots = [3, 0, 1]
+    for s, p in zip(slots, full):
+        m.seq_alloc(s, len(p) + 4)
+    lg0, _ = m.prefill([slots[0], slots[2]], [full[0][:70], full[2][:1]])
+    m.synchronize()
+    rest = [full[0][70:], full[1], full[2][1:]]
+    logits, nxt = m.prefill(slots, rest, all_logits=True)
+    m.synchronize()
+    g = logits.cpu().numpy()
+    row = 0
+    refs = []
+    for i, p in enumerate(full):
+        ref = o.forward(p, o.new_cache(len(p) + 1), logit_rows=range(len(p)))
+        refs.append(ref)
+        start = first.get(i, 0)
+        n = len(p) - start
+        _check_rows(g[row:row + n], ref[start:], TOL_BF16, f"seq {i}")
+        rms = float(np.sqrt(np.mean(ref[-1] ** 2)))
+        assert margin_ok(ref[-1], int(nxt[i].item()), TOL_BF16 * rms), f"seq {i} next token"
+        row += n
+    for s, p in zip(slots, full):
+        assert m.seq_length(s) == len(p)
+    # one decode step on top of the continued slots (the oracle's next rows)
+    toks = [q3synth.make_tokens(1, d.vocab, 80 + i).tolist()[0] for i in range(3)]
+    with torch.cuda.stream(m.stream):
+        dt = torch.tensor(toks, dtype=torch.int32, device=m.device)
+    lg, _ = m.decode(slots, dt)
+    m.synchronize()
+    gd = lg.cpu().numpy()
+    for i, p in enumerate(full):
+        ref = o.forward(p + [toks[i]], o.new_cache(len(p) + 1), logit_rows=[len(p)])
+        _check_rows(gd[i:i + 1], ref, TOL_BF16, f"decode seq {i}")
+    assert m.error_flags() == 0
+
+
+def test_f32_chunked_prefill_matches_oracle():
+    wl = q3synth.WORKLOADS["tiny2l_f32_p5_d16"]
+    d = wl.dims
+    w = weights_for(d, 31)
+    prompt = q3synth.make_tokens(90, d.vocab, 32).tolist()
+    o = OracleModel(d, w)
+    ref = o.forward(prompt, o.new_cache(90), logit_rows=range(90))
+    m = _model(d, max_slots=1, max_positions=128, max_prefill_tokens=64, kv_tokens=128)
+    m.load_weights(w)
+    m.seq_alloc(0, 96)
+    for a, b in [(0, 3), (3, 64), (64, 90)]:
+        logits, nxt = m.prefill([0], [prompt[a:b]], all_logits=True)
+        m.synchronize()
+        _check_rows(logits.cpu().numpy(), ref[a:b], TOL_F32, f"chunk {a}:{b}")
+        rms = float(np.sqrt(np.mean(ref[b - 1] ** 2)))
+        assert margin_ok(ref[b - 1], int(nxt[0].item()), TOL_F32 * rms)
+    assert m.error_flags() == 0
+
+
+def test_prefill_rejects_overflowing_continuation(bf16_two_layer):
+    from decoder_only_qwen3_amd import Q3Error
+    d, w = bf16_two_layer
+    m = _model(d, max_slots=1, max_positions=256, max_prefill_tokens=128, kv_tokens=128)
+    m.load_weights(w)
+    m.seq_alloc(0, 64)
+    m.prefill([0], [q3synth.make_tokens(60, d.vocab, 1).tolist()])
+    with pytest.raises(Q3Error) as ei:
+        m.prefill([0], [q3synth.make_tokens(5, d.vocab, 2).tolist()])
+    assert "CAPACITY" in str(ei.value)
+    m.synchronize()
+    assert m.seq_length(0) == 60
