@@ -86,11 +86,13 @@ def decode_bytes_per_step(d, ctxs):
     return weights + norms + kv_read + kv_write + logits
 
 
-def prefill_flops(d, lens):
+def prefill_flops(d, lens, calls=1):
+    """Prefill FLOPs of the prompts `lens`, split into `calls` calls (each call
+    ends with the head on every sequence's last row; attention is the same)."""
     L, H, Q, KV, I, V = d.n_layers, d.hidden, d.n_q_heads * 128, d.n_kv_heads * 128, d.ffn, d.vocab
     per_tok = 2 * L * (H * (Q + 2 * KV) + Q * H + 3 * I * H)
     attn = sum(4 * d.n_q_heads * 128 * L * n * (n + 1) // 2 for n in lens)
-    head = 2 * V * H * len(lens)
+    head = 2 * V * H * len(lens) * calls
     return per_tok * sum(lens) + attn + head
 
 
@@ -139,7 +141,13 @@ def main():
     t_gen = time.perf_counter() - t_gen
 
     cap = max(lens) + steps_dec
-    m = Q3Model(d, max_slots=B, max_positions=cap, max_prefill_tokens=sum(lens), kv_tokens=B * ((cap + 63) // 64 * 64))
+    # Chunked workloads prefill every prompt in calls of wl.chunk tokens.
+    if wl.chunk > 0 and len(set(lens)) != 1:
+        raise SystemExit("chunked workloads need equal prompt lengths")
+    bounds = ([(a, min(a + wl.chunk, lens[0])) for a in range(0, lens[0], wl.chunk)] if wl.chunk > 0
+              else [(0, None)])
+    max_call = sum(lens) if wl.chunk <= 0 else B * wl.chunk
+    m = Q3Model(d, max_slots=B, max_positions=cap, max_prefill_tokens=max_call, kv_tokens=B * ((cap + 63) // 64 * 64))
     m.load_weights(w)
     if args.no_graphs:
         m.set_graphs(False)
@@ -147,9 +155,12 @@ def main():
     for s in slots:
         m.seq_alloc(s, cap)
     dev = m.device
-    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    calls = []  # (cu_seqlens, device tokens) of each prefill call
     with torch.cuda.stream(m.stream):
-        d_prompt = torch.from_numpy(np.concatenate([np.asarray(p, np.int32) for p in prompts])).to(dev)
+        for a, b in bounds:
+            parts = [np.asarray(p[a:b], np.int32) for p in prompts]
+            cu = np.concatenate([[0], np.cumsum([len(x) for x in parts])]).astype(np.int32)
+            calls.append((cu, torch.from_numpy(np.concatenate(parts)).to(dev)))
         d_tok = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
         d_logits = torch.empty((B, d.vocab), dtype=torch.float32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -158,7 +169,8 @@ def main():
         m.seq_reset(slots)
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(m.stream)
-        m.prefill_raw(slots, cu, d_prompt, d_logits, d_tok[0])
+        for cu, d_prompt in calls:
+            m.prefill_raw(slots, cu, d_prompt, d_logits, d_tok[0])
         e1.record(m.stream)
         for i in range(steps_dec):
             m.decode_raw(slots, d_tok[i % 2], d_logits, d_tok[(i + 1) % 2])
@@ -187,7 +199,7 @@ def main():
     dec_step_s = (sum(dec_ms) / 1e3) / (args.steps * steps_dec)
     decode_hbm = {"bytes_per_step": float(byts), "achieved_GBs": byts / dec_step_s / 1e9,
                   "frac": byts / dec_step_s / 1e9 / HBM_PEAK_GBS}
-    pf = prefill_flops(d, lens)
+    pf = prefill_flops(d, lens, len(calls))
     prefill_mfma = {"flops": pf, "achieved_TFLOPs": pf / (np.mean(pre_ms) / 1e3) / 1e12,
                     "frac": pf / (np.mean(pre_ms) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
@@ -247,7 +259,8 @@ def main():
         "dtype": "bf16" if d.dtype == "bf16" else "f32",
         "data": "synthetic: seeded N(0,0.02) weights (norms 1+N(0,0.1)), uniform random token IDs",
         "config": {"workload": wl.name, "n_layers": d.n_layers, "n_seqs": B, "prompt_tokens": lens if B <= 4 else sum(lens),
-                   "decode_steps": steps_dec, "graphs": not args.no_graphs},
+                   "decode_steps": steps_dec, "graphs": not args.no_graphs,
+                   **({"prefill_chunk": wl.chunk} if wl.chunk > 0 else {})},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2),
         "prefill_ms": round(float(np.mean(pre_ms)), 3),

@@ -453,14 +453,17 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
   int cfg = g_gemm_cfg;
   if (cfg < 0) {
     // The largest tile whose grid still gives each of the 256 CUs a block:
-    // 256 x 256 (4-slice LDS pipeline, 16 wavefronts), else 128 x 128, else
-    // 64 x 64.  Measured on MI355X at M = 32768: 790, 970 and 950 TFLOP/s for
-    // the q/k/v, gate/up and down shapes with the pipeline; the other
-    // configurations (8-wavefront tiles, two blocks per CU, two LDS slices,
-    // fragment double-buffering) measured 5-25 % below it.
+    // 256 x 256 (4-slice LDS pipeline, 16 wavefronts), else 128 x 128 (the
+    // same pipeline, 4 wavefronts), else 64 x 64.  Measured on MI355X at
+    // M = 32768: 790, 970 and 950 TFLOP/s for the q/k/v, gate/up and down
+    // shapes with the 256 x 256 pipeline; the other configurations
+    // (8-wavefront tiles, two blocks per CU, two LDS slices, fragment
+    // double-buffering) measured 5-25 % below it.  At M = 4096 the 128 x 128
+    // pipeline runs the o and down shapes (256 tiles) at 445 and 516 TFLOP/s,
+    // 15 % above the 128 x 128 tile without it.
     const int64_t g256 = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
     const int64_t g128 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
-    cfg = g256 >= 256 ? 7 : (g128 >= 256 ? 1 : 0);
+    cfg = g256 >= 256 ? 7 : (g128 >= 256 ? 8 : 0);
   }
   switch (cfg) {
     case 0: return gemm_launch<2, 2, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   //  64 x  64, 4 waves

@@ -180,6 +180,10 @@ CASES = {
     "gemm_o_512": lambda lib, r, s: linear_case(lib, "gemm_o_512", 1, 512, H, Q, r, s, kernel=0),
     "gemm_gate_up_512": lambda lib, r, s: linear_case(lib, "gemm_gate_up_512", 2, 512, 2 * I, H, r, s, kernel=0),
     "gemm_down_512": lambda lib, r, s: linear_case(lib, "gemm_down_512", 1, 512, H, I, r, s, kernel=0),
+    "gemm_qkv_4k": lambda lib, r, s: linear_case(lib, "gemm_qkv_4k", 0, 4096, Q + 2 * KVW, H, r, s, kernel=0),
+    "gemm_o_4k": lambda lib, r, s: linear_case(lib, "gemm_o_4k", 1, 4096, H, Q, r, s, kernel=0),
+    "gemm_gate_up_4k": lambda lib, r, s: linear_case(lib, "gemm_gate_up_4k", 2, 4096, 2 * I, H, r, s, kernel=0),
+    "gemm_down_4k": lambda lib, r, s: linear_case(lib, "gemm_down_4k", 1, 4096, H, I, r, s, kernel=0),
     "flash_512": lambda lib, r, s: attention_case(lib, "flash_512", 0, 512, 1, r, s),
     "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
     "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),

@@ -67,6 +67,7 @@ class Workload:
     len_range: Tuple[int, int] = (0, 0)  # inclusive range for drawn lengths
     decode_steps: int = 0
     seed: int = 0
+    chunk: int = 0           # > 0: each prompt is prefilled in calls of this many tokens
 
     def prompt_lengths(self) -> np.ndarray:
         if self.prompt_len > 0:
@@ -90,6 +91,10 @@ WORKLOADS: Dict[str, Workload] = {
     # One 32,768-token prompt then 32 decode steps.
     "q06b_bf16_p32768_d32": Workload("q06b_bf16_p32768_d32", QWEN3_06B, n_seqs=1,
                                      prompt_len=32768, decode_steps=32, seed=1003),
+    # The 32,768-token prompt above prefilled in eight calls of 4096 tokens
+    # (each continuing the cache of the ones before), then 32 decode steps.
+    "q06b_bf16_p32768_c4096_d32": Workload("q06b_bf16_p32768_c4096_d32", QWEN3_06B, n_seqs=1,
+                                           prompt_len=32768, decode_steps=32, seed=1003, chunk=4096),
     # 64 sequences with lengths uniform in [128, 8192], packed prefill, 128 steps.
     "q06b_bf16_b64_ragged_d128": Workload("q06b_bf16_b64_ragged_d128", QWEN3_06B, n_seqs=64,
                                           prompt_len=0, len_range=(128, 8192),

@@ -55,6 +55,16 @@ def _prefill_then_forced(m, slots, prompts, forced):
     return np.stack([r.cpu().numpy() for r in rows])
 
 
+def _chunked_prefill(m, slot, prompt, chunk):
+    """Prefill one slot in calls of `chunk` tokens; logits of the last call."""
+    for a in range(0, len(prompt), chunk):
+        logits, nxt = m.prefill([slot], [prompt[a:a + chunk]])
+    with torch.cuda.stream(m.stream):
+        out = logits[0].clone()
+    m.synchronize()
+    return out.cpu().numpy(), int(nxt[0].item())
+
+
 def _check(ref, got, what):
     e = rel_err(got, ref)
     rms = float(np.sqrt(np.mean(ref ** 2)))
@@ -133,7 +143,11 @@ def test_workload_batch32_prefix2048_sampled_sequences():
 
 
 def test_workload_32k_prompt_one_layer_cut_and_properties():
+    """Also the same prompt prefilled in calls of 4096 tokens (the chunked
+    workload): against the oracle at one layer, against the single call at
+    full depth."""
     wl = q3synth.WORKLOADS["q06b_bf16_p32768_d32"]
+    chunk = q3synth.WORKLOADS["q06b_bf16_p32768_c4096_d32"].chunk
     L = wl.prompt_len
     # (a) one-layer cut at the full length against the oracle
     d1 = wl.dims.replace(n_layers=1)
@@ -150,6 +164,15 @@ def test_workload_32k_prompt_one_layer_cut_and_properties():
         _check(ref[i], got[i][0], f"1-layer step {i}")
     m.close()
     del m
+    mc = _model(d1, max_slots=1, max_positions=L + 64, max_prefill_tokens=chunk, kv_tokens=L + 64)
+    mc.load_weights(w1)
+    mc.seq_alloc(0, L + 64)
+    lc, nc = _chunked_prefill(mc, 0, prompt, chunk)
+    e = _check(ref[0], lc, "1-layer chunked prefill")
+    _say(f"1-layer chunked prefill error {e:.2e}")
+    assert mc.seq_length(0) == L and mc.error_flags() == 0
+    mc.close()
+    del mc
     # (b) full depth: decode after prefill(L-1) equals prefill(L), on the GPU
     d = wl.dims
     w = weights_for(d, wl.seed)
@@ -167,6 +190,11 @@ def test_workload_32k_prompt_one_layer_cut_and_properties():
     b = part[1][0]
     assert np.all(np.isfinite(a))
     assert rel_err(b, a) <= TOL, rel_err(b, a)
+    m.seq_reset([1])
+    c, nc = _chunked_prefill(m, 1, prompt, chunk)
+    _say(f"full-depth chunked vs single prefill: {rel_err(c, a):.2e}")
+    assert rel_err(c, a) <= TOL, rel_err(c, a)
+    assert margin_ok(a, nc, TOL * float(np.sqrt(np.mean(a ** 2))))
     assert m.error_flags() == 0
 
 
