@@ -31,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "to_bf16", "rms_norm", "rope_cos_sin", "rope_rotate", "attention_rows",
-    "silu", "swiglu", "greedy_pick", "KVCache", "OracleModel",
+    "silu", "swiglu", "greedy_pick", "sample_top_p", "KVCache", "OracleModel",
 ]
 
 
@@ -168,6 +168,42 @@ def greedy_pick(logits: np.ndarray) -> int:
     if not np.all(np.isfinite(logits)):
         raise FloatingPointError("non-finite logits")
     return int(np.argmax(logits))
+
+
+# ----------------------------------------------------------------------------
+# Paso 8: temperature + top-p (nucleus) sampling
+# ----------------------------------------------------------------------------
+def sample_top_p(logits: np.ndarray, temperature: float, top_p: float, u: float) -> int:
+    """One token from temperature + top-p sampling, the page's steps in order.
+
+    temperature == 0 is the greedy choice.  Otherwise: scale the logits by
+    1/temperature, softmax, order the probabilities from largest to smallest
+    (equal probabilities by increasing token ID), running sum, keep the first
+    #(running sum < top_p) + 1 of them (all of them at most), renormalise the
+    kept ones, and draw one.  The draw is taken by inverse transform with the
+    caller's uniform u in [0, 1): the kept token whose renormalised running
+    sum first exceeds u, in the same order.  (The page draws through a
+    categorical sampler; with the random number an input, inverse transform
+    is the plain deterministic form of that draw.)  Everything in float64.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    if not np.all(np.isfinite(z)):
+        raise FloatingPointError("non-finite logits")
+    if temperature == 0:
+        return greedy_pick(z)
+    if temperature < 0 or not 0.0 <= u < 1.0:
+        raise ValueError("temperature must be >= 0 and u in [0, 1)")
+    z = z / temperature
+    e = np.exp(z - z.max())
+    probs = e / e.sum()
+    order = np.argsort(-probs, kind="stable")
+    sorted_p = probs[order]
+    cumsum = np.cumsum(sorted_p)
+    cutoff = min(int(np.sum(cumsum < top_p)) + 1, z.size)
+    kept = sorted_p[:cutoff] / np.sum(sorted_p[:cutoff])
+    running = np.cumsum(kept)
+    j = int(np.sum(running <= u))          # first running sum that exceeds u
+    return int(order[min(j, cutoff - 1)])
 
 
 # ----------------------------------------------------------------------------

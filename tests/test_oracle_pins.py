@@ -15,7 +15,7 @@ import torch
 
 import q3synth
 from oracle import (OracleModel, attention_rows, greedy_pick, rms_norm, rope_cos_sin,
-                    rope_rotate, silu, swiglu, to_bf16)
+                    rope_rotate, sample_top_p, silu, swiglu, to_bf16)
 from scalar_model import scalar_forward_all
 
 RNG = np.random.default_rng(12345)
@@ -224,6 +224,70 @@ def test_greedy_lowest_index_on_tie_and_rejects_nan():
     assert greedy_pick(np.array([1.0, 3.0, 3.0, 2.0])) == 1
     with pytest.raises(FloatingPointError):
         greedy_pick(np.array([1.0, np.nan]))
+
+
+# ---------------------------------------------------------------- Paso 8: top-p sampling
+def test_top_p_worked_examples():
+    path = os.path.join(os.path.dirname(__file__), "golden", "top_p_worked_examples.json")
+    for case in json.load(open(path))["cases"]:
+        scale = case["temperature"] if case["temperature"] > 0 else 1.0
+        logits = scale * np.log(np.array(case["probs"]))
+        for u, tok in case["draws"]:
+            got = sample_top_p(logits, case["temperature"], case["top_p"], u)
+            assert got == tok, (case["work"], u, got, tok)
+
+
+def _nucleus_by_subsets(probs, top_p):
+    """The page's comment read as a set: the smallest set of tokens whose total
+    probability reaches top_p (among sets of that size, the heaviest), found by
+    enumerating every subset of a tiny vocabulary."""
+    V = len(probs)
+    best = None
+    for mask in range(1, 1 << V):
+        ids = [i for i in range(V) if mask >> i & 1]
+        mass = sum(probs[i] for i in ids)
+        if mass >= top_p or mask == (1 << V) - 1:
+            key = (len(ids), -mass)
+            if best is None or key < best[0]:
+                best = (key, ids)
+    return best[1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_p_nucleus_is_smallest_heaviest_set_and_draw_frequencies(seed):
+    rng = np.random.default_rng(seed)
+    V = 7
+    logits = rng.standard_normal(V) * 2.0
+    T = [0.5, 1.0, 1.7][seed % 3]
+    e = np.exp(logits / T - np.max(logits / T))
+    probs = e / e.sum()
+    for top_p in (0.3, 0.6, 0.9, 0.99):
+        nucleus = _nucleus_by_subsets(list(probs), top_p)
+        # inverse transform on a fine regular grid of u: each kept token is
+        # drawn in proportion to its renormalised probability, the rest never
+        N = 4000
+        counts = np.zeros(V)
+        for k in range(N):
+            counts[sample_top_p(logits, T, top_p, (k + 0.5) / N)] += 1
+        want = np.zeros(V)
+        want[nucleus] = probs[nucleus] / probs[nucleus].sum()
+        np.testing.assert_allclose(counts / N, want, atol=1.5 / N)
+
+
+def test_top_p_shift_and_temperature_invariance():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal(300) * 3
+    for u in rng.random(40):
+        a = sample_top_p(logits, 0.8, 0.9, u)
+        assert a == sample_top_p(logits + 123.0, 0.8, 0.9, u)
+        assert a == sample_top_p(logits / 0.8, 1.0, 0.9, u)
+
+
+def test_top_p_rejects_nonfinite_and_bad_u():
+    with pytest.raises(FloatingPointError):
+        sample_top_p(np.array([0.0, np.nan]), 1.0, 0.9, 0.5)
+    with pytest.raises(ValueError):
+        sample_top_p(np.array([0.0, 1.0]), 1.0, 0.9, 1.0)
 
 
 # ---------------------------------------------------------------- whole model
