@@ -37,6 +37,13 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
 // rope_append writes the same staging when given one.
 hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
                              uint16_t* vstage, hipStream_t s);
+// ---------------------------------------------------------------- k_sample.hip
+// Temperature + top-p sampling of rows 0..n-1 (temperature 0: greedy pick).
+// uniform[r] in [0, 1) drives row r's draw; ws holds sample_workspace_bytes(n)
+// bytes (rows are processed 64 at a time).
+size_t sample_workspace_bytes(int n_rows);
+hipError_t sample_top_p(const float* logits, int64_t ld, int n, int V, float temperature, float top_p,
+                        const float* uniform, int32_t* next, uint32_t* err, void* ws, hipStream_t s);
 hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
                        uint32_t* err, hipStream_t s);
 // Reduce per-block (max, index) partials of EPI_ARGMAX into next[m], then

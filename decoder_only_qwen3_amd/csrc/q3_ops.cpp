@@ -345,6 +345,24 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
   return Q3_OK;
 }
 
+size_t q3op_sample_workspace_bytes(int32_t n_rows) { return sample_workspace_bytes(n_rows); }
+
+q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab, int64_t ld, float temperature,
+                            float top_p, const float* d_uniform, int32_t* d_next, uint32_t* d_err, void* d_ws,
+                            size_t ws_bytes, void* stream) {
+  if (n_rows < 0 || vocab < 1 || ld < vocab) return op_fail(Q3_E_ARG, "bad shape");
+  if (temperature != 0.f && n_rows > 0 && (!d_ws || ws_bytes < sample_workspace_bytes(n_rows)))
+    return op_fail(Q3_E_ARG, "workspace too small");
+  if (n_rows > 0 && (!d_logits || !d_next || !d_err)) return op_fail(Q3_E_ARG, "NULL pointer");
+  if (!std::isfinite(temperature) || (temperature != 0.f && temperature < 1e-30f))
+    return op_fail(Q3_E_ARG, "temperature must be 0 or a finite value >= 1e-30");
+  if (!std::isfinite(top_p)) return op_fail(Q3_E_ARG, "top_p must be finite");
+  if (temperature != 0.f && n_rows > 0 && !d_uniform) return op_fail(Q3_E_ARG, "sampling needs d_uniform");
+  OP_TRY(sample_top_p(d_logits, ld, n_rows, vocab, temperature, top_p, d_uniform, d_next, d_err, d_ws,
+                      (hipStream_t)stream));
+  return Q3_OK;
+}
+
 size_t q3op_decode_attn_fused_workspace_bytes(int32_t n_seqs, int32_t n_q, int32_t smax, int32_t max_pos) {
   return al(n_seqs * sizeof(SeqState)) + 2 * al((size_t)max_pos * 64 * 4) +
          al((size_t)n_seqs * n_q * (smax > 0 ? smax : 64) * 130 * 4) + al((size_t)n_seqs * n_q * 4);

@@ -52,8 +52,8 @@ struct WeightLayout {
 };
 
 struct WsLayout {
-  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, vstage, state,
-      err, total;
+  size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, vstage, sample,
+      state, err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
   int64_t vstage_cap;  // keys per kv head of the fp16 value staging
   int amax_blocks;
@@ -159,6 +159,7 @@ WsLayout ws_layout(const q3_config& c) {
   // one continued sequence of up to max_positions
   W.vstage_cap = std::max<int64_t>(R, c.max_positions) + 64 * Q3_MAX_BATCH + 64;
   W.vstage = take(c.dtype == BF16 ? (size_t)W.vstage_cap * c.n_kv_heads * 128 * 2 : 16);
+  W.sample = take(sample_workspace_bytes(Q3_MAX_BATCH));  // top-p sampling, 64 rows at a time
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -788,6 +789,23 @@ q3_status q3_decode_step(q3_model* m, int32_t n, const int32_t* h_slots, const i
     if (st != Q3_OK) return st;
   }
   for (int b = 0; b < n; ++b) m->slots[h_slots[b]].len += 1;
+  g_err.clear();
+  return Q3_OK;
+}
+
+q3_status q3_sample(q3_model* m, int32_t n_rows, const float* d_logits, int64_t ld, float temperature,
+                    float top_p, const float* d_uniform, int32_t* d_next, void* stream) {
+  q3_status st;
+  if (!ready(m, &st)) return st;
+  const int V = (int)m->cfg.vocab;
+  if (n_rows < 0 || (n_rows > 0 && (!d_logits || !d_next))) return fail(Q3_E_ARG, "bad rows or NULL pointer");
+  if (ld < V) return fail(Q3_E_ARG, "ld smaller than the vocabulary");
+  if (!std::isfinite(temperature) || (temperature != 0.f && temperature < 1e-30f))
+    return fail(Q3_E_ARG, "temperature must be 0 or a finite value >= 1e-30");
+  if (!std::isfinite(top_p)) return fail(Q3_E_ARG, "top_p must be finite");
+  if (temperature != 0.f && n_rows > 0 && !d_uniform) return fail(Q3_E_ARG, "sampling needs d_uniform");
+  HIP_TRY(sample_top_p(d_logits, ld, n_rows, V, temperature, top_p, d_uniform, d_next, m->err(),
+                       m->WS(m->wsl.sample), (hipStream_t)stream));
   g_err.clear();
   return Q3_OK;
 }

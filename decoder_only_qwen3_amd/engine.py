@@ -144,6 +144,18 @@ class Q3Model:
         self.decode_raw(slots, tokens, logits, nxt)
         return logits, nxt
 
+    def sample(self, logits: torch.Tensor, temperature: float, top_p: float,
+               uniform: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Temperature + top-p token per logit row (q3_sample); `uniform`
+        holds one float32 in [0, 1) per row (unused at temperature 0)."""
+        n = logits.shape[0]
+        with torch.cuda.stream(self.stream):
+            nxt = torch.empty(n, dtype=torch.int32, device=self.device)
+        check(self.lib.q3_sample(self.handle, n, logits.data_ptr(), logits.stride(0), float(temperature),
+                                 float(top_p), uniform.data_ptr() if uniform is not None else None,
+                                 nxt.data_ptr(), self.sh))
+        return nxt
+
     def synchronize(self) -> None:
         self.stream.synchronize()
 

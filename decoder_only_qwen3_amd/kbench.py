@@ -144,6 +144,24 @@ def fused_attn_case(lib, name, lens, reps, stream, smax):
             "bytes": byts}
 
 
+def sample_case(lib, name, n, reps, stream, scale=1.0):
+    """Temperature + top-p sampling of n vocabulary-wide logit rows (T 0.8,
+    top_p 0.95); bytes = one read of the logits."""
+    logits = torch.randn((n, V), dtype=torch.float32, device="cuda:0") * scale
+    u = torch.rand(n, dtype=torch.float32, device="cuda:0")
+    nxt = torch.empty(n, dtype=torch.int32, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(lib.q3op_sample_workspace_bytes(n), dtype=torch.uint8, device="cuda:0")
+
+    def fn():
+        _lib.check(lib.q3op_sample_top_p(logits.data_ptr(), n, V, V, 0.8, 0.95, u.data_ptr(), nxt.data_ptr(),
+                                         err.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream))
+    us = _time(fn, reps, stream)
+    byts = n * V * 4
+    return {"kernel": name, "rows": n, "us": round(us, 2), "bytes": byts, "GBs": round(byts / us / 1e3, 1),
+            "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
+
+
 class ARGS:  # command-line settings the cases read
     attn_smax = 0
 
@@ -184,6 +202,9 @@ CASES = {
     "gemm_o_4k": lambda lib, r, s: linear_case(lib, "gemm_o_4k", 1, 4096, H, Q, r, s, kernel=0),
     "gemm_gate_up_4k": lambda lib, r, s: linear_case(lib, "gemm_gate_up_4k", 2, 4096, 2 * I, H, r, s, kernel=0),
     "gemm_down_4k": lambda lib, r, s: linear_case(lib, "gemm_down_4k", 1, 4096, H, I, r, s, kernel=0),
+    "sample_b1": lambda lib, r, s: sample_case(lib, "sample_b1", 1, r, s),
+    "sample_b64": lambda lib, r, s: sample_case(lib, "sample_b64", 64, r, s),
+    "sample_b64_flat": lambda lib, r, s: sample_case(lib, "sample_b64_flat", 64, r, s, scale=0.01),
     "flash_512": lambda lib, r, s: attention_case(lib, "flash_512", 0, 512, 1, r, s),
     "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
     "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),

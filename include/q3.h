@@ -174,6 +174,27 @@ q3_status q3_decode_step(q3_model* m, int32_t n_seqs, const int32_t* h_slots,
                          const int32_t* d_tokens, float* d_logits, int32_t* d_next,
                          void* stream);
 
+/* Temperature + top-p sampling (Paso 8) of n_rows logit rows, e.g. the
+ * d_logits of q3_decode_step or q3_prefill; its d_next stays the greedy pick,
+ * this call writes the sampled token of row r to d_next[r].
+ *   d_logits:    float [n_rows][ld], ld >= vocab; columns 0..vocab-1 used.
+ *   temperature: 0 = greedy (largest logit, lowest ID on ties); otherwise a
+ *                finite value >= 1e-30 dividing the logits before the softmax.
+ *   top_p:       finite; the kept set is the shortest run of tokens, in order
+ *                of decreasing probability (equal probabilities by increasing
+ *                ID), whose running sum reaches top_p (<= 0: the top token;
+ *                >= 1: every token).
+ *   d_uniform:   float [n_rows], one uniform number in [0, 1) per row (values
+ *                outside are clamped); the sampled token is the kept token
+ *                whose renormalised running sum, in the same order, first
+ *                exceeds it.  Unused (may be NULL) when temperature is 0.
+ * Probabilities are computed in float32 (exp of the shifted logits), their
+ * sums exactly on a 2^-40 fixed-point grid, so the result is deterministic.
+ * A row with a non-finite logit yields token 0 and raises error bit 2.
+ * Queued on `stream`; reads no model state besides the vocabulary size. */
+q3_status q3_sample(q3_model* m, int32_t n_rows, const float* d_logits, int64_t ld, float temperature,
+                    float top_p, const float* d_uniform, int32_t* d_next, void* stream);
+
 /* Options. */
 #define Q3_OPT_DECODE_GRAPH 1  /* value 0/1: record decode steps as HIP graphs (default 1) */
 q3_status q3_set_option(q3_model* m, int32_t option, int64_t value);

@@ -120,6 +120,17 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
                                  const float* d_kn, float eps, double theta, int32_t max_pos, int32_t smax,
                                  void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* Paso 8 sampling of n_rows logit rows of width `vocab` (stride ld): the
+ * same computation as q3_sample in q3.h, for any vocabulary size.  d_err is a
+ * device word that receives error bit 2 for a row with a non-finite logit.
+ * d_ws: q3op_sample_workspace_bytes(n_rows) bytes (about 0.6 MB per row, for
+ * at most 64 rows; larger calls run 64 rows at a time), unused at
+ * temperature 0. */
+size_t q3op_sample_workspace_bytes(int32_t n_rows);
+q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab, int64_t ld, float temperature,
+                            float top_p, const float* d_uniform, int32_t* d_next, uint32_t* d_err, void* d_ws,
+                            size_t ws_bytes, void* stream);
+
 /* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
  * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,

@@ -72,3 +72,25 @@ def ops():
 def call(status):
     from decoder_only_qwen3_amd import _lib
     _lib.check(status)
+
+
+# ---------------------------------------------------------------- Paso 8 sampling
+def sample_agrees(logits, temperature, top_p, u, gpu_token, eps=1e-5):
+    """(ok, near_tie): the GPU's sampled token equals the oracle's, or differs
+    only where a decision of the oracle sits within eps of its threshold (a
+    running sum within eps of top_p, the uniform within eps of a renormalised
+    running sum) or where two weights are equal to float32 precision."""
+    from oracle import sample_top_p
+    logits = np.asarray(logits, dtype=np.float64)
+    ref = sample_top_p(logits, temperature, top_p, u)
+    if gpu_token == ref:
+        return True, False
+    for dp in (-eps, 0.0, eps):
+        for du in (-eps, 0.0, eps):
+            uu = min(max(u + du, 0.0), 1.0 - 1e-12)
+            if sample_top_p(logits, temperature, top_p + dp, uu) == gpu_token:
+                return True, True
+    z = logits / temperature
+    if abs(z[gpu_token] - z[ref]) < 1e-6 * max(1.0, abs(z[ref])):
+        return True, True
+    return False, False

@@ -269,3 +269,33 @@ def test_prefill_rejects_overflowing_continuation(bf16_two_layer):
     assert "CAPACITY" in str(ei.value)
     m.synchronize()
     assert m.seq_length(0) == 60
+
+
+# ---------------------------------------------------------------- Paso 8 sampling
+def test_bf16_decode_then_top_p_sample(bf16_two_layer):
+    """A batched decode step's logits sampled by q3_sample agree with the
+    oracle's sampler on the same logits; temperature 0 gives the step's own
+    greedy token."""
+    from gpu_helpers import sample_agrees
+    d, w = bf16_two_layer
+    m = _model(d, max_slots=8, max_positions=128, max_prefill_tokens=512, kv_tokens=1024)
+    m.load_weights(w)
+    prompts = [q3synth.make_tokens(20 + 7 * i, d.vocab, 90 + i).tolist() for i in range(8)]
+    slots = list(range(8))
+    for s_, p in zip(slots, prompts):
+        m.seq_alloc(s_, 128)
+    _, nxt = m.prefill(slots, prompts)
+    lg, nx = m.decode(slots, nxt)
+    rng = np.random.default_rng(5)
+    with torch.cuda.stream(m.stream):
+        u = torch.from_numpy(rng.random(8).astype(np.float32)).to(m.device)
+    tok = m.sample(lg, 0.8, 0.9, u)
+    greedy = m.sample(lg, 0.0, 0.9)
+    m.synchronize()
+    logits = lg.cpu().numpy()
+    uh = u.cpu().numpy()
+    for r in range(8):
+        ok, _ = sample_agrees(logits[r].astype(np.float64), 0.8, 0.9, float(uh[r]), int(tok[r].item()))
+        assert ok, r
+    np.testing.assert_array_equal(greedy.cpu().numpy(), nx.cpu().numpy())
+    assert m.error_flags() == 0
