@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: decode steps sample (temperature + top-p, q3_sample) instead of the greedy pick")
+    ap.add_argument("--top-p", type=float, default=0.95)
     return ap.parse_args()
 
 
@@ -162,6 +165,10 @@ def main():
             cu = np.concatenate([[0], np.cumsum([len(x) for x in parts])]).astype(np.int32)
             calls.append((cu, torch.from_numpy(np.concatenate(parts)).to(dev)))
         d_tok = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+        d_greedy = torch.zeros(B, dtype=torch.int32, device=dev)
+        # one uniform number per sequence and step, drawn before any timing
+        g = torch.Generator(device=dev).manual_seed(wl.seed)
+        d_unif = torch.rand((max(steps_dec, 1), B), generator=g, device=dev, dtype=torch.float32)
         d_logits = torch.empty((B, d.vocab), dtype=torch.float32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -173,7 +180,12 @@ def main():
             m.prefill_raw(slots, cu, d_prompt, d_logits, d_tok[0])
         e1.record(m.stream)
         for i in range(steps_dec):
-            m.decode_raw(slots, d_tok[i % 2], d_logits, d_tok[(i + 1) % 2])
+            if args.temperature > 0:
+                m.decode_raw(slots, d_tok[i % 2], d_logits, d_greedy)
+                _lib.check(m.lib.q3_sample(m.handle, B, d_logits.data_ptr(), d.vocab, args.temperature, args.top_p,
+                                           d_unif[i].data_ptr(), d_tok[(i + 1) % 2].data_ptr(), m.sh))
+            else:
+                m.decode_raw(slots, d_tok[i % 2], d_logits, d_tok[(i + 1) % 2])
         e2.record(m.stream)
         return e0, e1, e2
 
@@ -260,7 +272,9 @@ def main():
         "data": "synthetic: seeded N(0,0.02) weights (norms 1+N(0,0.1)), uniform random token IDs",
         "config": {"workload": wl.name, "n_layers": d.n_layers, "n_seqs": B, "prompt_tokens": lens if B <= 4 else sum(lens),
                    "decode_steps": steps_dec, "graphs": not args.no_graphs,
-                   **({"prefill_chunk": wl.chunk} if wl.chunk > 0 else {})},
+                   **({"prefill_chunk": wl.chunk} if wl.chunk > 0 else {}),
+                   **({"sampling": {"temperature": args.temperature, "top_p": args.top_p}}
+                      if args.temperature > 0 else {})},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2),
         "prefill_ms": round(float(np.mean(pre_ms)), 3),
