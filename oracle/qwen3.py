@@ -228,6 +228,9 @@ class OracleModel:
     Weights use the page's tensor names; linear weights are (out, in) and apply
     as x @ W^T.  The lm_head is tied to the embedding matrix.
 
+    A weight named "lm_head.weight" (vocab, hidden), when present, is the head;
+    otherwise the head is the embedding matrix.
+
     `contract=True` (bf16 models) rounds to bf16: each RMSNorm output that feeds
     a projection (including the final one before the head), the queries and
     keys after QK-Norm and RoPE, the values, the attention output and the
@@ -330,7 +333,10 @@ class OracleModel:
         if d.n_layers == 0:
             x = x[rows]
         hf = self.rnd(rms_norm(x, self.W("model.norm.weight"), d.rms_eps))
-        return hf @ E.T
+        # Paso 8: the head is tied to the embedding unless the weights carry a
+        # separate lm_head matrix (the page's listing reads one by that name)
+        head = self.W("lm_head.weight") if "lm_head.weight" in self.w else E
+        return hf @ head.T
 
     # -- Paso 9: generation loops ---------------------------------------------
     def generate_greedy(self, prompt: Sequence[int], n_steps: int):

@@ -77,4 +77,5 @@ def scalar_forward_all(d, W, ids):
             new_x.append([x1[i] + dn[i] for i in range(d.hidden)])
         xs = new_x
     wf = L("model.norm.weight")
-    return [_matvec(E, _rmsnorm(xs[t], wf, d.rms_eps)) for t in range(T)]
+    head = L("lm_head.weight") if "lm_head.weight" in W else E
+    return [_matvec(head, _rmsnorm(xs[t], wf, d.rms_eps)) for t in range(T)]

@@ -307,6 +307,22 @@ def test_model_matches_scalar_brute_force(kw):
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
 
 
+def test_untied_head_matches_brute_force_and_reduces_to_tied():
+    d, w = _tiny_model()
+    ids = [3, 96, 0, 41]
+    tied = OracleModel(d, w).forward(ids, OracleModel(d, w).new_cache(4), logit_rows=range(4))
+    same = dict(w, **{"lm_head.weight": w["model.embed_tokens.weight"].copy()})
+    m = OracleModel(d, same)
+    np.testing.assert_array_equal(m.forward(ids, m.new_cache(4), logit_rows=range(4)), tied)
+    rng = np.random.default_rng(8)
+    untied = dict(w, **{"lm_head.weight": (rng.standard_normal(w["model.embed_tokens.weight"].shape) * 0.05)
+                        .astype(np.float32)})
+    m = OracleModel(d, untied)
+    got = m.forward(ids, m.new_cache(4), logit_rows=range(4))
+    np.testing.assert_allclose(got, np.array(scalar_forward_all(d, untied, ids)), rtol=1e-11, atol=1e-13)
+    assert not np.allclose(got, tied)
+
+
 def test_zero_layer_model_is_norm_then_embedding_product():
     d, w = _tiny_model(n_layers=0)
     E = w["model.embed_tokens.weight"].astype(np.float64)
