@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: decode steps sample (temperature + top-p, q3_sample) instead of the greedy pick")
     ap.add_argument("--top-p", type=float, default=0.95)
+    ap.add_argument("--checkpoint-load", action="store_true",
+                    help="also time q3_load_safetensors on the workload's weights written as a safetensors file")
     return ap.parse_args()
 
 
@@ -120,6 +122,26 @@ def cpu_baseline(d, w, prompt, seconds_budget=20.0):
             "sample": f"float64 numpy oracle, {d.n_layers} layers: {n_prompt}-token prefill "
                       f"({t1 - t0:.1f} s incl. one-time float64 weight conversion) then {steps} "
                       f"greedy decode steps timed ({t_dec:.1f} s)"}
+
+
+def checkpoint_load(m, w, d):
+    """Seconds and GB/s of q3_load_safetensors for the weights written as one
+    safetensors file (read back from the page cache: host memory -> HBM)."""
+    import tempfile
+
+    import torch
+    from safetensors.torch import save_file
+    dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    with tempfile.TemporaryDirectory(dir="/tmp") as td:
+        path = os.path.join(td, "model.safetensors")
+        save_file({k: torch.from_numpy(v).to(dt) for k, v in w.items()}, path)
+        size = os.path.getsize(path)
+        m.load_safetensors([path])  # warm: file in the page cache
+        t0 = time.perf_counter()
+        m.load_safetensors([path])
+        sec = time.perf_counter() - t0
+    return {"bytes": size, "seconds": round(sec, 3), "GBs": round(size / sec / 1e9, 2),
+            "source": "page cache"}
 
 
 def main():
@@ -287,6 +309,8 @@ def main():
                      "per_launch_us": round(per_launch_ms * 1e3, 2), "alg_bytes": alg_bytes},
         "host_setup_s": round(t_gen, 1),
     }
+    if args.checkpoint_load:
+        line["checkpoint_load"] = checkpoint_load(m, w, d)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, w, prompts[0])
     m.close()

@@ -7,4 +7,4 @@ fallback; constructing a model without the built library raises.
 """
 from ._lib import (LIB_PATH, Q3_BF16, Q3_F32, Q3_MAX_BATCH, Q3Error, EXPORTS,  # noqa: F401
                    load)
-from .engine import Q3Model, make_config  # noqa: F401
+from .engine import Q3Model, checkpoint_validate, make_config  # noqa: F401

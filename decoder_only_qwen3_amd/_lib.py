@@ -21,7 +21,8 @@ EXPORTS = [
     "q3_create", "q3_destroy", "q3_weights_bytes", "q3_kv_bytes", "q3_workspace_bytes",
     "q3_bind_memory", "q3_load_weights", "q3_seq_alloc", "q3_seq_reset", "q3_kv_reset",
     "q3_seq_length", "q3_prefill", "q3_decode_step", "q3_set_option", "q3_error_flags",
-    "q3_last_error", "q3_sample",
+    "q3_last_error", "q3_sample", "q3_checkpoint_validate", "q3_checkpoint_staging_bytes",
+    "q3_load_safetensors",
     "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear", "q3op_norm_linear",
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
     "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
@@ -35,7 +36,7 @@ class q3_config(C.Structure):
         ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
         ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double),
         ("dtype", C.c_int32), ("max_slots", C.c_int32), ("max_positions", C.c_int64),
-        ("max_prefill_tokens", C.c_int64), ("kv_tokens", C.c_int64),
+        ("max_prefill_tokens", C.c_int64), ("kv_tokens", C.c_int64), ("untied_lm_head", C.c_int32),
     ]
 
 
@@ -85,6 +86,9 @@ def load() -> C.CDLL:
         "q3_error_flags": (I32, [P, C.POINTER(C.c_uint32), VP]),
         "q3_last_error": (C.c_char_p, []),
         "q3_sample": (I32, [P, I32, VP, I64, C.c_float, C.c_float, VP, VP, VP]),
+        "q3_checkpoint_validate": (I32, [C.POINTER(q3_config), C.POINTER(C.c_char_p), I32]),
+        "q3_checkpoint_staging_bytes": (SZ, [C.POINTER(q3_config)]),
+        "q3_load_safetensors": (I32, [P, C.POINTER(C.c_char_p), I32, VP, SZ, VP]),
         "q3op_sample_workspace_bytes": (SZ, [I32]),
         "q3op_sample_top_p": (I32, [VP, I32, I32, I64, C.c_float, C.c_float, VP, VP, VP, VP, SZ, VP]),
         "q3op_embed": (I32, [I32, VP, I32, VP, I32, I32, VP, VP, VP]),

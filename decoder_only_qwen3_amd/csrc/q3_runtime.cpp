@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/q3.h"
+#include "checkpoint.h"
 #include "kernels.h"
 
 using namespace q3k;
@@ -47,7 +48,7 @@ struct LayerW {
 };
 
 struct WeightLayout {
-  size_t embed = 0, final_norm = 0, cos_t = 0, sin_t = 0, total = 0;
+  size_t embed = 0, head = 0, final_norm = 0, cos_t = 0, sin_t = 0, total = 0;  // head == embed when tied
   std::vector<LayerW> layers;
 };
 
@@ -85,6 +86,7 @@ bool valid_config(const q3_config* c, std::string* why) {
   if (c->dtype == Q3_F32 && c->max_positions > 8192) return bad("the float32 model supports at most 8192 positions");
   if (c->max_prefill_tokens <= 0 || c->max_prefill_tokens > (1 << 24)) return bad("max_prefill_tokens out of range");
   if (c->kv_tokens <= 0) return bad("kv_tokens must be > 0");
+  if (c->untied_lm_head != 0 && c->untied_lm_head != 1) return bad("untied_lm_head must be 0 or 1");
   return true;
 }
 
@@ -110,6 +112,7 @@ WeightLayout weight_layout(const q3_config& c) {
     L.layers.push_back(w);
   }
   L.final_norm = take(H * 4);
+  L.head = c.untied_lm_head ? take((size_t)c.vocab * H * e) : L.embed;
   L.cos_t = take((size_t)c.max_positions * 64 * 4);
   L.sin_t = take((size_t)c.max_positions * 64 * 4);
   L.total = off;
@@ -370,18 +373,18 @@ q3_status enqueue_head(q3_model* m, const RowMap& rows, int nrows, const SeqBatc
   if (!fuse_norm)
     LAUNCH(rmsnorm(c.dtype, x, nrows, rows, m->W<float>(m->wl.final_norm), c.hidden, c.rms_eps, h, s));
   if (c.dtype == Q3_BF16 && rowgemv_ok(nrows, c.hidden)) {
-    LAUNCH(rowgemv_bf16(EPI_ARGMAX, h, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, nullptr, 0.f, logits,
+    LAUNCH(rowgemv_bf16(EPI_ARGMAX, h, m->W<bf16_t>(m->wl.head), c.vocab, c.hidden, nullptr, 0.f, logits,
                         m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
     LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), rowgemv_argmax_blocks(c.vocab, c.hidden),
                          nrows, d_next, sb, m->state(), m->err(), s));
   } else if (c.dtype == Q3_BF16) {
-    LAUNCH(skinny_bf16(EPI_ARGMAX, fuse_norm ? (const void*)x : h, nrows, m->W<bf16_t>(m->wl.embed), c.vocab,
+    LAUNCH(skinny_bf16(EPI_ARGMAX, fuse_norm ? (const void*)x : h, nrows, m->W<bf16_t>(m->wl.head), c.vocab,
                        c.hidden, fuse_norm ? m->W<float>(m->wl.final_norm) : nullptr, c.rms_eps, logits, c.vocab,
                        m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
     LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), skinny_argmax_blocks(c.vocab),
                          nrows, d_next, sb, m->state(), m->err(), s));
   } else {
-    LAUNCH(gemv_f32(EPI_STORE, (const float*)h, nrows, m->W<float>(m->wl.embed), c.vocab, c.hidden, logits,
+    LAUNCH(gemv_f32(EPI_STORE, (const float*)h, nrows, m->W<float>(m->wl.head), c.vocab, c.hidden, logits,
                     c.vocab, s));
     RowMap ident;
     ident.n = nrows;
@@ -402,6 +405,144 @@ q3_status enqueue_decode(q3_model* m, const SeqBatch& sb, const int32_t* d_token
   RowMap all;
   all.n = -1;
   return enqueue_head(m, all, B, sb, d_logits, d_next, s);
+}
+
+// ------------------------------------------------------------- weights
+// Where a named tensor goes, and its shape (cols < 0: a vector).
+struct TensorSlot {
+  std::string kind;
+  int layer = -1;
+  int64_t rows = -1, cols = -1;
+};
+
+bool classify_tensor(const q3_config& c, const std::string& name, TensorSlot* ts, std::string* why) {
+  const int64_t H = c.hidden, Q = (int64_t)c.n_q_heads * 128, KVW = (int64_t)c.n_kv_heads * 128, I = c.ffn;
+  auto set = [&](const char* kind, int64_t r, int64_t k) {
+    ts->kind = kind;
+    ts->rows = r;
+    ts->cols = k;
+    return true;
+  };
+  if (name == "model.embed_tokens.weight") return set("embed", c.vocab, H);
+  if (name == "model.norm.weight") return set("final_norm", H, -1);
+  if (name == "lm_head.weight") {
+    if (!c.untied_lm_head) {
+      *why = "lm_head.weight given but the model ties its head to the embedding (untied_lm_head = 0)";
+      return false;
+    }
+    return set("head", c.vocab, H);
+  }
+  int li = -1;
+  char rest[128] = {0};
+  if (std::sscanf(name.c_str(), "model.layers.%d.%127s", &li, rest) != 2 || li < 0 || li >= c.n_layers) {
+    *why = "unknown tensor " + name;
+    return false;
+  }
+  ts->layer = li;
+  const std::string tail = rest;
+  if (tail == "self_attn.q_proj.weight") return set("q", Q, H);
+  if (tail == "self_attn.k_proj.weight") return set("k", KVW, H);
+  if (tail == "self_attn.v_proj.weight") return set("v", KVW, H);
+  if (tail == "self_attn.o_proj.weight") return set("o", H, Q);
+  if (tail == "self_attn.q_norm.weight") return set("qn", 128, -1);
+  if (tail == "self_attn.k_norm.weight") return set("kn", 128, -1);
+  if (tail == "input_layernorm.weight") return set("in", H, -1);
+  if (tail == "post_attention_layernorm.weight") return set("post", H, -1);
+  if (tail == "mlp.gate_proj.weight") return set("gate", I, H);
+  if (tail == "mlp.up_proj.weight") return set("up", I, H);
+  if (tail == "mlp.down_proj.weight") return set("down", H, I);
+  *why = "unknown tensor " + name;
+  return false;
+}
+
+size_t expected_tensors(const q3_config& c) { return 2 + (size_t)c.n_layers * 11 + (c.untied_lm_head ? 1 : 0); }
+
+// Copies one tensor (device or host memory, the model's dtype, row-major as
+// named) into the model's layout: q/k/v stacked, gate/up interleaved in runs
+// of 16 rows, norm weights widened to float32.
+hipError_t place_tensor(q3_model* m, const TensorSlot& ts, const void* data, hipStream_t s) {
+  const q3_config& c = m->cfg;
+  const int64_t H = c.hidden, Q = (int64_t)c.n_q_heads * 128, KVW = (int64_t)c.n_kv_heads * 128, I = c.ffn;
+  const size_t e = esz(c);
+  const char* src = (const char*)data;
+  auto copy = [&](size_t dst_off, size_t bytes) { return hipMemcpyAsync(m->W(dst_off), src, bytes, hipMemcpyDefault, s); };
+  auto norm = [&](size_t dst_off, int64_t len) {
+    if (c.dtype == Q3_BF16) return widen_bf16((const bf16_t*)src, m->W<float>(dst_off), len, s);
+    return hipMemcpyAsync(m->W(dst_off), src, len * 4, hipMemcpyDefault, s);
+  };
+  const std::string& k = ts.kind;
+  if (k == "embed") return copy(m->wl.embed, (size_t)c.vocab * H * e);
+  if (k == "head") return copy(m->wl.head, (size_t)c.vocab * H * e);
+  if (k == "final_norm") return norm(m->wl.final_norm, H);
+  const LayerW& lw = m->wl.layers[ts.layer];
+  if (k == "q") return copy(lw.qkv, Q * H * e);
+  if (k == "k") return copy(lw.qkv + Q * H * e, KVW * H * e);
+  if (k == "v") return copy(lw.qkv + (Q + KVW) * H * e, KVW * H * e);
+  if (k == "o") return copy(lw.o, H * Q * e);
+  if (k == "down") return copy(lw.d, H * I * e);
+  if (k == "gate" || k == "up") {
+    // runs of 16 rows: [gate 16 | up 16] [gate 16 | up 16] ...
+    const size_t run = 16 * H * e;
+    const size_t dst = lw.gu + (k == "up" ? run : 0);
+    return hipMemcpy2DAsync(m->W(dst), 2 * run, src, run, run, I / 16, hipMemcpyDefault, s);
+  }
+  if (k == "qn") return norm(lw.qn, 128);
+  if (k == "kn") return norm(lw.kn, 128);
+  if (k == "in") return norm(lw.in_norm, H);
+  if (k == "post") return norm(lw.post_norm, H);
+  return hipErrorInvalidValue;
+}
+
+// A tensor of a checkpoint file and where it goes.
+struct CkptJob {
+  int file, tensor;
+  TensorSlot slot;
+};
+
+// Reads the headers of the checkpoint files and checks them against the
+// model: every expected tensor exactly once across the files, no other
+// tensor, shapes as named, stored in the model's dtype (BF16 or F32).
+q3_status plan_checkpoint(const q3_config& c, const char* const* paths, int32_t n_paths, std::vector<StFile>* files,
+                          std::vector<CkptJob>* jobs) {
+  if (!paths || n_paths <= 0) return fail(Q3_E_ARG, "no checkpoint files");
+  const std::string want = c.dtype == Q3_BF16 ? "BF16" : "F32";
+  std::map<std::string, int> seen;
+  files->resize(n_paths);
+  for (int fi = 0; fi < n_paths; ++fi) {
+    if (!paths[fi]) return fail(Q3_E_ARG, "NULL checkpoint path");
+    std::string err;
+    if (!st_read_header(paths[fi], &(*files)[fi], &err)) return fail(Q3_E_ARG, err);
+    const auto& ts = (*files)[fi].tensors;
+    for (int ti = 0; ti < (int)ts.size(); ++ti) {
+      const StTensor& t = ts[ti];
+      if (seen.count(t.name)) return fail(Q3_E_ARG, "tensor " + t.name + " appears twice");
+      seen[t.name] = fi;
+      TensorSlot slot;
+      std::string why;
+      if (!classify_tensor(c, t.name, &slot, &why)) return fail(Q3_E_ARG, why);
+      if (t.dtype != want)
+        return fail(Q3_E_UNSUPPORTED, t.name + ": stored as " + t.dtype + ", the model needs " + want);
+      const bool ok = slot.cols < 0 ? (t.shape.size() == 1 && t.shape[0] == slot.rows)
+                                    : (t.shape.size() == 2 && t.shape[0] == slot.rows && t.shape[1] == slot.cols);
+      if (!ok) return fail(Q3_E_ARG, t.name + ": wrong shape");
+      jobs->push_back({fi, ti, slot});
+    }
+  }
+  if (jobs->size() != expected_tensors(c)) {
+    // name the first missing tensor
+    std::vector<std::string> names = {"model.embed_tokens.weight", "model.norm.weight"};
+    if (c.untied_lm_head) names.push_back("lm_head.weight");
+    static const char* tails[] = {"self_attn.q_proj.weight", "self_attn.k_proj.weight", "self_attn.v_proj.weight",
+                                  "self_attn.o_proj.weight", "self_attn.q_norm.weight", "self_attn.k_norm.weight",
+                                  "input_layernorm.weight", "post_attention_layernorm.weight",
+                                  "mlp.gate_proj.weight", "mlp.up_proj.weight", "mlp.down_proj.weight"};
+    for (int l = 0; l < c.n_layers; ++l)
+      for (const char* t : tails) names.push_back("model.layers." + std::to_string(l) + "." + t);
+    for (const auto& nm : names)
+      if (!seen.count(nm)) return fail(Q3_E_ARG, "checkpoint lacks " + nm);
+    return fail(Q3_E_ARG, "unexpected tensor count");
+  }
+  return Q3_OK;
 }
 
 }  // namespace
@@ -494,86 +635,132 @@ q3_status q3_load_weights(q3_model* m, const q3_tensor* t, int32_t n, void* stre
   if (!t || n <= 0) return fail(Q3_E_ARG, "no tensors");
   const q3_config& c = m->cfg;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t H = c.hidden, Q = (int64_t)c.n_q_heads * 128, KVW = (int64_t)c.n_kv_heads * 128, I = c.ffn;
-  const size_t e = esz(c);
   m->loaded = false;
   m->drop_graphs();
   std::map<std::string, int> seen;
   // Validate everything before the first copy.
-  struct Job { int idx; std::string kind; int layer; };
-  std::vector<Job> jobs;
+  std::vector<std::pair<int, TensorSlot>> jobs;
   for (int i = 0; i < n; ++i) {
     if (!t[i].name || !t[i].data) return fail(Q3_E_ARG, "tensor with NULL name or data");
     const std::string name = t[i].name;
     if (seen.count(name)) return fail(Q3_E_ARG, "duplicate tensor " + name);
     seen[name] = i;
     if (t[i].dtype != c.dtype) return fail(Q3_E_ARG, name + ": dtype differs from the model's");
-    int64_t r = -1, k = -1;
-    std::string kind;
-    int layer = -1;
-    if (name == "model.embed_tokens.weight") { kind = "embed"; r = c.vocab; k = H; }
-    else if (name == "model.norm.weight") { kind = "final_norm"; r = H; }
-    else {
-      int li = -1;
-      char rest[128] = {0};
-      if (std::sscanf(name.c_str(), "model.layers.%d.%127s", &li, rest) != 2 || li < 0 || li >= c.n_layers)
-        return fail(Q3_E_ARG, "unknown tensor " + name);
-      layer = li;
-      const std::string tail = rest;
-      if (tail == "self_attn.q_proj.weight") { kind = "q"; r = Q; k = H; }
-      else if (tail == "self_attn.k_proj.weight") { kind = "k"; r = KVW; k = H; }
-      else if (tail == "self_attn.v_proj.weight") { kind = "v"; r = KVW; k = H; }
-      else if (tail == "self_attn.o_proj.weight") { kind = "o"; r = H; k = Q; }
-      else if (tail == "self_attn.q_norm.weight") { kind = "qn"; r = 128; }
-      else if (tail == "self_attn.k_norm.weight") { kind = "kn"; r = 128; }
-      else if (tail == "input_layernorm.weight") { kind = "in"; r = H; }
-      else if (tail == "post_attention_layernorm.weight") { kind = "post"; r = H; }
-      else if (tail == "mlp.gate_proj.weight") { kind = "gate"; r = I; k = H; }
-      else if (tail == "mlp.up_proj.weight") { kind = "up"; r = I; k = H; }
-      else if (tail == "mlp.down_proj.weight") { kind = "down"; r = H; k = I; }
-      else return fail(Q3_E_ARG, "unknown tensor " + name);
-    }
-    const bool ok = (k < 0) ? (t[i].ndim == 1 && t[i].shape[0] == r)
-                            : (t[i].ndim == 2 && t[i].shape[0] == r && t[i].shape[1] == k);
+    TensorSlot ts;
+    std::string why;
+    if (!classify_tensor(c, name, &ts, &why)) return fail(Q3_E_ARG, why);
+    const bool ok = (ts.cols < 0) ? (t[i].ndim == 1 && t[i].shape[0] == ts.rows)
+                                  : (t[i].ndim == 2 && t[i].shape[0] == ts.rows && t[i].shape[1] == ts.cols);
     if (!ok) return fail(Q3_E_ARG, name + ": wrong shape");
-    jobs.push_back({i, kind, layer});
+    jobs.push_back({i, ts});
   }
-  const size_t expect = 2 + (size_t)c.n_layers * 11;
-  if (jobs.size() != expect) return fail(Q3_E_ARG, "expected " + std::to_string(expect) + " tensors");
-  for (const Job& j : jobs) {
-    const q3_tensor& tt = t[j.idx];
-    const char* src = (const char*)tt.data;
-    auto copy = [&](size_t dst_off, size_t bytes) {
-      return hipMemcpyAsync(m->W(dst_off), src, bytes, hipMemcpyDefault, s);
-    };
-    auto norm = [&](size_t dst_off, int64_t len) {
-      if (c.dtype == Q3_BF16) return widen_bf16((const bf16_t*)src, m->W<float>(dst_off), len, s);
-      return hipMemcpyAsync(m->W(dst_off), src, len * 4, hipMemcpyDefault, s);
-    };
-    hipError_t err = hipSuccess;
-    if (j.kind == "embed") err = copy(m->wl.embed, (size_t)c.vocab * H * e);
-    else if (j.kind == "final_norm") err = norm(m->wl.final_norm, H);
-    else {
-      const LayerW& lw = m->wl.layers[j.layer];
-      if (j.kind == "q") err = copy(lw.qkv, Q * H * e);
-      else if (j.kind == "k") err = copy(lw.qkv + Q * H * e, KVW * H * e);
-      else if (j.kind == "v") err = copy(lw.qkv + (Q + KVW) * H * e, KVW * H * e);
-      else if (j.kind == "o") err = copy(lw.o, H * Q * e);
-      else if (j.kind == "down") err = copy(lw.d, H * I * e);
-      else if (j.kind == "gate" || j.kind == "up") {
-        // runs of 16 rows: [gate 16 | up 16] [gate 16 | up 16] ...
-        const size_t run = 16 * H * e;
-        const size_t dst = lw.gu + (j.kind == "up" ? run : 0);
-        err = hipMemcpy2DAsync(m->W(dst), 2 * run, src, run, run, I / 16, hipMemcpyDefault, s);
-      }
-      else if (j.kind == "qn") err = norm(lw.qn, 128);
-      else if (j.kind == "kn") err = norm(lw.kn, 128);
-      else if (j.kind == "in") err = norm(lw.in_norm, H);
-      else if (j.kind == "post") err = norm(lw.post_norm, H);
-    }
+  if (jobs.size() != expected_tensors(c))
+    return fail(Q3_E_ARG, "expected " + std::to_string(expected_tensors(c)) + " tensors");
+  for (const auto& j : jobs) {
+    const hipError_t err = place_tensor(m, j.second, t[j.first].data, s);
     if (err != hipSuccess) return fail(Q3_E_HIP, std::string("weight copy: ") + hipGetErrorString(err));
   }
   HIP_TRY(hipStreamSynchronize(s));
+  m->loaded = true;
+  g_err.clear();
+  return Q3_OK;
+}
+
+size_t q3_checkpoint_staging_bytes(const q3_config* cfg) {
+  if (!cfg || !valid_config(cfg, nullptr)) return 0;
+  const size_t H = cfg->hidden, Q = (size_t)cfg->n_q_heads * 128, I = cfg->ffn;
+  return std::max({(size_t)cfg->vocab * H, I * H, Q * H}) * esz(*cfg);
+}
+
+q3_status q3_checkpoint_validate(const q3_config* cfg, const char* const* paths, int32_t n_paths) {
+  if (!cfg) return fail(Q3_E_ARG, "config is NULL");
+  std::string why;
+  if (!valid_config(cfg, &why)) return fail(Q3_E_ARG, why);
+  std::vector<CkptJob> jobs;
+  std::vector<StFile> files;
+  const q3_status st = plan_checkpoint(*cfg, paths, n_paths, &files, &jobs);
+  if (st == Q3_OK) g_err.clear();
+  return st;
+}
+
+q3_status q3_load_safetensors(q3_model* m, const char* const* paths, int32_t n_paths, void* d_staging,
+                              size_t staging_bytes, void* stream) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (!m->bound) return fail(Q3_E_STATE, "q3_bind_memory has not been called");
+  const q3_config& c = m->cfg;
+  if (!d_staging || staging_bytes < q3_checkpoint_staging_bytes(&c)) return fail(Q3_E_ARG, "staging buffer too small");
+  std::vector<CkptJob> jobs;
+  std::vector<StFile> files;
+  q3_status st = plan_checkpoint(c, paths, n_paths, &files, &jobs);
+  if (st != Q3_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  m->loaded = false;
+  m->drop_graphs();
+  // Tensor bytes go file -> pinned host chunks -> device staging, then into
+  // place with the same packing as q3_load_weights.  Two pinned chunks
+  // alternate: the file read of one overlaps the copy of the other (an event
+  // per chunk says when it may be refilled); stream order alone keeps the
+  // staging buffer from being refilled before the previous tensor is placed.
+  constexpr size_t kChunk = 32u << 20;
+  struct Chunks {  // released on every path out
+    void* p[2] = {nullptr, nullptr};
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    ~Chunks() {
+      for (int i = 0; i < 2; ++i) {
+        if (ev[i]) (void)hipEventDestroy(ev[i]);
+        if (p[i]) (void)hipHostFree(p[i]);
+      }
+    }
+  } ck;
+  void** pinned = ck.p;
+  hipEvent_t* done_ev = ck.ev;
+  bool in_use[2] = {false, false};
+  for (int i = 0; i < 2; ++i) {
+    HIP_TRY(hipHostMalloc(&pinned[i], kChunk, hipHostMallocDefault));
+    HIP_TRY(hipEventCreateWithFlags(&done_ev[i], hipEventDisableTiming));
+  }
+  st = Q3_OK;
+  int open_file = -1, turn = 0;
+  FILE* f = nullptr;
+  for (const CkptJob& j : jobs) {
+    const StFile& sf = files[j.file];
+    const StTensor& te = sf.tensors[j.tensor];
+    if (j.file != open_file) {
+      if (f) std::fclose(f);
+      f = std::fopen(sf.path.c_str(), "rb");
+      open_file = j.file;
+      if (!f) { st = fail(Q3_E_ARG, sf.path + ": cannot open"); break; }
+    }
+    const uint64_t bytes = te.end - te.begin;
+    if (std::fseek(f, (long)(sf.data_start + te.begin), SEEK_SET) != 0) {
+      st = fail(Q3_E_ARG, sf.path + ": cannot seek to " + te.name);
+      break;
+    }
+    for (uint64_t done = 0; done < bytes && st == Q3_OK;) {
+      const size_t part = (size_t)std::min<uint64_t>(kChunk, bytes - done);
+      hipError_t e = in_use[turn] ? hipEventSynchronize(done_ev[turn]) : hipSuccess;
+      if (e == hipSuccess && std::fread(pinned[turn], 1, part, f) != part) {
+        st = fail(Q3_E_ARG, sf.path + ": short read in " + te.name);
+        break;
+      }
+      if (e == hipSuccess) e = hipMemcpyAsync((char*)d_staging + done, pinned[turn], part, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(done_ev[turn], s);
+      if (e != hipSuccess) st = fail(Q3_E_HIP, std::string("checkpoint copy: ") + hipGetErrorString(e));
+      in_use[turn] = true;
+      turn ^= 1;
+      done += part;
+    }
+    if (st != Q3_OK) break;
+    const hipError_t e = place_tensor(m, j.slot, d_staging, s);
+    if (e != hipSuccess) {
+      st = fail(Q3_E_HIP, std::string("weight copy: ") + hipGetErrorString(e));
+      break;
+    }
+  }
+  const hipError_t es = hipStreamSynchronize(s);  // before the pinned chunks go
+  if (st == Q3_OK && es != hipSuccess) st = fail(Q3_E_HIP, std::string("checkpoint load: ") + hipGetErrorString(es));
+  if (f) std::fclose(f);
+  if (st != Q3_OK) return st;
   m->loaded = true;
   g_err.clear();
   return Q3_OK;
@@ -728,10 +915,10 @@ q3_status q3_prefill(q3_model* m, int32_t n, const int32_t* h_slots, const int32
     LAUNCH(rmsnorm(c.dtype, m->WS<float>(m->wsl.x), (int)T, every, m->W<float>(m->wl.final_norm), c.hidden,
                    c.rms_eps, h, s));
     if (c.dtype == Q3_BF16)
-      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, (int)T, m->W<bf16_t>(m->wl.embed), c.vocab, c.hidden, d_logits,
+      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, (int)T, m->W<bf16_t>(m->wl.head), c.vocab, c.hidden, d_logits,
                        c.vocab, s));
     else
-      LAUNCH(gemv_f32(EPI_STORE, (const float*)h, (int)T, m->W<float>(m->wl.embed), c.vocab, c.hidden, d_logits,
+      LAUNCH(gemv_f32(EPI_STORE, (const float*)h, (int)T, m->W<float>(m->wl.head), c.vocab, c.hidden, d_logits,
                       c.vocab, s));
     LAUNCH(argmax_rows(d_logits, c.vocab, last, c.vocab, d_next, m->err(), s));
     LAUNCH(seq_advance(sb, m->state(), s));

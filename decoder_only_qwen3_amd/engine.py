@@ -16,26 +16,35 @@ from ._lib import Q3_BF16, Q3_F32, check, i32_array, load, q3_config, q3_tensor
 
 
 def make_config(dims, *, max_slots: int, max_positions: int, max_prefill_tokens: int,
-                kv_tokens: int) -> q3_config:
+                kv_tokens: int, untied_lm_head: bool = False) -> q3_config:
     """q3_config from a q3synth.ModelDims-like object plus capacities."""
     return q3_config(
         n_layers=dims.n_layers, hidden=dims.hidden, n_q_heads=dims.n_q_heads,
         n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim, ffn=dims.ffn, vocab=dims.vocab,
         rms_eps=dims.rms_eps, rope_theta=dims.rope_theta,
         dtype=Q3_BF16 if dims.dtype == "bf16" else Q3_F32, max_slots=max_slots,
-        max_positions=max_positions, max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens)
+        max_positions=max_positions, max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens,
+        untied_lm_head=1 if untied_lm_head else 0)
+
+
+def checkpoint_validate(cfg: q3_config, paths: Sequence[str]) -> None:
+    """Check safetensors checkpoint headers against a config (host only)."""
+    arr = (C.c_char_p * len(paths))(*[p.encode() for p in paths])
+    check(load().q3_checkpoint_validate(C.byref(cfg), arr, len(paths)))
 
 
 class Q3Model:
     """One libq3 model handle plus the device memory it borrows."""
 
     def __init__(self, dims, *, max_slots: int, max_positions: int, max_prefill_tokens: int,
-                 kv_tokens: int, device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None):
+                 kv_tokens: int, device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None,
+                 untied_lm_head: bool = False):
         self.lib = load()
         self.dims = dims
         self.device = torch.device(device)
         self.cfg = make_config(dims, max_slots=max_slots, max_positions=max_positions,
-                               max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens)
+                               max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens,
+                               untied_lm_head=untied_lm_head)
         self.handle = C.c_void_p()
         check(self.lib.q3_create(C.byref(self.cfg), C.byref(self.handle)))
         self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
@@ -52,6 +61,16 @@ class Q3Model:
                                       nb[1], self.bufs[2].data_ptr(), nb[2], self.sh))
 
     # ------------------------------------------------------------------ setup
+    def load_safetensors(self, paths: Sequence[str]) -> None:
+        """Load a safetensors checkpoint (one file or shards) into the model."""
+        n = self.lib.q3_checkpoint_staging_bytes(C.byref(self.cfg))
+        with torch.cuda.stream(self.stream):
+            staging = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        arr = (C.c_char_p * len(paths))(*[p.encode() for p in paths])
+        check(self.lib.q3_load_safetensors(self.handle, arr, len(paths), staging.data_ptr(), staging.numel(),
+                                           self.sh))
+        del staging
+
     def load_weights(self, weights: Dict[str, np.ndarray]) -> None:
         """Upload float32 arrays (bf16-valued for a bf16 model) by the page's names."""
         bf = self.cfg.dtype == Q3_BF16

@@ -70,6 +70,8 @@ typedef struct q3_config {
   int64_t max_positions;      /* longest sequence, in tokens (RoPE table rows) */
   int64_t max_prefill_tokens; /* most tokens in one q3_prefill call (workspace sizing) */
   int64_t kv_tokens;          /* KV arena capacity in tokens, summed over slots */
+  int32_t untied_lm_head;     /* 0: the head is the embedding matrix (tied);
+                                 1: a separate "lm_head.weight" (vocab, hidden) */
 } q3_config;
 
 /* A named weight tensor in device memory, stored as the page's listings read
@@ -81,7 +83,8 @@ typedef struct q3_config {
  *   model.layers.{i}.self_attn.{q,k}_norm.weight   (head_dim)
  *   model.layers.{i}.post_attention_layernorm.weight
  *   model.layers.{i}.mlp.{gate,up,down}_proj.weight
- *   model.norm.weight                              (hidden) */
+ *   model.norm.weight                              (hidden)
+ *   lm_head.weight                                 (vocab, hidden); only with untied_lm_head = 1 */
 typedef struct q3_tensor {
   const char* name;
   const void* data;   /* device pointer, contiguous row-major */
@@ -118,6 +121,30 @@ q3_status q3_bind_memory(q3_model* m, void* d_weights, size_t weights_bytes, voi
  * shape and dtype above.  The source tensors may be freed once `stream` has
  * been synchronised. */
 q3_status q3_load_weights(q3_model* m, const q3_tensor* tensors, int32_t n, void* stream);
+
+/* Checkpoints in the safetensors format (one file or shards): an 8-byte
+ * little-endian header length, a JSON header of {name: {dtype, shape,
+ * data_offsets}}, then the tensor bytes.  Tensors carry the names listed at
+ * q3_load_weights ("lm_head.weight" too when untied_lm_head = 1), each exactly
+ * once across the files, stored as BF16 for a Q3_BF16 model or F32 for a
+ * Q3_F32 model.
+ *
+ * q3_checkpoint_validate: reads and checks only the headers against `cfg`
+ * (host only: no device, no model).  Q3_E_ARG names the first problem (an
+ * unreadable or malformed header, an unknown, repeated or missing tensor, a
+ * wrong shape, a byte range outside the file); Q3_E_UNSUPPORTED a dtype other
+ * than the model's.
+ * q3_checkpoint_staging_bytes: size of the device buffer q3_load_safetensors
+ * needs (the largest tensor), 0 for an invalid config.
+ * q3_load_safetensors: validates as above, then streams every tensor through
+ * pinned host memory (allocated and freed by the call) into d_staging and from
+ * there into the model's layout, as q3_load_weights does.  Synchronises
+ * `stream`; d_staging may be freed afterwards.  On an error the model is left
+ * unloaded. */
+q3_status q3_checkpoint_validate(const q3_config* cfg, const char* const* paths, int32_t n_paths);
+size_t q3_checkpoint_staging_bytes(const q3_config* cfg);
+q3_status q3_load_safetensors(q3_model* m, const char* const* paths, int32_t n_paths, void* d_staging,
+                              size_t staging_bytes, void* stream);
 
 /* Give slot `slot` a KV region of `capacity_tokens` (rounded up to 64) from
  * the arena, and empty it.  A slot can be allocated once per arena reset. */
