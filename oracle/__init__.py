@@ -18,5 +18,6 @@ available.
 """
 from .qwen3 import (  # noqa: F401
     OracleModel, KVCache, rms_norm, rope_cos_sin, rope_rotate, attention_rows,
-    silu, swiglu, greedy_pick, sample_top_p, to_bf16,
+    silu, swiglu, greedy_pick, sample_top_p, to_bf16, quantize_affine, dequantize_affine,
+    quantized_weights,
 )

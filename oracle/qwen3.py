@@ -31,7 +31,8 @@ import numpy as np
 
 __all__ = [
     "to_bf16", "rms_norm", "rope_cos_sin", "rope_rotate", "attention_rows",
-    "silu", "swiglu", "greedy_pick", "sample_top_p", "KVCache", "OracleModel",
+    "silu", "swiglu", "greedy_pick", "sample_top_p", "quantize_affine", "dequantize_affine",
+    "quantized_weights", "KVCache", "OracleModel",
 ]
 
 
@@ -204,6 +205,66 @@ def sample_top_p(logits: np.ndarray, temperature: float, top_p: float, u: float)
     running = np.cumsum(kept)
     j = int(np.sum(running <= u))          # first running sum that exceeds u
     return int(order[min(j, cutoff - 1)])
+
+
+# ----------------------------------------------------------------------------
+# Weight-only affine group quantization (Laya MLX performance research,
+# "Cuantización" section: groups of 64 along the input dimension, 8 or 4 bits,
+# fp16 scale and offset per group)
+# ----------------------------------------------------------------------------
+QUANT_GROUP = 64
+LINEAR_SUFFIXES = ("q_proj.weight", "k_proj.weight", "v_proj.weight", "o_proj.weight",
+                   "gate_proj.weight", "up_proj.weight", "down_proj.weight")
+
+
+def quantize_affine(w: np.ndarray, bits: int, group: int = QUANT_GROUP):
+    """Codes q (uint8, one per element), scales s and offsets b (float16, one
+    per group of `group` consecutive elements of a row) with w ~ q*s + b.
+
+    Per group: b is the minimum and s = (max - min) / (2^bits - 1), each
+    rounded to float16; q = clamp(floor((w - b) / s + 1/2), 0, 2^bits - 1),
+    computed in float32 from the float16 values (q = 0 when s is 0).  The page
+    fixes the scheme (affine, per group, fp16 scale and offset); these are the
+    plain formulas for it, and the float32 steps are the precision in which
+    the codes are decided on both sides.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    rows, K = w.shape
+    if K % group != 0:
+        raise ValueError("the row length must be a multiple of the group size")
+    g = w.reshape(rows, K // group, group)
+    mn = g.min(axis=2)
+    mx = g.max(axis=2)
+    levels = np.float32(2 ** bits - 1)
+    s16 = ((mx - mn) / levels).astype(np.float16)
+    b16 = mn.astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    b32 = b16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.floor((g - b32) / s32 + np.float32(0.5))
+    t = np.where(s32 == 0, 0, t)
+    q = np.clip(t, 0, 2 ** bits - 1).astype(np.uint8).reshape(rows, K)
+    return q, s16, b16
+
+
+def dequantize_affine(q: np.ndarray, s: np.ndarray, b: np.ndarray, group: int = QUANT_GROUP) -> np.ndarray:
+    """w' = q * s + b in float64 (exact for float16 s and b)."""
+    rows, K = q.shape
+    g = q.reshape(rows, K // group, group).astype(np.float64)
+    return (g * s.astype(np.float64)[..., None] + b.astype(np.float64)[..., None]).reshape(rows, K)
+
+
+def quantized_weights(weights: Dict[str, np.ndarray], bits: int) -> Dict[str, np.ndarray]:
+    """The weights a weight-only quantized model computes with: every linear
+    projection of the blocks replaced by its dequantized values; embedding,
+    head and norm weights unchanged."""
+    out = {}
+    for name, w in weights.items():
+        if name.startswith("model.layers.") and name.endswith(LINEAR_SUFFIXES):
+            out[name] = dequantize_affine(*quantize_affine(w, bits))
+        else:
+            out[name] = w
+    return out
 
 
 # ----------------------------------------------------------------------------

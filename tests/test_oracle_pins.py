@@ -14,8 +14,9 @@ import pytest
 import torch
 
 import q3synth
-from oracle import (OracleModel, attention_rows, greedy_pick, rms_norm, rope_cos_sin,
-                    rope_rotate, sample_top_p, silu, swiglu, to_bf16)
+from oracle import (OracleModel, attention_rows, dequantize_affine, greedy_pick, quantize_affine,
+                    quantized_weights, rms_norm, rope_cos_sin, rope_rotate, sample_top_p, silu, swiglu,
+                    to_bf16)
 from scalar_model import scalar_forward_all
 
 RNG = np.random.default_rng(12345)
@@ -288,6 +289,69 @@ def test_top_p_rejects_nonfinite_and_bad_u():
         sample_top_p(np.array([0.0, np.nan]), 1.0, 0.9, 0.5)
     with pytest.raises(ValueError):
         sample_top_p(np.array([0.0, 1.0]), 1.0, 0.9, 1.0)
+
+
+# ---------------------------------------------------------------- weight-only quantization
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantizer_reproduces_values_on_its_grid(bits):
+    # rows built as b0 + q * s0 with float16 s0, b0 and both end codes present:
+    # the quantizer must return exactly those codes, scale and offset
+    rng = np.random.default_rng(bits)
+    levels = 2 ** bits - 1
+    s0 = np.float16(2.0 ** -10)
+    b0 = np.float16(-0.125)
+    q0 = rng.integers(0, levels + 1, size=(3, 128))
+    q0[:, 0::64] = 0
+    q0[:, 1::64] = levels
+    w = (q0 * np.float64(s0) + np.float64(b0)).astype(np.float32)
+    q, s, b = quantize_affine(w, bits)
+    np.testing.assert_array_equal(q, q0)
+    assert np.all(s == s0) and np.all(b == b0)
+    np.testing.assert_array_equal(dequantize_affine(q, s, b), w.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantizer_error_within_half_a_step(bits):
+    rng = np.random.default_rng(10 + bits)
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    q, s, b = quantize_affine(w, bits)
+    assert q.max() <= 2 ** bits - 1
+    err = np.abs(dequantize_affine(q, s, b) - w).reshape(16, 8, 64).max(axis=2)
+    g = w.reshape(16, 8, 64)
+    # half a step, plus what the float16 rounding of offset and scale moves
+    bound = 0.5 * s.astype(np.float64) + 2.0 ** -11 * (np.abs(g.min(axis=2)) + np.abs(g.max(axis=2))) * 1.01
+    assert np.all(err <= bound), float(np.max(err - bound))
+
+
+def test_quantizer_constant_group_and_row_independence():
+    w = np.full((2, 64), 0.3, np.float32)
+    w[1] = np.linspace(-1, 1, 64)
+    q, s, b = quantize_affine(w, 8)
+    assert np.all(q[0] == 0) and s[0, 0] == 0 and b[0, 0] == np.float16(0.3)
+    q1, _, _ = quantize_affine(w[1:], 8)
+    np.testing.assert_array_equal(q[1:], q1)
+
+
+def test_quantized_storage_matches_the_page():
+    # bits/8 + 4/64 bytes per parameter at group 64 with float16 scale and
+    # offset: 1.0625 (8-bit) and 0.5625 (4-bit), as the page states
+    N, K = 32, 1024
+    for bits, per in ((8, 1.0625), (4, 0.5625)):
+        q, s, b = quantize_affine(np.zeros((N, K), np.float32), bits)
+        nbytes = q.size * bits / 8 + s.nbytes + b.nbytes
+        assert nbytes / (N * K) == per
+
+
+def test_quantized_weights_touch_only_block_projections():
+    d = q3synth.tiny_dims(dtype="bf16", hidden=64, n_q_heads=2, n_kv_heads=1, head_dim=32, ffn=128)
+    w = {k: q3synth.round_to_bf16(v) for k, v in q3synth.make_weights(d, seed=7).items()}
+    qw = quantized_weights(w, 8)
+    for name, a in w.items():
+        if name.endswith("_proj.weight"):
+            assert not np.array_equal(qw[name], a)
+            np.testing.assert_allclose(qw[name], a, atol=float(np.ptp(a)) / 255)  # within one step
+        else:
+            assert qw[name] is a
 
 
 # ---------------------------------------------------------------- whole model
