@@ -26,7 +26,7 @@ EXPORTS = [
     "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear", "q3op_norm_linear",
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
     "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
-    "q3op_sample_workspace_bytes", "q3op_sample_top_p",
+    "q3op_sample_workspace_bytes", "q3op_sample_top_p", "q3op_quantize", "q3op_dequantize", "q3op_qlinear",
 ]
 
 
@@ -37,6 +37,7 @@ class q3_config(C.Structure):
         ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_double),
         ("dtype", C.c_int32), ("max_slots", C.c_int32), ("max_positions", C.c_int64),
         ("max_prefill_tokens", C.c_int64), ("kv_tokens", C.c_int64), ("untied_lm_head", C.c_int32),
+        ("weight_bits", C.c_int32),
     ]
 
 
@@ -90,6 +91,9 @@ def load() -> C.CDLL:
         "q3_checkpoint_staging_bytes": (SZ, [C.POINTER(q3_config)]),
         "q3_load_safetensors": (I32, [P, C.POINTER(C.c_char_p), I32, VP, SZ, VP]),
         "q3op_sample_workspace_bytes": (SZ, [I32]),
+        "q3op_quantize": (I32, [VP, I32, I32, I32, VP, VP, VP]),
+        "q3op_dequantize": (I32, [VP, VP, I32, I32, I32, VP, VP]),
+        "q3op_qlinear": (I32, [I32, I32, VP, VP, VP, I32, I32, VP, C.c_float, VP, VP]),
         "q3op_sample_top_p": (I32, [VP, I32, I32, I64, C.c_float, C.c_float, VP, VP, VP, VP, SZ, VP]),
         "q3op_embed": (I32, [I32, VP, I32, VP, I32, I32, VP, VP, VP]),
         "q3op_rmsnorm": (I32, [I32, VP, I32, VP, I32, C.c_float, VP, VP]),

@@ -37,6 +37,24 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
 // rope_append writes the same staging when given one.
 hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
                              uint16_t* vstage, hipStream_t s);
+// ---------------------------------------------------------------- k_quant.hip
+// Weight-only affine group quantization (groups of 64 along K, 8 or 4 bits,
+// fp16 scale and offset per group packed in one 32-bit word).
+size_t quant_code_bytes(int rows, int K, int bits);
+size_t quant_sb_bytes(int rows, int K);
+// Quantize bf16 rows [rows][K] into codes/sb at destination row dst_row0 + r
+// (interleave: gate/up runs of 16 rows, up = 0 for gate, 1 for up).
+hipError_t quantize_rows(const bf16_t* src, int rows, int K, int bits, uint8_t* codes, uint32_t* sb, int dst_row0,
+                         int interleave, int up, hipStream_t s);
+// bf16(q * s + b) for every weight of a quantized [N, K] matrix.
+hipError_t dequant_rows(const uint8_t* codes, const uint32_t* sb, int N, int K, int bits, bf16_t* out, hipStream_t s);
+bool qrowgemv_ok(int K);
+// One activation row against a quantized matrix: EPI_STORE / EPI_SWIGLU (with
+// an optional RMSNorm prologue from the float32 residual when gnorm is given)
+// or EPI_RESADD (bf16 activation).
+hipError_t qrowgemv(int epi, int bits, const void* X, const uint8_t* codes, const uint32_t* sb, int N, int K,
+                    const float* gnorm, float eps, void* out, hipStream_t s);
+
 // ---------------------------------------------------------------- k_sample.hip
 // Temperature + top-p sampling of rows 0..n-1 (temperature 0: greedy pick).
 // uniform[r] in [0, 1) drives row r's draw; ws holds sample_workspace_bytes(n)

@@ -345,6 +345,37 @@ q3_status q3op_attention(int32_t kernel, const void* d_q, int32_t n, const int32
   return Q3_OK;
 }
 
+q3_status q3op_quantize(const void* d_w, int32_t rows, int32_t K, int32_t bits, void* d_codes, void* d_sb,
+                        void* stream) {
+  if (rows < 1 || K < 64 || K % 64 != 0 || (bits != 8 && bits != 4)) return op_fail(Q3_E_ARG, "bad shape or bits");
+  if (!d_w || !d_codes || !d_sb) return op_fail(Q3_E_ARG, "NULL pointer");
+  OP_TRY(quantize_rows((const bf16_t*)d_w, rows, K, bits, (uint8_t*)d_codes, (uint32_t*)d_sb, 0, 0, 0,
+                       (hipStream_t)stream));
+  return Q3_OK;
+}
+
+q3_status q3op_dequantize(const void* d_codes, const void* d_sb, int32_t rows, int32_t K, int32_t bits, void* d_out,
+                          void* stream) {
+  if (rows < 1 || K < 64 || K % 64 != 0 || (bits != 8 && bits != 4)) return op_fail(Q3_E_ARG, "bad shape or bits");
+  if (!d_codes || !d_sb || !d_out) return op_fail(Q3_E_ARG, "NULL pointer");
+  OP_TRY(dequant_rows((const uint8_t*)d_codes, (const uint32_t*)d_sb, rows, K, bits, (bf16_t*)d_out,
+                      (hipStream_t)stream));
+  return Q3_OK;
+}
+
+q3_status q3op_qlinear(int32_t bits, int32_t epi, const void* d_x, const void* d_codes, const void* d_sb, int32_t N,
+                       int32_t K, const float* d_gnorm, float eps, void* d_out, void* stream) {
+  if (bits != 8 && bits != 4) return op_fail(Q3_E_ARG, "bits must be 8 or 4");
+  if (!qrowgemv_ok(K) || N < 1) return op_fail(Q3_E_UNSUPPORTED, "K must be 1024, 2048, 3072 or 4096");
+  if (epi != EPI_STORE && epi != EPI_RESADD && epi != EPI_SWIGLU) return op_fail(Q3_E_ARG, "epilogue");
+  if (epi == EPI_SWIGLU && N % 32 != 0) return op_fail(Q3_E_ARG, "SwiGLU needs N % 32 == 0");
+  if (epi == EPI_RESADD && d_gnorm) return op_fail(Q3_E_ARG, "no RMSNorm prologue with the residual epilogue");
+  if (!d_x || !d_codes || !d_sb || !d_out) return op_fail(Q3_E_ARG, "NULL pointer");
+  OP_TRY(qrowgemv(epi, bits, d_x, (const uint8_t*)d_codes, (const uint32_t*)d_sb, N, K, d_gnorm, eps, d_out,
+                  (hipStream_t)stream));
+  return Q3_OK;
+}
+
 size_t q3op_sample_workspace_bytes(int32_t n_rows) { return sample_workspace_bytes(n_rows); }
 
 q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab, int64_t ld, float temperature,

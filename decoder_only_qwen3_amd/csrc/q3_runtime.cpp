@@ -43,7 +43,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct LayerW {
-  size_t qkv, o, gu, d;               // packed projection weights (model dtype)
+  size_t qkv, o, gu, d;               // packed projection weights (model dtype), or their codes
+  size_t qkv_sb = 0, o_sb = 0, gu_sb = 0, d_sb = 0;  // quantized: scale/offset words
   size_t in_norm, post_norm, qn, kn;  // float32
 };
 
@@ -54,7 +55,7 @@ struct WeightLayout {
 
 struct WsLayout {
   size_t x, h, qkv, q, o, m, logits, amax_val, amax_idx, attn_part, attn_cnt, lin_part, lin_cnt, vstage, sample,
-      state, err, total;
+      wdq, state, err, total;
   int64_t rows;        // activation rows (max prefill tokens, at least Q3_MAX_BATCH)
   int64_t vstage_cap;  // keys per kv head of the fp16 value staging
   int amax_blocks;
@@ -87,6 +88,8 @@ bool valid_config(const q3_config* c, std::string* why) {
   if (c->max_prefill_tokens <= 0 || c->max_prefill_tokens > (1 << 24)) return bad("max_prefill_tokens out of range");
   if (c->kv_tokens <= 0) return bad("kv_tokens must be > 0");
   if (c->untied_lm_head != 0 && c->untied_lm_head != 1) return bad("untied_lm_head must be 0 or 1");
+  if (c->weight_bits != 0 && c->weight_bits != 8 && c->weight_bits != 4) return bad("weight_bits must be 0, 8 or 4");
+  if (c->weight_bits != 0 && c->dtype != Q3_BF16) return bad("quantized weights need the bf16 model");
   return true;
 }
 
@@ -99,12 +102,20 @@ WeightLayout weight_layout(const q3_config& c) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L.embed = take((size_t)c.vocab * H * e);
+  const int bits = c.weight_bits;
+  // a projection's weights: bf16, or codes then scale/offset words
+  auto proj = [&](size_t rows, size_t K, size_t* sb) {
+    if (!bits) return take(rows * K * e);
+    const size_t o = take(quant_code_bytes((int)rows, (int)K, bits));
+    *sb = take(quant_sb_bytes((int)rows, (int)K));
+    return o;
+  };
   for (int i = 0; i < c.n_layers; ++i) {
     LayerW w;
-    w.qkv = take((size_t)qkv_rows(c) * H * e);
-    w.o = take(H * Q * e);
-    w.gu = take(2 * I * H * e);
-    w.d = take(H * I * e);
+    w.qkv = proj((size_t)qkv_rows(c), H, &w.qkv_sb);
+    w.o = proj(H, Q, &w.o_sb);
+    w.gu = proj(2 * I, H, &w.gu_sb);
+    w.d = proj(H, I, &w.d_sb);
     w.in_norm = take(H * 4);
     w.post_norm = take(H * 4);
     w.qn = take(128 * 4);
@@ -163,6 +174,9 @@ WsLayout ws_layout(const q3_config& c) {
   W.vstage_cap = std::max<int64_t>(R, c.max_positions) + 64 * Q3_MAX_BATCH + 64;
   W.vstage = take(c.dtype == BF16 ? (size_t)W.vstage_cap * c.n_kv_heads * 128 * 2 : 16);
   W.sample = take(sample_workspace_bytes(Q3_MAX_BATCH));  // top-p sampling, 64 rows at a time
+  // quantized weights: one layer's projections dequantized to bf16 for the
+  // prefill and batched-decode kernels
+  W.wdq = take(c.weight_bits ? ((size_t)qkv_rows(c) * H + H * Q + 3 * I * H) * 2 : 16);
   W.state = take((size_t)c.max_slots * sizeof(SeqState));
   W.err = take(16);
   W.total = off;
@@ -274,27 +288,51 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   }
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.
-  const bool one_h = bf && decode && rowgemv_ok(T, H);
-  const bool one_q = bf && decode && rowgemv_ok(T, Q);
-  const bool one_i = bf && decode && rowgemv_ok(T, I);
+  // Quantized weights: batch-1 decode reads the codes directly (every
+  // projection); other calls dequantize each layer's projections to bf16
+  // first and run the bf16 kernels on that copy.
+  const int bits = c.weight_bits;
+  const bool qone = bits && decode && T == 1 && qrowgemv_ok(H) && qrowgemv_ok(Q) && qrowgemv_ok(I);
+  const bool one_h = !bits && bf && decode && rowgemv_ok(T, H);
+  const bool one_q = !bits && bf && decode && rowgemv_ok(T, Q);
+  const bool one_i = !bits && bf && decode && rowgemv_ok(T, I);
   const bool rows_o = bf && decode && rowdot_ok(T, Q);
   const bool rows_d = bf && decode && rowdot_ok(T, I);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
+    const bf16_t *Wqkv = nullptr, *Wo = nullptr, *Wgu = nullptr, *Wd = nullptr;
+    if (bf && !bits) {
+      Wqkv = m->W<bf16_t>(lw.qkv);
+      Wo = m->W<bf16_t>(lw.o);
+      Wgu = m->W<bf16_t>(lw.gu);
+      Wd = m->W<bf16_t>(lw.d);
+    } else if (bits && !qone) {
+      bf16_t* dq = m->WS<bf16_t>(L.wdq);
+      Wqkv = dq;
+      Wo = Wqkv + (size_t)NQKV * H;
+      Wgu = Wo + (size_t)H * Q;
+      Wd = Wgu + (size_t)2 * I * H;
+      LAUNCH(dequant_rows(m->W<uint8_t>(lw.qkv), m->W<uint32_t>(lw.qkv_sb), NQKV, H, bits, (bf16_t*)Wqkv, s));
+      LAUNCH(dequant_rows(m->W<uint8_t>(lw.o), m->W<uint32_t>(lw.o_sb), H, Q, bits, (bf16_t*)Wo, s));
+      LAUNCH(dequant_rows(m->W<uint8_t>(lw.gu), m->W<uint32_t>(lw.gu_sb), 2 * I, H, bits, (bf16_t*)Wgu, s));
+      LAUNCH(dequant_rows(m->W<uint8_t>(lw.d), m->W<uint32_t>(lw.d_sb), H, I, bits, (bf16_t*)Wd, s));
+    }
     // Paso 3 + Paso 5: normalised input, fused q/k/v projection.  Decode with
     // few rows folds the RMSNorm into the projection kernel's prologue.
-    const bool fuse_norm = bf && decode && (one_h || skinny_norm_fuse(T));
+    const bool fuse_norm = bf && decode && (one_h || qone || skinny_norm_fuse(T));
     if (!fuse_norm) LAUNCH(rmsnorm(c.dtype, x, T, all, m->W<float>(lw.in_norm), H, c.rms_eps, h, s));
     if (!bf) {
       LAUNCH(gemv_f32(EPI_STORE, (const float*)h, T, m->W<float>(lw.qkv), NQKV, H, qkv, NQKV, s));
+    } else if (qone) {
+      LAUNCH(qrowgemv(EPI_STORE, bits, x, m->W<uint8_t>(lw.qkv), m->W<uint32_t>(lw.qkv_sb), NQKV, H,
+                      m->W<float>(lw.in_norm), c.rms_eps, qkv, s));
     } else if (one_h) {
-      LAUNCH(rowgemv_bf16(EPI_STORE, x, m->W<bf16_t>(lw.qkv), NQKV, H, m->W<float>(lw.in_norm), c.rms_eps, qkv,
-                          nullptr, nullptr, s));
+      LAUNCH(rowgemv_bf16(EPI_STORE, x, Wqkv, NQKV, H, m->W<float>(lw.in_norm), c.rms_eps, qkv, nullptr, nullptr, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_STORE, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.qkv), NQKV, H,
+      LAUNCH(skinny_bf16(EPI_STORE, fuse_norm ? (const void*)x : h, T, Wqkv, NQKV, H,
                          fuse_norm ? m->W<float>(lw.in_norm) : nullptr, c.rms_eps, qkv, NQKV, nullptr, nullptr, s));
     } else {
-      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, m->W<bf16_t>(lw.qkv), NQKV, H, qkv, NQKV, s));
+      LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, Wqkv, NQKV, H, qkv, NQKV, s));
     }
     // QK-Norm, RoPE, cache append and attention (Pasos 4-5).  bf16 decode does
     // all of it in one kernel; the other paths append first.
@@ -319,15 +357,17 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     // Output projection + residual (Paso 5 end, Paso 7).
     if (!bf) {
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
+    } else if (qone) {
+      LAUNCH(qrowgemv(EPI_RESADD, bits, ob, m->W<uint8_t>(lw.o), m->W<uint32_t>(lw.o_sb), H, Q, nullptr, 0.f, x, s));
     } else if (one_q) {
-      LAUNCH(rowgemv_bf16(EPI_RESADD, ob, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, nullptr, nullptr, s));
+      LAUNCH(rowgemv_bf16(EPI_RESADD, ob, Wo, H, Q, nullptr, 0.f, x, nullptr, nullptr, s));
     } else if (rows_o) {
-      LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s));
+      LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)ob, T, Wo, H, Q, x, H, s));
     } else if (decode) {
-      LAUNCH(skinny_bf16(EPI_RESADD, ob, T, m->W<bf16_t>(lw.o), H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s,
+      LAUNCH(skinny_bf16(EPI_RESADD, ob, T, Wo, H, Q, nullptr, 0.f, x, H, nullptr, nullptr, s,
                          m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
-      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, m->W<bf16_t>(lw.o), H, Q, x, H, s,
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)ob, T, Wo, H, Q, x, H, s,
                        m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     }
     // SwiGLU MLP + residual (Paso 6, Paso 7).
@@ -335,23 +375,27 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     if (!bf) {
       LAUNCH(gemv_f32(EPI_SWIGLU, (const float*)h, T, m->W<float>(lw.gu), 2 * I, H, mb, I, s));
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)mb, T, m->W<float>(lw.d), H, I, x, H, s));
+    } else if (qone) {
+      LAUNCH(qrowgemv(EPI_SWIGLU, bits, x, m->W<uint8_t>(lw.gu), m->W<uint32_t>(lw.gu_sb), 2 * I, H,
+                      m->W<float>(lw.post_norm), c.rms_eps, mb, s));
+      LAUNCH(qrowgemv(EPI_RESADD, bits, mb, m->W<uint8_t>(lw.d), m->W<uint32_t>(lw.d_sb), H, I, nullptr, 0.f, x, s));
     } else if (decode) {
       if (one_h)
-        LAUNCH(rowgemv_bf16(EPI_SWIGLU, x, m->W<bf16_t>(lw.gu), 2 * I, H, m->W<float>(lw.post_norm), c.rms_eps, mb,
-                            nullptr, nullptr, s));
+        LAUNCH(rowgemv_bf16(EPI_SWIGLU, x, Wgu, 2 * I, H, m->W<float>(lw.post_norm), c.rms_eps, mb, nullptr, nullptr,
+                            s));
       else
-        LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, m->W<bf16_t>(lw.gu), 2 * I, H,
+        LAUNCH(skinny_bf16(EPI_SWIGLU, fuse_norm ? (const void*)x : h, T, Wgu, 2 * I, H,
                            fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps, mb, I, nullptr, nullptr, s));
       if (one_i)
-        LAUNCH(rowgemv_bf16(EPI_RESADD, mb, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, nullptr, nullptr, s));
+        LAUNCH(rowgemv_bf16(EPI_RESADD, mb, Wd, H, I, nullptr, 0.f, x, nullptr, nullptr, s));
       else if (rows_d)
-        LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s));
+        LAUNCH(rowdot_bf16(EPI_RESADD, (const bf16_t*)mb, T, Wd, H, I, x, H, s));
       else
-        LAUNCH(skinny_bf16(EPI_RESADD, mb, T, m->W<bf16_t>(lw.d), H, I, nullptr, 0.f, x, H, nullptr, nullptr, s,
+        LAUNCH(skinny_bf16(EPI_RESADD, mb, T, Wd, H, I, nullptr, 0.f, x, H, nullptr, nullptr, s,
                            m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else {
-      LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, m->W<bf16_t>(lw.gu), 2 * I, H, mb, I, s));
-      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, m->W<bf16_t>(lw.d), H, I, x, H, s,
+      LAUNCH(gemm_bf16(EPI_SWIGLU, (const bf16_t*)h, T, Wgu, 2 * I, H, mb, I, s));
+      LAUNCH(gemm_bf16(EPI_RESADD, (const bf16_t*)mb, T, Wd, H, I, x, H, s,
                        m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     }
   }
@@ -471,6 +515,22 @@ hipError_t place_tensor(q3_model* m, const TensorSlot& ts, const void* data, hip
     return hipMemcpyAsync(m->W(dst_off), src, len * 4, hipMemcpyDefault, s);
   };
   const std::string& k = ts.kind;
+  const int bits = c.weight_bits;
+  if (bits && ts.layer >= 0 && ts.cols > 0) {  // a block projection: quantized from the bf16 source
+    const LayerW& lw = m->wl.layers[ts.layer];
+    const bf16_t* w = (const bf16_t*)data;
+    auto q = [&](size_t codes, size_t sb, int rows, int K, int row0, int inter, int up) {
+      return quantize_rows(w, rows, K, bits, m->W<uint8_t>(codes), m->W<uint32_t>(sb), row0, inter, up, s);
+    };
+    if (k == "q") return q(lw.qkv, lw.qkv_sb, (int)Q, (int)H, 0, 0, 0);
+    if (k == "k") return q(lw.qkv, lw.qkv_sb, (int)KVW, (int)H, (int)Q, 0, 0);
+    if (k == "v") return q(lw.qkv, lw.qkv_sb, (int)KVW, (int)H, (int)(Q + KVW), 0, 0);
+    if (k == "o") return q(lw.o, lw.o_sb, (int)H, (int)Q, 0, 0, 0);
+    if (k == "down") return q(lw.d, lw.d_sb, (int)H, (int)I, 0, 0, 0);
+    if (k == "gate") return q(lw.gu, lw.gu_sb, (int)I, (int)H, 0, 1, 0);
+    if (k == "up") return q(lw.gu, lw.gu_sb, (int)I, (int)H, 0, 1, 1);
+    return hipErrorInvalidValue;
+  }
   if (k == "embed") return copy(m->wl.embed, (size_t)c.vocab * H * e);
   if (k == "head") return copy(m->wl.head, (size_t)c.vocab * H * e);
   if (k == "final_norm") return norm(m->wl.final_norm, H);
@@ -646,6 +706,13 @@ q3_status q3_load_weights(q3_model* m, const q3_tensor* t, int32_t n, void* stre
     if (seen.count(name)) return fail(Q3_E_ARG, "duplicate tensor " + name);
     seen[name] = i;
     if (t[i].dtype != c.dtype) return fail(Q3_E_ARG, name + ": dtype differs from the model's");
+    if (c.weight_bits) {  // the quantizer reads the source on the device
+      hipPointerAttribute_t at;
+      if (hipPointerGetAttributes(&at, t[i].data) != hipSuccess || at.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return fail(Q3_E_ARG, name + ": a quantized model needs its tensors in device memory");
+      }
+    }
     TensorSlot ts;
     std::string why;
     if (!classify_tensor(c, name, &ts, &why)) return fail(Q3_E_ARG, why);

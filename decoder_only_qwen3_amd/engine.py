@@ -16,7 +16,7 @@ from ._lib import Q3_BF16, Q3_F32, check, i32_array, load, q3_config, q3_tensor
 
 
 def make_config(dims, *, max_slots: int, max_positions: int, max_prefill_tokens: int,
-                kv_tokens: int, untied_lm_head: bool = False) -> q3_config:
+                kv_tokens: int, untied_lm_head: bool = False, weight_bits: int = 0) -> q3_config:
     """q3_config from a q3synth.ModelDims-like object plus capacities."""
     return q3_config(
         n_layers=dims.n_layers, hidden=dims.hidden, n_q_heads=dims.n_q_heads,
@@ -24,7 +24,7 @@ def make_config(dims, *, max_slots: int, max_positions: int, max_prefill_tokens:
         rms_eps=dims.rms_eps, rope_theta=dims.rope_theta,
         dtype=Q3_BF16 if dims.dtype == "bf16" else Q3_F32, max_slots=max_slots,
         max_positions=max_positions, max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens,
-        untied_lm_head=1 if untied_lm_head else 0)
+        untied_lm_head=1 if untied_lm_head else 0, weight_bits=weight_bits)
 
 
 def checkpoint_validate(cfg: q3_config, paths: Sequence[str]) -> None:
@@ -38,13 +38,13 @@ class Q3Model:
 
     def __init__(self, dims, *, max_slots: int, max_positions: int, max_prefill_tokens: int,
                  kv_tokens: int, device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None,
-                 untied_lm_head: bool = False):
+                 untied_lm_head: bool = False, weight_bits: int = 0):
         self.lib = load()
         self.dims = dims
         self.device = torch.device(device)
         self.cfg = make_config(dims, max_slots=max_slots, max_positions=max_positions,
                                max_prefill_tokens=max_prefill_tokens, kv_tokens=kv_tokens,
-                               untied_lm_head=untied_lm_head)
+                               untied_lm_head=untied_lm_head, weight_bits=weight_bits)
         self.handle = C.c_void_p()
         check(self.lib.q3_create(C.byref(self.cfg), C.byref(self.handle)))
         self.stream = stream if stream is not None else torch.cuda.Stream(self.device)

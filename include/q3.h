@@ -72,6 +72,14 @@ typedef struct q3_config {
   int64_t kv_tokens;          /* KV arena capacity in tokens, summed over slots */
   int32_t untied_lm_head;     /* 0: the head is the embedding matrix (tied);
                                  1: a separate "lm_head.weight" (vocab, hidden) */
+  int32_t weight_bits;        /* 0: projections in the model dtype; 8 or 4: the
+                                 q/k/v/o/gate/up/down weights of every block
+                                 are stored as affine group codes (groups of
+                                 64 along the input dimension, float16 scale
+                                 and offset per group, w ~ q * s + b), made at
+                                 load time from the bf16 weights (Q3_BF16
+                                 models only; embedding, head and norms stay
+                                 as they are) */
 } q3_config;
 
 /* A named weight tensor in device memory, stored as the page's listings read

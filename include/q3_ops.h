@@ -131,6 +131,27 @@ q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab
                             float top_p, const float* d_uniform, int32_t* d_next, uint32_t* d_err, void* d_ws,
                             size_t ws_bytes, void* stream);
 
+/* Weight-only affine group quantization (the page "Laya MLX performance
+ * research", quantization section): groups of 64 along K, `bits` = 8 or 4.
+ * Codes [rows][K * bits / 8] bytes (4-bit: byte j holds k = 2j in its low
+ * nibble and 2j + 1 in its high nibble); scale/offset words [rows][K / 64],
+ * the float16 scale in the low 16 bits and the float16 offset in the high.
+ * q3op_quantize: from bf16 weights [rows][K] (b = fp16(min), s = fp16((max -
+ * min) / (2^bits - 1)), q = clamp(floor((w - b) / s + 1/2)), all in float32;
+ * q = 0 when s is 0).
+ * q3op_dequantize: bf16(q * s + b) into d_out [rows][K].
+ * q3op_qlinear: one activation row against the quantized W[N,K] (K = 1024 *
+ * 1..4): epi 0 store float32 out[N], 1 add into float32 out[N], 2 SwiGLU on
+ * gate/up rows interleaved in runs of 16 (bf16 out[N/2]).  d_x is bf16 [K], or
+ * with d_gnorm (epi 0 and 2) the float32 residual row normalised in the
+ * kernel: bf16(x * rsqrt(mean(x^2) + eps) * g). */
+q3_status q3op_quantize(const void* d_w, int32_t rows, int32_t K, int32_t bits, void* d_codes, void* d_sb,
+                        void* stream);
+q3_status q3op_dequantize(const void* d_codes, const void* d_sb, int32_t rows, int32_t K, int32_t bits, void* d_out,
+                          void* stream);
+q3_status q3op_qlinear(int32_t bits, int32_t epi, const void* d_x, const void* d_codes, const void* d_sb, int32_t N,
+                       int32_t K, const float* d_gnorm, float eps, void* d_out, void* stream);
+
 /* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
  * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,

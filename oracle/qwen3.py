@@ -255,13 +255,15 @@ def dequantize_affine(q: np.ndarray, s: np.ndarray, b: np.ndarray, group: int = 
 
 
 def quantized_weights(weights: Dict[str, np.ndarray], bits: int) -> Dict[str, np.ndarray]:
-    """The weights a weight-only quantized model computes with: every linear
-    projection of the blocks replaced by its dequantized values; embedding,
-    head and norm weights unchanged."""
+    """The weights a weight-only quantized bf16 model computes with: every
+    linear projection of the blocks replaced by its dequantized values, each
+    rounded to bf16 like every other weight of the bf16 model (the matrix
+    products of the bf16 contract take bf16 operands); embedding, head and
+    norm weights unchanged."""
     out = {}
     for name, w in weights.items():
         if name.startswith("model.layers.") and name.endswith(LINEAR_SUFFIXES):
-            out[name] = dequantize_affine(*quantize_affine(w, bits))
+            out[name] = to_bf16(dequantize_affine(*quantize_affine(w, bits)))
         else:
             out[name] = w
     return out
