@@ -71,19 +71,24 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: decode steps sample (temperature + top-p, q3_sample) instead of the greedy pick")
     ap.add_argument("--top-p", type=float, default=0.95)
+    ap.add_argument("--weight-bits", type=int, default=0, choices=[0, 8, 4],
+                    help="8 or 4: block projections stored as affine group codes (weight-only quantization)")
     ap.add_argument("--checkpoint-load", action="store_true",
                     help="also time q3_load_safetensors on the workload's weights written as a safetensors file")
     return ap.parse_args()
 
 
-def decode_bytes_per_step(d, ctxs):
+def decode_bytes_per_step(d, ctxs, weight_bits=0):
     """Algorithmic HBM bytes of one decode step of len(ctxs) sequences, sequence b
     attending over ctxs[b] keys (its new token included): every weight once, each
-    sequence's cache read, the new keys/values written, one logits row each."""
+    sequence's cache read, the new keys/values written, one logits row each.
+    Quantized projections count bits/8 + 4/64 bytes per weight (codes plus the
+    fp16 scale and offset of each group of 64)."""
     L, H, Q, KV, I, V = d.n_layers, d.hidden, d.n_q_heads * 128, d.n_kv_heads * 128, d.ffn, d.vocab
     e = 2 if d.dtype == "bf16" else 4
     B = len(ctxs)
-    weights = (L * (H * (Q + 2 * KV) + Q * H + 2 * I * H + I * H) + V * H) * e
+    pe = (weight_bits / 8 + 4 / 64) if weight_bits else e
+    weights = L * (H * (Q + 2 * KV) + Q * H + 2 * I * H + I * H) * pe + V * H * e
     norms = (L * (2 * H + 256) + H) * 4
     kv_read = sum(ctxs) * L * 2 * KV * e
     kv_write = B * L * 2 * KV * e
@@ -172,7 +177,8 @@ def main():
     bounds = ([(a, min(a + wl.chunk, lens[0])) for a in range(0, lens[0], wl.chunk)] if wl.chunk > 0
               else [(0, None)])
     max_call = sum(lens) if wl.chunk <= 0 else B * wl.chunk
-    m = Q3Model(d, max_slots=B, max_positions=cap, max_prefill_tokens=max_call, kv_tokens=B * ((cap + 63) // 64 * 64))
+    m = Q3Model(d, max_slots=B, max_positions=cap, max_prefill_tokens=max_call, kv_tokens=B * ((cap + 63) // 64 * 64),
+                weight_bits=args.weight_bits)
     m.load_weights(w)
     if args.no_graphs:
         m.set_graphs(False)
@@ -229,7 +235,7 @@ def main():
     decode_tok_s = B * steps_dec * args.steps / (sum(dec_ms) / 1e3)
 
     # Whole-step decode HBM fraction: algorithmic bytes averaged over the steps.
-    byts = np.mean([decode_bytes_per_step(d, [L + 1 + i for L in lens]) for i in range(steps_dec)])
+    byts = np.mean([decode_bytes_per_step(d, [L + 1 + i for L in lens], args.weight_bits) for i in range(steps_dec)])
     dec_step_s = (sum(dec_ms) / 1e3) / (args.steps * steps_dec)
     decode_hbm = {"bytes_per_step": float(byts), "achieved_GBs": byts / dec_step_s / 1e9,
                   "frac": byts / dec_step_s / 1e9 / HBM_PEAK_GBS}
@@ -296,7 +302,8 @@ def main():
                    "decode_steps": steps_dec, "graphs": not args.no_graphs,
                    **({"prefill_chunk": wl.chunk} if wl.chunk > 0 else {}),
                    **({"sampling": {"temperature": args.temperature, "top_p": args.top_p}}
-                      if args.temperature > 0 else {})},
+                      if args.temperature > 0 else {}),
+                   **({"weight_bits": args.weight_bits} if args.weight_bits else {})},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2),
         "prefill_ms": round(float(np.mean(pre_ms)), 3),

@@ -21,7 +21,14 @@ namespace {
 
 constexpr int kGroup = 64;
 
+typedef __bf16 bf16x2_q __attribute__((ext_vector_type(2)));
+
 Q3_DEV float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+// Two floats -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32;
+// the dequantizer and the GEMV on codes both round this way).
+Q3_DEV uint32_t pack_bf2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_q));
+}
 Q3_DEV float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // One thread per (row, group).  Destination row: dst_row0 + r, or for the
@@ -118,13 +125,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
   u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf2(fmaf((float)q[2 * i], s, b), fmaf((float)q[2 * i + 1], s, b));
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf2_rne(fmaf((float)q[2 * i], s, b), fmaf((float)q[2 * i + 1], s, b));
   *reinterpret_cast<u32x4*>(out + (int64_t)r * K + k0) = o;
 }
 
 Q3_DEV float silu_q(float g) { return g / (1.f + __expf(-g)); }
-
-typedef __bf16 bf16x2_q __attribute__((ext_vector_type(2)));
 
 // One activation row against a quantized W[N,K].  A wavefront owns RW rows;
 // lane l covers k = 16 l + 1024 i (i < KS, K = 1024 KS): 16 codes per load (16
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(256) void qrowgemv_kernel(const void* __restrict__ 
           q0 = (cw[r][i][j >> 3] >> (4 * (j & 7))) & 0xfu;
           q1 = (cw[r][i][j >> 3] >> (4 * ((j + 1) & 7))) & 0xfu;
         }
-        const uint32_t wpair = pack_bf2(fmaf((float)q0, s, b), fmaf((float)q1, s, b));
+        const uint32_t wpair = pack_bf2_rne(fmaf((float)q0, s, b), fmaf((float)q1, s, b));
         const uint32_t apair = ap[i][j >> 1];
         acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_q, wpair),
                                                  __builtin_bit_cast(bf16x2_q, apair), acc[r], false);
@@ -276,6 +281,10 @@ template <int EPI, int BITS, int KS, bool NORM>
 hipError_t launch_q(int rw, dim3 grid, dim3 block, const void* X, const uint8_t* C, const uint32_t* S, int N, int K,
                     const float* g, float eps, void* out, hipStream_t s) {
   switch (rw) {
+    case 1:
+      if constexpr (EPI == EPI_SWIGLU) return hipErrorInvalidValue;  // gate and up rows come in pairs
+      else qrowgemv_kernel<EPI, BITS, KS, 1, NORM><<<grid, block, 0, s>>>(X, C, S, N, K, g, eps, out);
+      break;
     case 2: qrowgemv_kernel<EPI, BITS, KS, 2, NORM><<<grid, block, 0, s>>>(X, C, S, N, K, g, eps, out); break;
     case 4: qrowgemv_kernel<EPI, BITS, KS, 4, NORM><<<grid, block, 0, s>>>(X, C, S, N, K, g, eps, out); break;
     case 8: qrowgemv_kernel<EPI, BITS, KS, 8, NORM><<<grid, block, 0, s>>>(X, C, S, N, K, g, eps, out); break;
@@ -300,13 +309,17 @@ template <int BITS>
 hipError_t qrowgemv_bits(int epi, const void* X, const uint8_t* C, const uint32_t* S, int N, int K,
                          const float* gnorm, float eps, void* out, hipStream_t s) {
   const int KS = K / 1024;
-  // about eight code loads in flight per lane
-  const int rw = KS >= 3 ? 2 : (KS == 2 ? 4 : 8);
+  // Dequantizing costs about three VALU operations per weight, so the rows
+  // are spread thin for many wavefronts and SIMDs; with the RMSNorm prologue
+  // every wavefront also reads the whole activation and norm rows (8 KiB at
+  // K = 1024), so there four rows share that read.
+  const bool norm_in = gnorm != nullptr;
+  const int rw = norm_in ? 4 : 2;
   const int64_t nwaves = ((int64_t)N + rw - 1) / rw;
   int waves = 4;
   while (waves > 1 && (nwaves + waves - 1) / waves < 256) waves >>= 1;
   dim3 grid((unsigned)((nwaves + waves - 1) / waves)), block(64 * waves);
-  const bool norm = gnorm != nullptr;
+  const bool norm = norm_in;
   switch (epi) {
     case EPI_STORE:
       return norm ? launch_qks<EPI_STORE, BITS, true>(KS, rw, grid, block, X, C, S, N, K, gnorm, eps, out, s)

@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import json
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -162,6 +163,30 @@ def sample_case(lib, name, n, reps, stream, scale=1.0):
             "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
 
 
+def qlinear_case(lib, name, bits, epi, N, K, reps, stream, norm=False, pool=32):
+    """Single-row GEMV on quantized weights (codes + fp16 scale/offset per 64),
+    weights cycled through `pool` copies; bytes = codes + scales + activations
+    + outputs."""
+    codes = [torch.randint(0, 256, (N * K * bits // 8,), dtype=torch.uint8, device="cuda:0") for _ in range(pool)]
+    # scale 2^-8 and offset -2^-7 in every group (float16 bits, scale low)
+    word = int(np.array([0x1c00 | (0xa000 << 16)], dtype=np.uint32).view(np.int32)[0])
+    sb = [torch.full((N * (K // 64),), word, dtype=torch.int32, device="cuda:0") for _ in range(pool)]
+    x = (torch.randn(K, device="cuda:0") if norm else torch.randn(K, device="cuda:0").to(torch.bfloat16))
+    g = torch.ones(K, device="cuda:0")
+    out = torch.zeros(N // 2 if epi == 2 else N, dtype=torch.int16 if epi == 2 else torch.float32, device="cuda:0")
+    it = [0]
+
+    def fn():
+        i = it[0] % pool
+        it[0] += 1
+        _lib.check(lib.q3op_qlinear(bits, epi, x.data_ptr(), codes[i].data_ptr(), sb[i].data_ptr(), N, K,
+                                    g.data_ptr() if norm else None, 1e-6, out.data_ptr(), stream.cuda_stream))
+    us = _time(fn, reps, stream)
+    byts = N * K * bits // 8 + N * (K // 64) * 4 + K * (4 if norm else 2) + (N // 2 * 2 if epi == 2 else N * 4)
+    return {"kernel": name, "bits": bits, "N": N, "K": K, "us": round(us, 2), "bytes": byts,
+            "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
+
+
 class ARGS:  # command-line settings the cases read
     attn_smax = 0
 
@@ -205,6 +230,14 @@ CASES = {
     "sample_b1": lambda lib, r, s: sample_case(lib, "sample_b1", 1, r, s),
     "sample_b64": lambda lib, r, s: sample_case(lib, "sample_b64", 64, r, s),
     "sample_b64_flat": lambda lib, r, s: sample_case(lib, "sample_b64_flat", 64, r, s, scale=0.01),
+    "q8_qkv": lambda lib, r, s: qlinear_case(lib, "q8_qkv", 8, 0, Q + 2 * KVW, H, r, s, norm=True),
+    "q8_o": lambda lib, r, s: qlinear_case(lib, "q8_o", 8, 1, H, Q, r, s),
+    "q8_gate_up": lambda lib, r, s: qlinear_case(lib, "q8_gate_up", 8, 2, 2 * I, H, r, s, norm=True),
+    "q8_down": lambda lib, r, s: qlinear_case(lib, "q8_down", 8, 1, H, I, r, s),
+    "q4_qkv": lambda lib, r, s: qlinear_case(lib, "q4_qkv", 4, 0, Q + 2 * KVW, H, r, s, norm=True),
+    "q4_o": lambda lib, r, s: qlinear_case(lib, "q4_o", 4, 1, H, Q, r, s),
+    "q4_gate_up": lambda lib, r, s: qlinear_case(lib, "q4_gate_up", 4, 2, 2 * I, H, r, s, norm=True),
+    "q4_down": lambda lib, r, s: qlinear_case(lib, "q4_down", 4, 1, H, I, r, s),
     "flash_512": lambda lib, r, s: attention_case(lib, "flash_512", 0, 512, 1, r, s),
     "flash_32k": lambda lib, r, s: attention_case(lib, "flash_32k", 0, 32768, 1, max(2, r // 10), s),
     "decode_attn_32k": lambda lib, r, s: attention_case(lib, "decode_attn_32k", 1, 32799, 1, r, s),
