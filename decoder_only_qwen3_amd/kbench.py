@@ -247,6 +247,7 @@ CASES = {
                                                           ARGS.attn_smax),
     "fused_b64_uniform": lambda lib, r, s: fused_attn_case(lib, "fused_b64_uniform", [4160] * 64, r, s,
                                                            ARGS.attn_smax),
+    "fused_b1_640": lambda lib, r, s: fused_attn_case(lib, "fused_b1_640", [640], r, s, ARGS.attn_smax),
     "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax),
 }
 
