@@ -27,6 +27,7 @@ EXPORTS = [
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
     "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
     "q3op_sample_workspace_bytes", "q3op_sample_top_p", "q3op_quantize", "q3op_dequantize", "q3op_qlinear",
+    "q3op_qlinear_rows_workspace_bytes", "q3op_qlinear_rows",
 ]
 
 
@@ -94,6 +95,8 @@ def load() -> C.CDLL:
         "q3op_quantize": (I32, [VP, I32, I32, I32, VP, VP, VP]),
         "q3op_dequantize": (I32, [VP, VP, I32, I32, I32, VP, VP]),
         "q3op_qlinear": (I32, [I32, I32, VP, VP, VP, I32, I32, VP, C.c_float, VP, VP]),
+        "q3op_qlinear_rows_workspace_bytes": (SZ, [I32, I32, I32]),
+        "q3op_qlinear_rows": (I32, [I32, I32, VP, I32, VP, VP, I32, I32, VP, C.c_float, VP, I64, VP, SZ, VP]),
         "q3op_sample_top_p": (I32, [VP, I32, I32, I64, C.c_float, C.c_float, VP, VP, VP, VP, SZ, VP]),
         "q3op_embed": (I32, [I32, VP, I32, VP, I32, I32, VP, VP, VP]),
         "q3op_rmsnorm": (I32, [I32, VP, I32, VP, I32, C.c_float, VP, VP]),

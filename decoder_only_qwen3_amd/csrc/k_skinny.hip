@@ -29,16 +29,28 @@ namespace q3k {
 namespace {
 Q3_DEV float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
+typedef __bf16 bf16x2_k __attribute__((ext_vector_type(2)));
+// Two floats -> packed bf16 by v_cvt_pk_bf16_f32 (round to nearest even), as
+// the dequantizer and the single-row GEMV on codes round.
+Q3_DEV uint32_t pack_bf2_hw(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_k));
+}
+
 constexpr int kMaxWaves = 16;
 constexpr int kNormMaxM = 64;
 
-template <int EPI, int MT, int NST, bool NORM>
+// BITS = 8 or 4: W holds affine group codes of the weights (groups of 64
+// along K, a 32-bit fp16 scale/offset word per group in sbw); each lane
+// loads its 8 codes and the group's word and forms bf16(q * s + b), the same
+// bf16 values the dequantizer writes, before the MFMA loop.
+template <int EPI, int MT, int NST, bool NORM, int BITS = 0>
 __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ Xin, int M,
-                                                      const bf16_t* __restrict__ W, int N, int K,
+                                                      const void* __restrict__ Wv, int N, int K,
                                                       const float* __restrict__ gnorm, float eps,
                                                       void* __restrict__ out, int64_t ldo,
                                                       float* __restrict__ amax_val,
-                                                      int32_t* __restrict__ amax_idx) {
+                                                      int32_t* __restrict__ amax_idx,
+                                                      const uint32_t* __restrict__ sbw) {
   constexpr int RG = (EPI == EPI_SWIGLU) ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int nw = blockDim.x >> 6;
@@ -50,12 +62,30 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
 
   // Weight fragments first: they are the HBM stream.
   u32x4 wf[RG][NST];
+  uint32_t wq[BITS ? RG : 1][BITS ? NST : 1][BITS == 8 ? 2 : 1], wsb[BITS ? RG : 1][BITS ? NST : 1];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    const bf16_t* wp = W + (int64_t)(row0 + g * 16 + (lane & 15)) * K + k0;
+    const int64_t row = row0 + g * 16 + (lane & 15);
+    if constexpr (BITS == 0) {
+      const bf16_t* wp = reinterpret_cast<const bf16_t*>(Wv) + row * K + k0;
 #pragma unroll
-    for (int s = 0; s < NST; ++s)
-      wf[g][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + s * 32));
+      for (int s = 0; s < NST; ++s)
+        wf[g][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + s * 32));
+    } else {
+      const uint8_t* cp = reinterpret_cast<const uint8_t*>(Wv) + row * (K * BITS / 8);
+#pragma unroll
+      for (int s = 0; s < NST; ++s) {
+        const int kk = k0 + s * 32;
+        if constexpr (BITS == 8) {
+          const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cp + kk));
+          wq[g][s][0] = c[0];
+          wq[g][s][1] = c[1];
+        } else {
+          wq[g][s][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cp + kk / 2));
+        }
+        wsb[g][s] = sbw[row * (K / 64) + kk / 64];
+      }
+    }
   }
 
   float* red = smem;                                  // [nw][RG][MT][256]
@@ -102,6 +132,26 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
       inv[threadIdx.x] = rsqrtf(t / (float)K + eps);
     }
     __syncthreads();
+  }
+
+  if constexpr (BITS != 0) {  // codes -> bf16(q * s + b) fragments
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int s = 0; s < NST; ++s) {
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(wsb[g][s] & 0xffffu));
+        const float of = (float)__builtin_bit_cast(_Float16, (uint16_t)(wsb[g][s] >> 16));
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t q;
+          if constexpr (BITS == 8) q = (wq[g][s][i >> 2] >> (8 * (i & 3))) & 0xffu;
+          else q = (wq[g][s][0] >> (4 * i)) & 0xfu;
+          v[i] = fmaf((float)q, sc, of);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[g][s][i] = pack_bf2_hw(v[2 * i], v[2 * i + 1]);
+      }
   }
 
   f32x4 acc[RG][MT];
@@ -249,11 +299,12 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
   }
 }
 
-template <int EPI, int NST, bool NORM>
-hipError_t launch_mt(int MT, dim3 grid, dim3 block, size_t lds, const void* X, int M, const bf16_t* W, int N,
+template <int EPI, int NST, bool NORM, int BITS>
+hipError_t launch_mt(int MT, dim3 grid, dim3 block, size_t lds, const void* X, int M, const void* W, int N,
                      int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
-                     hipStream_t s) {
-#define Q3_SK(mt) skinny_kernel<EPI, mt, NST, NORM><<<grid, block, lds, s>>>(X, M, W, N, K, g, eps, out, ldo, av, ai)
+                     hipStream_t s, const uint32_t* sb) {
+#define Q3_SK(mt) \
+  skinny_kernel<EPI, mt, NST, NORM, BITS><<<grid, block, lds, s>>>(X, M, W, N, K, g, eps, out, ldo, av, ai, sb)
   switch (MT) {
     case 1: Q3_SK(1); break;
     case 2: Q3_SK(2); break;
@@ -264,23 +315,24 @@ hipError_t launch_mt(int MT, dim3 grid, dim3 block, size_t lds, const void* X, i
   return hipGetLastError();
 }
 
-template <int EPI, bool NORM>
-hipError_t launch_nst(const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const bf16_t* W, int N,
+template <int EPI, bool NORM, int BITS>
+hipError_t launch_nst(const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const void* W, int N,
                       int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
-                      hipStream_t s) {
+                      hipStream_t s, const uint32_t* sb) {
   const int rg = (EPI == EPI_SWIGLU) ? 2 : 1;
   const size_t lds = (size_t)p.waves * rg * MT * 256 * 4 + kNormMaxM * 4;
   dim3 block(64 * p.waves);
-  if (p.nst == 8) return launch_mt<EPI, 8, NORM>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
-  return launch_mt<EPI, 4, NORM>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
+  if (p.nst == 8)
+    return launch_mt<EPI, 8, NORM, BITS>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s, sb);
+  return launch_mt<EPI, 4, NORM, BITS>(MT, grid, block, lds, X, M, W, N, K, g, eps, out, ldo, av, ai, s, sb);
 }
 
-template <int EPI>
-hipError_t launch_norm(bool norm, const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const bf16_t* W,
+template <int EPI, int BITS = 0>
+hipError_t launch_norm(bool norm, const SkinnyPlan& p, int MT, dim3 grid, const void* X, int M, const void* W,
                        int N, int K, const float* g, float eps, void* out, int64_t ldo, float* av, int32_t* ai,
-                       hipStream_t s) {
-  if (norm) return launch_nst<EPI, true>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
-  return launch_nst<EPI, false>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s);
+                       hipStream_t s, const uint32_t* sb = nullptr) {
+  if (norm) return launch_nst<EPI, true, BITS>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s, sb);
+  return launch_nst<EPI, false, BITS>(p, MT, grid, X, M, W, N, K, g, eps, out, ldo, av, ai, s, sb);
 }
 }  // namespace
 
@@ -357,6 +409,44 @@ hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, in
     case EPI_ARGMAX: return launch_norm<EPI_ARGMAX>(norm, p, MT, grid, X, M, W, N, K, gnorm, eps, out, ldo, amax_val, amax_idx, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t skinny_q(int epi, int bits, const void* X, int M, const uint8_t* codes, const uint32_t* sb, int N, int K,
+                    const float* gnorm, float eps, void* out, int64_t ldo, hipStream_t s, float* split_part,
+                    uint32_t* split_cnt) {
+  if (M <= 0) return hipSuccess;
+  if (M > 64 || (bits != 8 && bits != 4) || K % 64 != 0) return hipErrorInvalidValue;
+  if (epi != EPI_STORE && epi != EPI_RESADD && epi != EPI_SWIGLU) return hipErrorInvalidValue;
+  const bool norm = gnorm != nullptr;
+  if (norm && M > kNormMaxM) return hipErrorInvalidValue;
+  auto go = [&](auto bits_c, const SkinnyPlan& p, int MT, dim3 grid, float* av, int32_t* ai) -> hipError_t {
+    constexpr int B = decltype(bits_c)::value;
+    switch (epi) {
+      case EPI_STORE: return launch_norm<EPI_STORE, B>(norm, p, MT, grid, X, M, codes, N, K, gnorm, eps, out, ldo, av, ai, s, sb);
+      case EPI_RESADD: return launch_norm<EPI_RESADD, B>(norm, p, MT, grid, X, M, codes, N, K, gnorm, eps, out, ldo, av, ai, s, sb);
+      default: return launch_norm<EPI_SWIGLU, B>(norm, p, MT, grid, X, M, codes, N, K, gnorm, eps, out, ldo, av, ai, s, sb);
+    }
+  };
+  const int sp = (!norm && split_part && split_cnt) ? skinny_splits(epi, M, N, K) : 1;
+  const int MT = (M + 15) / 16;
+  if (sp > 1) {
+    const SkinnyPlan p = skinny_plan(epi, M, N, K / sp);
+    if (N % 16 != 0 || p.waves * p.nst * 32 * sp != K || p.waves > kMaxWaves || p.waves * MT > 96)
+      return hipErrorInvalidValue;
+    dim3 grid(N / 16, sp);
+    float* av = split_part;
+    int32_t* ai = reinterpret_cast<int32_t*>(split_cnt);
+    return bits == 8 ? go(std::integral_constant<int, 8>{}, p, MT, grid, av, ai)
+                     : go(std::integral_constant<int, 4>{}, p, MT, grid, av, ai);
+  }
+  const SkinnyPlan p = skinny_plan(epi, M, N, K);
+  const int rg = (epi == EPI_SWIGLU) ? 2 : 1;
+  if (N % (16 * rg) != 0 || p.waves * p.nst * 32 != K || p.waves > kMaxWaves || p.waves * rg * MT > 96 ||
+      (norm && K % 4 != 0))
+    return hipErrorInvalidValue;
+  dim3 grid(N / (16 * rg));
+  return bits == 8 ? go(std::integral_constant<int, 8>{}, p, MT, grid, nullptr, nullptr)
+                   : go(std::integral_constant<int, 4>{}, p, MT, grid, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------- row-parallel decode GEMV

@@ -49,6 +49,12 @@ hipError_t quantize_rows(const bf16_t* src, int rows, int K, int bits, uint8_t* 
 // bf16(q * s + b) for every weight of a quantized [N, K] matrix.
 hipError_t dequant_rows(const uint8_t* codes, const uint32_t* sb, int N, int K, int bits, bf16_t* out, hipStream_t s);
 bool qrowgemv_ok(int K);
+// The weight-streaming decode projection (k_skinny.hip) on codes: M <= 64
+// rows, EPI_STORE / EPI_RESADD (split over K with the workspace as in
+// skinny_bf16) / EPI_SWIGLU, optional RMSNorm prologue.
+hipError_t skinny_q(int epi, int bits, const void* X, int M, const uint8_t* codes, const uint32_t* sb, int N, int K,
+                    const float* gnorm, float eps, void* out, int64_t ldo, hipStream_t s, float* split_part = nullptr,
+                    uint32_t* split_cnt = nullptr);
 // One activation row against a quantized matrix: EPI_STORE / EPI_SWIGLU (with
 // an optional RMSNorm prologue from the float32 residual when gnorm is given)
 // or EPI_RESADD (bf16 activation).

@@ -376,6 +376,32 @@ q3_status q3op_qlinear(int32_t bits, int32_t epi, const void* d_x, const void* d
   return Q3_OK;
 }
 
+size_t q3op_qlinear_rows_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || N < 16 || K < 64) return 0;
+  return al(std::max<size_t>(16, skinny_split_floats(M, N, K)) * 4) + al((size_t)(N / 16 + 1) * 4);
+}
+
+q3_status q3op_qlinear_rows(int32_t bits, int32_t epi, const void* d_x, int32_t M, const void* d_codes,
+                            const void* d_sb, int32_t N, int32_t K, const float* d_gnorm, float eps, void* d_out,
+                            int64_t ldo, void* d_ws, size_t ws_bytes, void* stream) {
+  if (bits != 8 && bits != 4) return op_fail(Q3_E_ARG, "bits must be 8 or 4");
+  if (M < 1 || M > 64) return op_fail(Q3_E_ARG, "M must be 1..64");
+  if (epi != EPI_STORE && epi != EPI_RESADD && epi != EPI_SWIGLU) return op_fail(Q3_E_ARG, "epilogue");
+  if (d_gnorm && (epi == EPI_RESADD || M > 16)) return op_fail(Q3_E_ARG, "RMSNorm prologue: store/SwiGLU, M <= 16");
+  if (!d_x || !d_codes || !d_sb || !d_out) return op_fail(Q3_E_ARG, "NULL pointer");
+  float* part = nullptr;
+  uint32_t* cnt = nullptr;
+  if (epi == EPI_RESADD && d_ws) {
+    if (ws_bytes < q3op_qlinear_rows_workspace_bytes(M, N, K)) return op_fail(Q3_E_ARG, "workspace too small");
+    part = (float*)d_ws;
+    cnt = (uint32_t*)((char*)d_ws + al(std::max<size_t>(16, skinny_split_floats(M, N, K)) * 4));
+    OP_TRY(fill_u32(cnt, 0u, N / 16 + 1, (hipStream_t)stream));
+  }
+  OP_TRY(skinny_q(epi, bits, d_x, M, (const uint8_t*)d_codes, (const uint32_t*)d_sb, N, K, d_gnorm, eps, d_out, ldo,
+                  (hipStream_t)stream, part, cnt));
+  return Q3_OK;
+}
+
 size_t q3op_sample_workspace_bytes(int32_t n_rows) { return sample_workspace_bytes(n_rows); }
 
 q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab, int64_t ld, float temperature,

@@ -288,16 +288,18 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   }
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.
-  // Quantized weights: batch-1 decode reads the codes directly (every
-  // projection); other calls dequantize each layer's projections to bf16
-  // first and run the bf16 kernels on that copy.
+  // Quantized weights: decode reads the codes directly (batch 1: the
+  // single-row GEMV; batches: the weight-streaming kernel); prefill
+  // dequantizes each layer's projections to bf16 first and runs the GEMMs on
+  // that copy.
   const int bits = c.weight_bits;
   const bool qone = bits && decode && T == 1 && qrowgemv_ok(H) && qrowgemv_ok(Q) && qrowgemv_ok(I);
+  const bool qsk = bits && decode && !qone;
   const bool one_h = !bits && bf && decode && rowgemv_ok(T, H);
   const bool one_q = !bits && bf && decode && rowgemv_ok(T, Q);
   const bool one_i = !bits && bf && decode && rowgemv_ok(T, I);
-  const bool rows_o = bf && decode && rowdot_ok(T, Q);
-  const bool rows_d = bf && decode && rowdot_ok(T, I);
+  const bool rows_o = !bits && bf && decode && rowdot_ok(T, Q);
+  const bool rows_d = !bits && bf && decode && rowdot_ok(T, I);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
     const bf16_t *Wqkv = nullptr, *Wo = nullptr, *Wgu = nullptr, *Wd = nullptr;
@@ -306,7 +308,7 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       Wo = m->W<bf16_t>(lw.o);
       Wgu = m->W<bf16_t>(lw.gu);
       Wd = m->W<bf16_t>(lw.d);
-    } else if (bits && !qone) {
+    } else if (bits && !decode) {
       bf16_t* dq = m->WS<bf16_t>(L.wdq);
       Wqkv = dq;
       Wo = Wqkv + (size_t)NQKV * H;
@@ -326,6 +328,10 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else if (qone) {
       LAUNCH(qrowgemv(EPI_STORE, bits, x, m->W<uint8_t>(lw.qkv), m->W<uint32_t>(lw.qkv_sb), NQKV, H,
                       m->W<float>(lw.in_norm), c.rms_eps, qkv, s));
+    } else if (qsk) {
+      LAUNCH(skinny_q(EPI_STORE, bits, fuse_norm ? (const void*)x : h, T, m->W<uint8_t>(lw.qkv),
+                      m->W<uint32_t>(lw.qkv_sb), NQKV, H, fuse_norm ? m->W<float>(lw.in_norm) : nullptr, c.rms_eps,
+                      qkv, NQKV, s));
     } else if (one_h) {
       LAUNCH(rowgemv_bf16(EPI_STORE, x, Wqkv, NQKV, H, m->W<float>(lw.in_norm), c.rms_eps, qkv, nullptr, nullptr, s));
     } else if (decode) {
@@ -359,6 +365,9 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       LAUNCH(gemv_f32(EPI_RESADD, (const float*)ob, T, m->W<float>(lw.o), H, Q, x, H, s));
     } else if (qone) {
       LAUNCH(qrowgemv(EPI_RESADD, bits, ob, m->W<uint8_t>(lw.o), m->W<uint32_t>(lw.o_sb), H, Q, nullptr, 0.f, x, s));
+    } else if (qsk) {
+      LAUNCH(skinny_q(EPI_RESADD, bits, ob, T, m->W<uint8_t>(lw.o), m->W<uint32_t>(lw.o_sb), H, Q, nullptr, 0.f, x, H,
+                      s, m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else if (one_q) {
       LAUNCH(rowgemv_bf16(EPI_RESADD, ob, Wo, H, Q, nullptr, 0.f, x, nullptr, nullptr, s));
     } else if (rows_o) {
@@ -379,6 +388,12 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       LAUNCH(qrowgemv(EPI_SWIGLU, bits, x, m->W<uint8_t>(lw.gu), m->W<uint32_t>(lw.gu_sb), 2 * I, H,
                       m->W<float>(lw.post_norm), c.rms_eps, mb, s));
       LAUNCH(qrowgemv(EPI_RESADD, bits, mb, m->W<uint8_t>(lw.d), m->W<uint32_t>(lw.d_sb), H, I, nullptr, 0.f, x, s));
+    } else if (qsk) {
+      LAUNCH(skinny_q(EPI_SWIGLU, bits, fuse_norm ? (const void*)x : h, T, m->W<uint8_t>(lw.gu),
+                      m->W<uint32_t>(lw.gu_sb), 2 * I, H, fuse_norm ? m->W<float>(lw.post_norm) : nullptr, c.rms_eps,
+                      mb, I, s));
+      LAUNCH(skinny_q(EPI_RESADD, bits, mb, T, m->W<uint8_t>(lw.d), m->W<uint32_t>(lw.d_sb), H, I, nullptr, 0.f, x, H,
+                      s, m->WS<float>(L.lin_part), m->WS<uint32_t>(L.lin_cnt)));
     } else if (decode) {
       if (one_h)
         LAUNCH(rowgemv_bf16(EPI_SWIGLU, x, Wgu, 2 * I, H, m->W<float>(lw.post_norm), c.rms_eps, mb, nullptr, nullptr,

@@ -151,6 +151,15 @@ q3_status q3op_dequantize(const void* d_codes, const void* d_sb, int32_t rows, i
                           void* stream);
 q3_status q3op_qlinear(int32_t bits, int32_t epi, const void* d_x, const void* d_codes, const void* d_sb, int32_t N,
                        int32_t K, const float* d_gnorm, float eps, void* d_out, void* stream);
+/* M = 1..64 activation rows (d_x bf16 [M][K], or with d_gnorm, M <= 16, the
+ * float32 residual rows) against the quantized W[N,K] by the weight-streaming
+ * kernel (K = 128 * 4..16 * 8 as for q3op_linear kernel 1), output rows of
+ * stride ldo: epi 0 float32 store, 1 float32 add (split over K when d_ws is
+ * given, q3op_qlinear_rows_workspace_bytes bytes), 2 SwiGLU (bf16). */
+size_t q3op_qlinear_rows_workspace_bytes(int32_t M, int32_t N, int32_t K);
+q3_status q3op_qlinear_rows(int32_t bits, int32_t epi, const void* d_x, int32_t M, const void* d_codes,
+                            const void* d_sb, int32_t N, int32_t K, const float* d_gnorm, float eps, void* d_out,
+                            int64_t ldo, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Kernel tuning knobs for benchmarks (process-wide, not thread-safe; they
  * affect q3_prefill too).  Returns Q3_E_ARG for an unknown key or value.

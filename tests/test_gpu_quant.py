@@ -119,6 +119,51 @@ def test_qlinear_rmsnorm_prologue(bits):
     assert np.median(np.abs(got - ref)) < 1e-5 * np.sqrt(np.mean(ref ** 2)) + 1e-6
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M", [2, 17, 64])
+def test_qlinear_rows_weight_streaming(bits, M):
+    """M activation rows by the weight-streaming kernel on codes: store,
+    split-K residual, SwiGLU, and the RMSNorm prologue for M <= 16."""
+    _, lib = ops()
+    rng = np.random.default_rng(bits * 7 + M)
+    for N, K in ((1024, 2048), (2048, 1024)):
+        W = rand_bf16(rng, (N, K), 0.02)
+        codes, sb = _quantize_gpu(W, bits)
+        Wq = to_bf16(dequantize_affine(*quantize_affine(W, bits)))
+        X = rand_bf16(rng, (M, K))
+        ref = X.astype(np.float64) @ Wq.T
+        ws = torch.zeros(max(256, lib.q3op_qlinear_rows_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda:0")
+        dx = dev_bf16(X)
+        for epi in (0, 1, 2):
+            base = rng.standard_normal((M, N)).astype(np.float32)
+            if epi == 2:
+                out = torch.zeros((M, N // 2), dtype=torch.int16, device="cuda:0")
+                ldo = N // 2
+            else:
+                out = dev_f32(base if epi == 1 else np.zeros((M, N), np.float32))
+                ldo = N
+            call(lib.q3op_qlinear_rows(bits, epi, dx.data_ptr(), M, codes.data_ptr(), sb.data_ptr(), N, K, None, 1e-6,
+                                       out.data_ptr(), ldo, ws.data_ptr(), ws.numel(), None))
+            torch.cuda.synchronize()
+            if epi == 2:
+                g_rows = np.concatenate([np.arange(c * 32, c * 32 + 16) for c in range(N // 32)])
+                want = to_bf16(silu(ref[:, g_rows]) * ref[:, g_rows + 16])
+                np.testing.assert_allclose(host_bf16(out), want, rtol=2 ** -7, atol=1e-6)
+            else:
+                got = out.cpu().numpy() - (base if epi == 1 else 0)
+                assert rel_err(got, ref) < 2e-5, (N, K, epi)
+        if M <= 16:
+            x = rng.standard_normal((M, K)).astype(np.float32)
+            g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+            a = to_bf16(rms_norm(x.astype(np.float64), g.astype(np.float64), 1e-6))
+            out = dev_f32(np.zeros((M, N), np.float32))
+            dxf, dg = dev_f32(x), dev_f32(g)
+            call(lib.q3op_qlinear_rows(bits, 0, dxf.data_ptr(), M, codes.data_ptr(), sb.data_ptr(), N, K, dg.data_ptr(),
+                                       1e-6, out.data_ptr(), N, None, 0, None))
+            torch.cuda.synchronize()
+            assert rel_err(out.cpu().numpy(), a @ Wq.T) < 5e-3
+
+
 def test_qlinear_rejects_bad_arguments():
     mod, lib = ops()
     z = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda:0")
