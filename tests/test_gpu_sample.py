@@ -56,6 +56,17 @@ def test_sample_matches_oracle(V, n, scale, T, p):
     assert near <= max(2, n // 10), near
 
 
+def test_sample_more_rows_than_one_batch():
+    """70 rows: the sampler runs its launches 64 rows at a time."""
+    rng = np.random.default_rng(11)
+    logits = (rng.standard_normal((70, 5000)) * 2).astype(np.float32)
+    u = rng.random(70).astype(np.float32)
+    got, err = _run(logits, 0.9, 0.9, u)
+    assert err == 0
+    near = _check_rows(logits, 0.9, 0.9, u, got)
+    assert near <= 2, near
+
+
 def test_sample_temperature_zero_is_greedy():
     rng = np.random.default_rng(1)
     logits = rng.standard_normal((70, 151936)).astype(np.float32)  # more rows than one launch takes
