@@ -106,19 +106,20 @@ def prefill_flops(d, lens, calls=1):
     return per_tok * sum(lens) + attn + head
 
 
-def cpu_baseline(d, w, prompt, seconds_budget=20.0):
-    """Time the CPU oracle (float64 numpy) on a bounded sample: a short prefill, then decode steps."""
+def cpu_baseline(d, w, prompt, seconds_budget=12.0, max_steps=600):
+    """Time the CPU oracle (float64 numpy) on a bounded sample: a short prefill,
+    then greedy decode steps for about `seconds_budget` seconds."""
     from oracle import OracleModel
     cores = len(os.sched_getaffinity(0))
     m = OracleModel(d, w)
     n_prompt = 16
-    cache = m.new_cache(n_prompt + 64)
+    cache = m.new_cache(n_prompt + max_steps)
     t0 = time.perf_counter()
     lg = m.forward(prompt[:n_prompt], cache)[0]   # also converts the weights to float64 once
     t1 = time.perf_counter()
     tok = int(np.argmax(lg))
     steps, t_dec = 0, 0.0
-    while steps < 64 and (steps < 2 or t_dec < seconds_budget):
+    while steps < max_steps and (steps < 2 or t_dec < seconds_budget):
         s0 = time.perf_counter()
         tok = int(np.argmax(m.forward([tok], cache)[0]))
         t_dec += time.perf_counter() - s0
