@@ -121,7 +121,7 @@ def test_linear_store_and_residual(kernel, M, N, K):
     assert _rel(got - base, ref) < 2e-5
 
 
-@pytest.mark.parametrize("M", [64, 500, 512, 1000])
+@pytest.mark.parametrize("M", [64, 500, 512, 1000, 4000, 4096])
 @pytest.mark.parametrize("N,K", [(1024, 2048), (1024, 3072), (2048, 1024)])
 def test_gemm_split_k_residual(M, N, K):
     """Residual GEMMs on grids too small to fill the chip are split over K; the
