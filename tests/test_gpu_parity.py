@@ -269,6 +269,9 @@ def test_prefill_rejects_overflowing_continuation(bf16_two_layer):
     assert "CAPACITY" in str(ei.value)
     m.synchronize()
     assert m.seq_length(0) == 60
+    m.prefill([0], [q3synth.make_tokens(4, d.vocab, 3).tolist()])  # exactly to the slot's end
+    m.synchronize()
+    assert m.seq_length(0) == 64 and m.error_flags() == 0
 
 
 # ---------------------------------------------------------------- Paso 8 sampling

@@ -235,6 +235,34 @@ def test_quantized_model_matches_oracle(two_layer, bits):
     assert m.error_flags() == 0
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantized_small_model_general_shapes(bits):
+    """A 512-wide model: the single-row GEMV on codes needs K % 1024 == 0, so
+    one-sequence decode takes the weight-streaming kernel on codes."""
+    from decoder_only_qwen3_amd import Q3Model
+    d = q3synth.QWEN3_06B.replace(n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=2, ffn=1024, vocab=4096)
+    w = weights_for(d, 91)
+    m = Q3Model(d, max_slots=2, max_positions=128, max_prefill_tokens=128, kv_tokens=256, weight_bits=bits)
+    m.load_weights(w)
+    o = OracleModel(d, quantized_weights(w, bits), contract=True)
+    prompt = q3synth.make_tokens(37, d.vocab, 92).tolist()
+    ref = o.forced_logits(prompt, [5, 6])
+    m.seq_alloc(0, 64)
+    lg, _ = m.prefill([0], [prompt])
+    with torch.cuda.stream(m.stream):
+        rows = [lg[0].clone()]
+    for t in (5, 6):
+        with torch.cuda.stream(m.stream):
+            tok = torch.tensor([t], dtype=torch.int32, device=m.device)
+        lg1, _ = m.decode([0], tok)
+        with torch.cuda.stream(m.stream):
+            rows.append(lg1[0].clone())
+    m.synchronize()
+    for i, r in enumerate(rows):
+        assert rel_err(r.cpu().numpy(), ref[i]) <= 3e-2, (i, rel_err(r.cpu().numpy(), ref[i]))
+    assert m.error_flags() == 0
+
+
 def test_quantized_checkpoint_load_equals_upload(two_layer, tmp_path):
     d, w = two_layer
     path = str(tmp_path / "model.safetensors")
