@@ -101,13 +101,108 @@ Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
   *reinterpret_cast<u32x2*>(p) = w;
 }
 
+// Prefill values: block (64-position tile of one sequence, kv head g).  Tiles
+// are aligned to positions (tile i covers positions 64i .. 64i + 63), so a
+// continuation's first and last tiles may be partial.  The tile's values are
+// read as rows, transposed through LDS and written as 16-byte runs of
+// consecutive positions into the cache's value blocks ([128 dims][32 keys]
+// per 32 positions), so both sides move whole cache lines.
+constexpr int VT_TILE = 64;
+
+struct VtTiles {
+  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of tiles per sequence
+  int32_t first[Q3_MAX_BATCH];        // position tile index of each sequence's first tile
+  int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
+};
+
+Q3_DEV int vt_seq(const VtTiles& tt, int n, int tix) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T>
+Q3_DEV void vt_append_tile(const float* __restrict__ qkv, const SeqBatch& sb, const VtTiles& tt,
+                           const SeqState* __restrict__ st, T* __restrict__ kv, int layer, int n_q, int n_kv,
+                           uint16_t* __restrict__ vh, int64_t vh_keys, int tix, int g) {
+  __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
+  const int b = vt_seq(tt, sb.n, tix);
+  const int P = sb.prior[b], L = sb.cu[b + 1] - sb.cu[b];
+  const int p0 = (tt.first[b] + tix - tt.tile_cu[b]) * VT_TILE;  // first position of the tile
+  // new positions in the tile: p0 + lo .. p0 + n - 1
+  const int lo = max(P - p0, 0), n = min(VT_TILE, P + L - p0);
+  const int units = n_q + 2 * n_kv;
+  const float* src = qkv + (int64_t)(sb.cu[b] + p0 - P) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
+  // read: thread -> (token r0 + 8i, 4 dims); 256 threads cover 8 tokens per
+  // pass, and all eight passes' loads are issued before the first LDS store
+  const int c4 = (threadIdx.x & 31) * 4, r0 = threadIdx.x >> 5;
+  float4 v[VT_TILE / 8];
+#pragma unroll
+  for (int i = 0; i < VT_TILE / 8; ++i) {
+    const int r = r0 + 8 * i;
+    if (r >= lo && r < n) v[i] = *reinterpret_cast<const float4*>(src + (int64_t)r * units * Q3_HEAD_DIM + c4);
+  }
+#pragma unroll
+  for (int i = 0; i < VT_TILE / 8; ++i) {
+    const int r = r0 + 8 * i;
+    if (r >= lo && r < n) {
+      st_f<T>(&tile[c4 + 0][r], v[i].x);
+      st_f<T>(&tile[c4 + 1][r], v[i].y);
+      st_f<T>(&tile[c4 + 2][r], v[i].z);
+      st_f<T>(&tile[c4 + 3][r], v[i].w);
+    }
+  }
+  __syncthreads();
+  const SeqState s = st[sb.slot[b]];
+  T* vt = kv_vt(kv, s, KvGeom{n_kv, layer}, g);
+  // write: thread -> (dim, 16-byte run of positions)
+  constexpr int RUN = 16 / sizeof(T), RUNS = VT_TILE / RUN;
+  for (int e = threadIdx.x; e < Q3_HEAD_DIM * RUNS; e += 256) {
+    const int d = e / RUNS, k0 = (e % RUNS) * RUN;
+    if (k0 >= lo && k0 + RUN <= n) {  // a run never crosses a 32-key block (p0 is a multiple of 64)
+      *reinterpret_cast<u32x4*>(vt + vt_off(p0 + k0, d)) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
+    } else {
+      for (int k = max(k0, lo); k < min(k0 + RUN, n); ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    // fp16 staging copy of the stored bf16 values for the flash kernel, the
+    // tile's keys past the sequence end zero (only for calls without cached
+    // tokens: then the tile holds every key of its positions)
+    if (vh) {
+      uint16_t* dst = vh + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;
+      for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
+        const int d = e >> 3, k0 = (e & 7) * 8;
+        u32x4 v;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = k0 + 2 * w < n ? tile[d][k0 + 2 * w] : 0u;
+          const uint32_t hi = k0 + 2 * w + 1 < n ? tile[d][k0 + 2 * w + 1] : 0u;
+          v[w] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + vt_off(p0 + k0, d)) = bf16x8_to_f16x8(v);
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ qkv, int T_, SeqBatch sb, SeqState* __restrict__ st, T* __restrict__ kv,
     int layer, int n_q, int n_kv, const float* __restrict__ qn, const float* __restrict__ kn, float eps,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t, T* __restrict__ q_out,
-    uint32_t* err) {
-  // Prefill handles the value heads in vt_append_kernel (tiled transpose).
+    uint32_t* err, int rope_blocks, VtTiles tt, uint16_t* __restrict__ vh, int64_t vh_keys) {
+  // Prefill: blocks from rope_blocks on transpose the value heads (one
+  // 64-position tile of one KV head each); the others normalise, rotate and
+  // store query and key heads, 16 heads of one token position per block.
+  if ((int)blockIdx.x >= rope_blocks) {
+    const int i = (int)blockIdx.x - rope_blocks;
+    vt_append_tile<T>(qkv, sb, tt, st, kv, layer, n_q, n_kv, vh, vh_keys, i / n_kv, i % n_kv);
+    return;
+  }
   const int units = sb.decode ? n_q + 2 * n_kv : n_q + n_kv;
   const int stride_units = n_q + 2 * n_kv;
   const int64_t gu = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // unit index (uniform per 16 lanes)
@@ -153,86 +248,6 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     for (int k = 0; k < 4; ++k) {
       st_f<T>(dst + vt_off(pos, 4 * j + k), av[k]);
       st_f<T>(dst + vt_off(pos, 64 + 4 * j + k), cv[k]);
-    }
-  }
-}
-
-// Prefill values: block (64-position tile of one sequence, kv head g).  Tiles
-// are aligned to positions (tile i covers positions 64i .. 64i + 63), so a
-// continuation's first and last tiles may be partial.  The tile's values are
-// read as rows, transposed through LDS and written as 16-byte runs of
-// consecutive positions into the cache's value blocks ([128 dims][32 keys]
-// per 32 positions), so both sides move whole cache lines.
-constexpr int VT_TILE = 64;
-
-struct VtTiles {
-  int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of tiles per sequence
-  int32_t first[Q3_MAX_BATCH];        // position tile index of each sequence's first tile
-  int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
-};
-
-Q3_DEV int vt_seq(const VtTiles& tt, int n, int tix) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tt.tile_cu[mid] <= tix) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void vt_append_kernel(const float* __restrict__ qkv, SeqBatch sb, VtTiles tt,
-                                                        const SeqState* __restrict__ st, T* __restrict__ kv,
-                                                        int layer, int n_q, int n_kv, uint16_t* __restrict__ vh,
-                                                        int64_t vh_keys) {
-  __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
-  const int tix = blockIdx.x, g = blockIdx.y;
-  const int b = vt_seq(tt, sb.n, tix);
-  const int P = sb.prior[b], L = sb.cu[b + 1] - sb.cu[b];
-  const int p0 = (tt.first[b] + tix - tt.tile_cu[b]) * VT_TILE;  // first position of the tile
-  // new positions in the tile: p0 + lo .. p0 + n - 1
-  const int lo = max(P - p0, 0), n = min(VT_TILE, P + L - p0);
-  const int units = n_q + 2 * n_kv;
-  const float* src = qkv + (int64_t)(sb.cu[b] + p0 - P) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
-  // read: thread -> (token r, 4 dims); 256 threads cover 8 tokens per pass
-  const int c4 = (threadIdx.x & 31) * 4, r0 = threadIdx.x >> 5;
-  for (int r = lo + r0; r < n; r += 8) {
-    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)r * units * Q3_HEAD_DIM + c4);
-    st_f<T>(&tile[c4 + 0][r], v.x);
-    st_f<T>(&tile[c4 + 1][r], v.y);
-    st_f<T>(&tile[c4 + 2][r], v.z);
-    st_f<T>(&tile[c4 + 3][r], v.w);
-  }
-  __syncthreads();
-  const SeqState s = st[sb.slot[b]];
-  T* vt = kv_vt(kv, s, KvGeom{n_kv, layer}, g);
-  // write: thread -> (dim, 16-byte run of positions)
-  constexpr int RUN = 16 / sizeof(T), RUNS = VT_TILE / RUN;
-  for (int e = threadIdx.x; e < Q3_HEAD_DIM * RUNS; e += 256) {
-    const int d = e / RUNS, k0 = (e % RUNS) * RUN;
-    if (k0 >= lo && k0 + RUN <= n) {  // a run never crosses a 32-key block (p0 is a multiple of 64)
-      *reinterpret_cast<u32x4*>(vt + vt_off(p0 + k0, d)) = *reinterpret_cast<const u32x4*>(&tile[d][k0]);
-    } else {
-      for (int k = max(k0, lo); k < min(k0 + RUN, n); ++k) vt[vt_off(p0 + k, d)] = tile[d][k];
-    }
-  }
-  if constexpr (sizeof(T) == 2) {
-    // fp16 staging copy of the stored bf16 values for the flash kernel, the
-    // tile's keys past the sequence end zero (only for calls without cached
-    // tokens: then the tile holds every key of its positions)
-    if (vh) {
-      uint16_t* dst = vh + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;
-      for (int e = threadIdx.x; e < Q3_HEAD_DIM * (VT_TILE / 8); e += 256) {
-        const int d = e >> 3, k0 = (e & 7) * 8;
-        u32x4 v;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = k0 + 2 * w < n ? tile[d][k0 + 2 * w] : 0u;
-          const uint32_t hi = k0 + 2 * w + 1 < n ? tile[d][k0 + 2 * w + 1] : 0u;
-          v[w] = lo | (hi << 16);
-        }
-        *reinterpret_cast<u32x4*>(dst + vt_off(p0 + k0, d)) = bf16x8_to_f16x8(v);
-      }
     }
   }
 }
@@ -292,28 +307,30 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                        uint32_t* err, hipStream_t s, uint16_t* vstage) {
   if (T <= 0) return hipSuccess;
   const int64_t units = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
-  dim3 grid((unsigned)((units + 15) / 16));
-  if (dtype == BF16)
-    rope_append_kernel<bf16_t><<<grid, 256, 0, s>>>(qkv, T, sb, st, (bf16_t*)kv, layer, n_q, n_kv, qn, kn,
-                                                    eps, cos_t, sin_t, (bf16_t*)q_out, err);
-  else
-    rope_append_kernel<float><<<grid, 256, 0, s>>>(qkv, T, sb, st, (float*)kv, layer, n_q, n_kv, qn, kn,
-                                                   eps, cos_t, sin_t, (float*)q_out, err);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sb.decode) return e;
-  const VtTiles tt = vt_tiles(sb, false);
-  dim3 vgrid((unsigned)tt.tile_cu[sb.n], n_kv);
+  const int64_t rope_blocks = (units + 15) / 16;
+  // Prefill: the value tiles ride in the same launch (blocks past rope_blocks).
   // A continuation stages all of its sequences' values from the cache once
   // the new ones are in; a fresh prompt stages them here, as they pass.
+  VtTiles tt{};
+  int64_t vt_blocks = 0;
   const bool cont = has_prior(sb);
-  const int64_t vh_keys = vstage_keys(sb);
+  const int64_t vh_keys = sb.decode ? 0 : vstage_keys(sb);
+  if (!sb.decode) {
+    tt = vt_tiles(sb, false);
+    vt_blocks = (int64_t)tt.tile_cu[sb.n] * n_kv;
+  }
+  if (rope_blocks + vt_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(rope_blocks + vt_blocks));
   if (dtype == BF16)
-    vt_append_kernel<bf16_t><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (bf16_t*)kv, layer, n_q, n_kv,
-                                                   cont ? nullptr : vstage, vh_keys);
+    rope_append_kernel<bf16_t><<<grid, 256, 0, s>>>(qkv, T, sb, st, (bf16_t*)kv, layer, n_q, n_kv, qn, kn,
+                                                    eps, cos_t, sin_t, (bf16_t*)q_out, err, (int)rope_blocks, tt,
+                                                    cont ? nullptr : vstage, vh_keys);
   else
-    vt_append_kernel<float><<<vgrid, 256, 0, s>>>(qkv, sb, tt, st, (float*)kv, layer, n_q, n_kv, nullptr, 0);
-  e = hipGetLastError();
-  if (e != hipSuccess || !cont || !vstage || dtype != BF16) return e;
+    rope_append_kernel<float><<<grid, 256, 0, s>>>(qkv, T, sb, st, (float*)kv, layer, n_q, n_kv, qn, kn,
+                                                   eps, cos_t, sin_t, (float*)q_out, err, (int)rope_blocks, tt,
+                                                   nullptr, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sb.decode || !cont || !vstage || dtype != BF16) return e;
   return vstage_from_cache(T, sb, st, (const bf16_t*)kv, layer, n_kv, vstage, s);
 }
 
