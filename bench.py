@@ -153,7 +153,7 @@ def checkpoint_load(m, w, d):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

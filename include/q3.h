@@ -38,7 +38,7 @@ typedef enum q3_status {
   Q3_E_STATE = -2,        /* call not valid in the current state (e.g. before q3_load_weights) */
   Q3_E_CAPACITY = -3,     /* the KV cache of a sequence or the arena would overflow */
   Q3_E_HIP = -4,          /* a HIP runtime call failed */
-  Q3_E_UNSUPPORTED = -5   /* a shape or option this build does not handle */
+  Q3_E_UNSUPPORTED = -5   /* a shape or option the library does not handle */
 } q3_status;
 
 typedef enum q3_dtype { Q3_F32 = 0, Q3_BF16 = 1 } q3_dtype;
