@@ -189,6 +189,9 @@ Q3_DEV void vt_append_tile(const float* __restrict__ qkv, const SeqBatch& sb, co
   }
 }
 
+constexpr int ROPE_UPG = 2;                         // heads per 16-lane group
+constexpr int ROPE_UNITS_PER_BLOCK = 16 * ROPE_UPG;  // 256 threads = 16 groups
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ qkv, int T_, SeqBatch sb, SeqState* __restrict__ st, T* __restrict__ kv,
@@ -197,57 +200,73 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     uint32_t* err, int rope_blocks, VtTiles tt, uint16_t* __restrict__ vh, int64_t vh_keys) {
   // Prefill: blocks from rope_blocks on transpose the value heads (one
   // 64-position tile of one KV head each); the others normalise, rotate and
-  // store query and key heads, 16 heads of one token position per block.
+  // store query and key heads (in decode also the value heads), 32 heads per
+  // block.
   if ((int)blockIdx.x >= rope_blocks) {
     const int i = (int)blockIdx.x - rope_blocks;
     vt_append_tile<T>(qkv, sb, tt, st, kv, layer, n_q, n_kv, vh, vh_keys, i / n_kv, i % n_kv);
     return;
   }
+  // Each 16-lane group takes ROPE_UPG heads (16 apart), loading all of them
+  // before any arithmetic so that more of the stream is in flight.
   const int units = sb.decode ? n_q + 2 * n_kv : n_q + n_kv;
   const int stride_units = n_q + 2 * n_kv;
-  const int64_t gu = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // unit index (uniform per 16 lanes)
   const int j = threadIdx.x & 15;
-  if (gu >= (int64_t)T_ * units) return;
-  const int t = (int)(gu / units), u = (int)(gu - (int64_t)t * units);
-  const int b = seq_of_token(sb, t);
-  const SeqState s = st[sb.slot[b]];
-  const int pos = sb.decode ? s.len : sb.prior[b] + t - sb.cu[b];
-  if (pos < 0 || pos >= s.cap) {  // host validation makes this unreachable
-    if (j == 0) atomicOr(err, 4u);
-    return;
+  const int64_t n_units = (int64_t)T_ * units;
+  int64_t gu[ROPE_UPG];
+  float4 a[ROPE_UPG], c[ROPE_UPG];
+#pragma unroll
+  for (int k = 0; k < ROPE_UPG; ++k) {
+    gu[k] = (int64_t)blockIdx.x * ROPE_UNITS_PER_BLOCK + 16 * k + (threadIdx.x >> 4);  // uniform per 16 lanes
+    if (gu[k] < n_units) {
+      const int t = (int)(gu[k] / units), u = (int)(gu[k] - (int64_t)t * units);
+      const float* src = qkv + (int64_t)t * stride_units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
+      a[k] = *reinterpret_cast<const float4*>(src + 4 * j);
+      c[k] = *reinterpret_cast<const float4*>(src + 64 + 4 * j);
+    }
   }
-  const float* src = qkv + (int64_t)t * stride_units * Q3_HEAD_DIM + u * Q3_HEAD_DIM;
-  float4 a = *reinterpret_cast<const float4*>(src + 4 * j);
-  float4 c = *reinterpret_cast<const float4*>(src + 64 + 4 * j);
   const KvGeom g{n_kv, layer};
-  if (u < n_q + n_kv) {
-    const float* w = u < n_q ? qn : kn;
-    float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
-    const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
-    const float4 wa = *reinterpret_cast<const float4*>(w + 4 * j);
-    const float4 wc = *reinterpret_cast<const float4*>(w + 64 + 4 * j);
-    a = float4{a.x * inv * wa.x, a.y * inv * wa.y, a.z * inv * wa.z, a.w * inv * wa.w};
-    c = float4{c.x * inv * wc.x, c.y * inv * wc.y, c.z * inv * wc.z, c.w * inv * wc.w};
-    const float4 cs = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * 64 + 4 * j);
-    const float4 sn = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * 64 + 4 * j);
-    T* dst;
-    if (u < n_q)
-      dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
-    else
-      dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
-    store4<T>(dst + 4 * j, a.x * cs.x - c.x * sn.x, a.y * cs.y - c.y * sn.y, a.z * cs.z - c.z * sn.z,
-              a.w * cs.w - c.w * sn.w);
-    store4<T>(dst + 64 + 4 * j, a.x * sn.x + c.x * cs.x, a.y * sn.y + c.y * cs.y, a.z * sn.z + c.z * cs.z,
-              a.w * sn.w + c.w * cs.w);
-  } else {
-    T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
-    const float av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.x, c.y, c.z, c.w};
+  for (int k = 0; k < ROPE_UPG; ++k) {
+    if (gu[k] >= n_units) continue;
+    const int t = (int)(gu[k] / units), u = (int)(gu[k] - (int64_t)t * units);
+    const int b = seq_of_token(sb, t);
+    const SeqState s = st[sb.slot[b]];
+    const int pos = sb.decode ? s.len : sb.prior[b] + t - sb.cu[b];
+    if (pos < 0 || pos >= s.cap) {  // host validation makes this unreachable
+      if (j == 0) atomicOr(err, 4u);
+      continue;
+    }
+    float4 x = a[k], y = c[k];
+    if (u < n_q + n_kv) {
+      const float* w = u < n_q ? qn : kn;
+      float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      st_f<T>(dst + vt_off(pos, 4 * j + k), av[k]);
-      st_f<T>(dst + vt_off(pos, 64 + 4 * j + k), cv[k]);
+      for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+      const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
+      const float4 wa = *reinterpret_cast<const float4*>(w + 4 * j);
+      const float4 wc = *reinterpret_cast<const float4*>(w + 64 + 4 * j);
+      x = float4{x.x * inv * wa.x, x.y * inv * wa.y, x.z * inv * wa.z, x.w * inv * wa.w};
+      y = float4{y.x * inv * wc.x, y.y * inv * wc.y, y.z * inv * wc.z, y.w * inv * wc.w};
+      const float4 cs = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * 64 + 4 * j);
+      const float4 sn = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * 64 + 4 * j);
+      T* dst;
+      if (u < n_q)
+        dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
+      else
+        dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
+      store4<T>(dst + 4 * j, x.x * cs.x - y.x * sn.x, x.y * cs.y - y.y * sn.y, x.z * cs.z - y.z * sn.z,
+                x.w * cs.w - y.w * sn.w);
+      store4<T>(dst + 64 + 4 * j, x.x * sn.x + y.x * cs.x, x.y * sn.y + y.y * cs.y, x.z * sn.z + y.z * cs.z,
+                x.w * sn.w + y.w * cs.w);
+    } else {
+      T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
+      const float av[4] = {x.x, x.y, x.z, x.w}, cv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st_f<T>(dst + vt_off(pos, 4 * j + e), av[e]);
+        st_f<T>(dst + vt_off(pos, 64 + 4 * j + e), cv[e]);
+      }
     }
   }
 }
@@ -307,7 +326,7 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
                        uint32_t* err, hipStream_t s, uint16_t* vstage) {
   if (T <= 0) return hipSuccess;
   const int64_t units = (int64_t)T * (sb.decode ? n_q + 2 * n_kv : n_q + n_kv);
-  const int64_t rope_blocks = (units + 15) / 16;
+  const int64_t rope_blocks = (units + ROPE_UNITS_PER_BLOCK - 1) / ROPE_UNITS_PER_BLOCK;
   // Prefill: the value tiles ride in the same launch (blocks past rope_blocks).
   // A continuation stages all of its sequences' values from the cache once
   // the new ones are in; a fresh prompt stages them here, as they pass.
