@@ -116,9 +116,10 @@ def attention_case(lib, name, kernel, L, B, reps, stream):
             "GBs": round(byts / us / 1e3, 1), "hbm_frac": round(byts / us / 1e3 / HBM, 4)}
 
 
-def fused_attn_case(lib, name, lens, reps, stream, smax):
+def fused_attn_case(lib, name, lens, reps, stream, smax, pool=1):
     """Fused decode attention (QK-Norm, RoPE, append, split attention) over
-    sequences with contexts `lens` (+1 new key each); bytes = cache read."""
+    sequences with contexts `lens` (+1 new key each); bytes = cache read.
+    `pool` > 1 cycles through that many copies of the cache (cold reads)."""
     n_q, n_kv = 16, 8
     B = len(lens)
     caps = [(L + 1 + 63) // 64 * 64 for L in lens]
@@ -126,7 +127,8 @@ def fused_attn_case(lib, name, lens, reps, stream, smax):
     bases = [0]
     for r in regions[:-1]:
         bases.append(bases[-1] + r)
-    kv = _rand_bf16((sum(regions),))
+    kvs = [_rand_bf16((sum(regions),)) for _ in range(pool)]
+    it = [0]
     qkv = torch.randn((B, (n_q + 2 * n_kv) * 128), dtype=torch.float32, device="cuda:0")
     qn = torch.ones(128, dtype=torch.float32, device="cuda:0")
     out = torch.empty((B, n_q, 128), dtype=torch.int16, device="cuda:0")
@@ -136,6 +138,8 @@ def fused_attn_case(lib, name, lens, reps, stream, smax):
     a_b, a_c, a_l = _lib.i64_array(bases), _lib.i32_array(caps), _lib.i32_array(lens)
 
     def fn():
+        kv = kvs[it[0] % pool]
+        it[0] += 1
         _lib.check(lib.q3op_decode_attn_fused(qkv.data_ptr(), B, a_b, a_c, a_l, kv.data_ptr(), n_q, n_kv,
                                               qn.data_ptr(), qn.data_ptr(), 1e-6, 1e6, max_pos, smax,
                                               out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream))
@@ -248,7 +252,7 @@ CASES = {
     "fused_b64_uniform": lambda lib, r, s: fused_attn_case(lib, "fused_b64_uniform", [4160] * 64, r, s,
                                                            ARGS.attn_smax),
     "fused_b1_640": lambda lib, r, s: fused_attn_case(lib, "fused_b1_640", [640], r, s, ARGS.attn_smax),
-    "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax),
+    "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax, pool=3),
 }
 
 
