@@ -370,12 +370,13 @@ class OracleModel:
         return x
 
     # -- Paso 2 + Paso 8: one call over new tokens ----------------------------
-    def forward(self, ids: Sequence[int], cache: KVCache,
-                logit_rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    def final_hidden(self, ids: Sequence[int], cache: KVCache,
+                     logit_rows: Optional[Iterable[int]] = None) -> np.ndarray:
         """Run `ids` at positions cache.length.. and append them to the cache.
 
-        Returns logits (n_rows, vocab) for `logit_rows` (indices into ids;
-        default: the last row only).
+        Returns the final-norm output (n_rows, hidden) of the rows `logit_rows`
+        (indices into ids; default: the last row only): the vectors the head
+        multiplies (bf16 values in contract mode).
         """
         d = self.d
         ids = np.asarray(ids, dtype=np.int64)
@@ -395,27 +396,44 @@ class OracleModel:
         cache.length = pos0 + ids.size
         if d.n_layers == 0:
             x = x[rows]
-        hf = self.rnd(rms_norm(x, self.W("model.norm.weight"), d.rms_eps))
-        # Paso 8: the head is tied to the embedding unless the weights carry a
-        # separate lm_head matrix (the page's listing reads one by that name)
-        head = self.W("lm_head.weight") if "lm_head.weight" in self.w else E
-        return hf @ head.T
+        return self.rnd(rms_norm(x, self.W("model.norm.weight"), d.rms_eps))
+
+    def head(self, hf: np.ndarray) -> np.ndarray:
+        """Paso 8: logits = hf @ head^T.  The head is tied to the embedding
+        unless the weights carry a separate lm_head matrix (the page's listing
+        reads one by that name)."""
+        name = "lm_head.weight" if "lm_head.weight" in self.w else "model.embed_tokens.weight"
+        return np.asarray(hf, dtype=np.float64) @ self.W(name).T
+
+    def forward(self, ids: Sequence[int], cache: KVCache,
+                logit_rows: Optional[Iterable[int]] = None) -> np.ndarray:
+        """Run `ids` at positions cache.length.. and append them to the cache.
+
+        Returns logits (n_rows, vocab) for `logit_rows` (indices into ids;
+        default: the last row only).
+        """
+        return self.head(self.final_hidden(ids, cache, logit_rows))
 
     # -- Paso 9: generation loops ---------------------------------------------
-    def generate_greedy(self, prompt: Sequence[int], n_steps: int):
+    def generate_greedy(self, prompt: Sequence[int], n_steps: int, return_hidden: bool = False):
         """Prefill, then n_steps one-token steps feeding back the argmax.
 
         Returns (tokens, logits): n_steps + 1 greedy tokens (the first comes
-        from the prefill's last row) and the logits each was picked from.
+        from the prefill's last row) and the logits each was picked from; with
+        return_hidden, also the final-norm vectors those logits came from.
         """
         cache = self.new_cache(len(prompt) + n_steps)
-        lg = self.forward(prompt, cache)[0]
-        toks, logits = [greedy_pick(lg)], [lg]
+        hf = self.final_hidden(prompt, cache)[0]
+        lg = self.head(hf)
+        toks, logits, hidden = [greedy_pick(lg)], [lg], [hf]
         for _ in range(n_steps):
-            lg = self.forward([toks[-1]], cache)[0]
+            hf = self.final_hidden([toks[-1]], cache)[0]
+            lg = self.head(hf)
             toks.append(greedy_pick(lg))
             logits.append(lg)
-        return np.asarray(toks, dtype=np.int64), np.stack(logits)
+            hidden.append(hf)
+        out = (np.asarray(toks, dtype=np.int64), np.stack(logits))
+        return out + (np.stack(hidden),) if return_hidden else out
 
     def forced_logits(self, prompt: Sequence[int], forced: Sequence[int]) -> np.ndarray:
         """Logits after the prompt and after each forced token, in one pass.

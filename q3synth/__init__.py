@@ -75,6 +75,12 @@ class Workload:
         return make_lengths(self.n_seqs, self.len_range[0], self.len_range[1],
                             seed=self.seed + 2)
 
+    def prompts(self) -> List[List[int]]:
+        """The token IDs of every prompt: sequence i draws its own with seed
+        seed + 1 + i."""
+        return [make_tokens(int(L), self.dims.vocab, self.seed + 1 + i).tolist()
+                for i, L in enumerate(self.prompt_lengths())]
+
 
 QWEN3_06B = ModelDims()
 

@@ -500,3 +500,49 @@ def test_last_layer_row_pruning_matches_full_rows():
         m.forward(ids, c1, logit_rows=range(7))
         m.forward(ids, c2)
         np.testing.assert_allclose(m.forward([9], c1), m.forward([9], c2), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- bf16 contract mode
+def test_scalar_bf16_rounder_matches_torch_conversion():
+    """The scalar model's bf16 rounding (integer bits) against torch's
+    float32 -> bfloat16 conversion, ties and carries included."""
+    from scalar_model import Bf16Rounder
+    r = Bf16Rounder()
+    vals = list(RNG.standard_normal(2000) * 10.0 ** RNG.integers(-6, 6, 2000))
+    # exact float32 midpoints between neighbouring bf16 values, odd and even lower neighbours
+    for hi in (0x3F80, 0x3F81, 0xBF80, 0xBF81, 0x4049, 0x7F7E):
+        vals.append(float(np.array([(hi << 16) | 0x8000], np.uint32).view(np.float32)[0]))
+    vals.append(float(np.array([0x3F80FFFF], np.uint32).view(np.float32)[0]))   # carry into the exponent field
+    got = np.array([r(v) for v in vals])
+    ref = torch.tensor(np.asarray(vals, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("kw,seed,mlp_scale", [({}, 7, 1.0), ({"n_kv_heads": 1}, 8, 1.0),
+                                                ({"n_layers": 1, "n_kv_heads": 4}, 9, 1.0), ({}, 7, 8.0)])
+def test_contract_mode_matches_scalar_bf16_brute_force(kw, seed, mlp_scale):
+    """The oracle's contract mode (bf16 weights and cache, activations rounded
+    at the bf16 model's points) against the scalar model's own bf16 mode: same
+    rounding points, different code.  Every rounded value of the scalar run
+    sits far from a rounding decision point (checked), so the small
+    differences of summation order between the two cannot flip a rounding, and
+    the logits agree to float64 precision.  Dropping any one rounding point
+    fails at least one case: with mlp_scale = 8 (gate, up and down weights
+    times 8, still bf16 values) the MLP output dominates the residual, so the
+    rounding of the SwiGLU product is not absorbed by the roundings after it."""
+    from scalar_model import Bf16Rounder
+    d = q3synth.tiny_dims(dtype="bf16", **kw)
+    w = q3synth.make_weights(d, seed=seed)
+    if mlp_scale != 1.0:
+        w = {k: (v * np.float32(mlp_scale) if ".mlp." in k else v) for k, v in w.items()}
+    ids = [3, 96, 0, 41, 41, 7]
+    m = OracleModel(d, w)
+    assert m.contract
+    got = m.forward(ids, m.new_cache(len(ids)), logit_rows=range(len(ids)))
+    r = Bf16Rounder()
+    ref = np.array(scalar_forward_all(d, w, ids, rounder=r))
+    assert r.closest > 1e-10, f"a rounded value sits {r.closest:.1e} (relative) from a rounding decision point"
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # and the rounding is not a no-op at this shape: the unrounded model differs
+    plain = np.array(scalar_forward_all(d, w, ids))
+    assert np.max(np.abs(plain - ref)) > 1e-5
