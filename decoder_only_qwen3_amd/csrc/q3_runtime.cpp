@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "../../include/q3.h"
+#include "../../include/q3_ops.h"
 #include "checkpoint.h"
 #include "kernels.h"
 
@@ -257,6 +258,21 @@ q3_status check(hipError_t e, const char* what) {
     if (st_ != Q3_OK) return st_;                      \
   } while (0)
 
+// Key splits per (sequence, kv head) of bf16 decode attention, from the
+// contexts at this call (a recorded graph keeps the split count it was
+// recorded with, which only matters for speed).
+int decode_smax(const q3_model* m, const SeqBatch& sb) {
+  const q3_config& c = m->cfg;
+  int64_t maxcap = 1, maxctx = 1, minctx = INT64_MAX;
+  for (int b = 0; b < sb.n; ++b) {
+    const auto& hs = m->slots[sb.slot[b]];
+    maxcap = std::max<int64_t>(maxcap, std::min<int64_t>(hs.cap, c.max_positions));
+    maxctx = std::max<int64_t>(maxctx, hs.len + 1);
+    minctx = std::min<int64_t>(minctx, hs.len + 1);
+  }
+  return fused_attn_smax(sb.n, c.n_kv_heads, maxcap, maxctx >= 2 * minctx);
+}
+
 // The transformer blocks of Paso 7 over `T` rows already embedded in x.
 q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hipStream_t s) {
   const q3_config& c = m->cfg;
@@ -273,19 +289,7 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   RowMap all;
   all.n = -1;
   const bool bf = c.dtype == Q3_BF16;
-  int smax = 1;
-  if (decode && bf) {
-    // (the contexts at this call; a recorded graph keeps the split count it
-    // was recorded with, which only matters for speed)
-    int64_t maxcap = 1, maxctx = 1, minctx = INT64_MAX;
-    for (int b = 0; b < sb.n; ++b) {
-      const auto& hs = m->slots[sb.slot[b]];
-      maxcap = std::max<int64_t>(maxcap, std::min<int64_t>(hs.cap, c.max_positions));
-      maxctx = std::max<int64_t>(maxctx, hs.len + 1);
-      minctx = std::min<int64_t>(minctx, hs.len + 1);
-    }
-    smax = fused_attn_smax(sb.n, c.n_kv_heads, maxcap, maxctx >= 2 * minctx);
-  }
+  const int smax = decode && bf ? decode_smax(m, sb) : 1;
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.
   // Quantized weights: decode reads the codes directly (batch 1: the
@@ -1080,3 +1084,34 @@ q3_status q3_sample(q3_model* m, int32_t n_rows, const float* d_logits, int64_t 
 }
 
 }  // extern "C"
+
+// Single-kernel entry on a live model (include/q3_ops.h): the fused decode
+// attention of one layer for the given slots, as q3_decode_step runs it.
+q3_status q3op_model_decode_attention(q3_model* m, int32_t layer, int32_t n, const int32_t* h_slots, void* stream) {
+  q3_status st;
+  if (!ready(m, &st)) return st;
+  if ((st = check_slots(m, n, h_slots)) != Q3_OK) return st;
+  const q3_config& c = m->cfg;
+  if (c.dtype != Q3_BF16) return fail(Q3_E_UNSUPPORTED, "the fused decode attention is the bf16 model's kernel");
+  if (layer < 0 || layer >= c.n_layers) return fail(Q3_E_ARG, "layer out of range");
+  SeqBatch sb;
+  std::memset(&sb, 0, sizeof(sb));
+  sb.n = n;
+  sb.decode = 1;
+  for (int b = 0; b < n; ++b) {
+    const HostSlot& hs = m->slots[h_slots[b]];
+    if (hs.len < 1) return fail(Q3_E_STATE, "slot is empty");
+    if (hs.len + 1 > hs.cap || hs.len + 1 > c.max_positions) return fail(Q3_E_CAPACITY, "KV cache full");
+    sb.slot[b] = h_slots[b];
+    sb.cu[b] = b;
+  }
+  sb.cu[n] = n;
+  const WsLayout& L = m->wsl;
+  const LayerW& lw = m->wl.layers[layer];
+  LAUNCH(decode_attn_fused(m->WS<float>(L.qkv), sb, m->state(), (bf16_t*)m->kv, layer, c.n_q_heads, c.n_kv_heads,
+                           m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, m->W<float>(m->wl.cos_t),
+                           m->W<float>(m->wl.sin_t), decode_smax(m, sb), m->WS<float>(L.attn_part),
+                           m->WS<uint32_t>(L.attn_cnt), (bf16_t*)m->WS(L.o), (hipStream_t)stream));
+  g_err.clear();
+  return Q3_OK;
+}

@@ -175,6 +175,11 @@ class Q3Model:
                                  nxt.data_ptr(), self.sh))
         return nxt
 
+    def decode_attention_kernel(self, layer: int, slots: Sequence[int]) -> None:
+        """Queue one launch of the fused decode attention of `layer` on the
+        slots' current state (q3op_model_decode_attention; no sync)."""
+        check(self.lib.q3op_model_decode_attention(self.handle, layer, len(slots), i32_array(slots), self.sh))
+
     def synchronize(self) -> None:
         self.stream.synchronize()
 

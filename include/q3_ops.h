@@ -120,6 +120,17 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n_seqs, const int64
                                  const float* d_kn, float eps, double theta, int32_t max_pos, int32_t smax,
                                  void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* The fused decode attention kernel above (Pasos 4-5) on a live bf16 model,
+ * exactly as q3_decode_step launches it for layer `layer`: the query, key and
+ * value rows are the model's projection workspace as the last call left
+ * them, the key and value are written at each slot's current length (which
+ * is not advanced, so repeated calls rewrite the same entry), the output goes
+ * to the model's attention-output workspace.  Host validation as in
+ * q3_decode_step (Q3_E_STATE for an empty slot, Q3_E_CAPACITY for a full
+ * one); queued on `stream` without synchronising it, so a benchmark can time
+ * repeated launches with events. */
+q3_status q3op_model_decode_attention(q3_model* m, int32_t layer, int32_t n, const int32_t* h_slots, void* stream);
+
 /* Paso 8 sampling of n_rows logit rows of width `vocab` (stride ld): the
  * same computation as q3_sample in q3.h, for any vocabulary size.  d_err is a
  * device word that receives error bit 2 for a row with a non-finite logit.
