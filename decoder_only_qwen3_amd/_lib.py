@@ -28,6 +28,7 @@ EXPORTS = [
     "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
     "q3op_sample_workspace_bytes", "q3op_sample_top_p", "q3op_quantize", "q3op_dequantize", "q3op_qlinear",
     "q3op_qlinear_rows_workspace_bytes", "q3op_qlinear_rows", "q3op_model_decode_attention",
+    "q3op_linear_noalloc",
 ]
 
 
@@ -114,6 +115,7 @@ def load() -> C.CDLL:
         "q3op_attention": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, I32, VP, VP,
                                  SZ, VP]),
         "q3op_model_decode_attention": (I32, [VP, I32, I32, i32p, VP]),
+        "q3op_linear_noalloc": (I32, [I32, I32, VP, I32, VP, I32, I32, VP, I64, VP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -225,6 +226,53 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
     return rowgemv_op(epi, d_x, nullptr, 0.f, d_w, N, K, d_out, d_next, d_ws, ws_bytes, s);
   }
   return op_fail(Q3_E_ARG, "unknown kernel");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation variant
+// The workspace of q3op_linear_noalloc: a file-scope device array, one copy
+// per GPU for the life of the process.  In host code `scratch` only names the
+// symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch_ptr.
+namespace {
+constexpr size_t kScratchBytes = (size_t)Q3OP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+q3_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  OP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return op_fail(Q3_E_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return op_fail(Q3_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return Q3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+q3_status q3op_linear_noalloc(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
+                              int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
+  const size_t need = q3op_linear_workspace_bytes(kernel, epi, M, N, K);
+  if (need > kScratchBytes)
+    return op_fail(Q3_E_CAPACITY, "q3op_linear_noalloc: the call needs " + std::to_string(need) +
+                                      " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
+                                      "-byte static scratch; use q3op_linear with a workspace");
+  void* ws = nullptr;
+  q3_status st = scratch_for_current_device(&ws);
+  if (st != Q3_OK) return st;
+  return q3op_linear(kernel, epi, d_x, M, d_w, N, K, d_out, ldo, d_next, ws, kScratchBytes, stream);
 }
 
 q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_t M, const float* d_gnorm,

@@ -64,6 +64,23 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
                       int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,
                       void* stream);
 
+/* q3op_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, epilogues and validation, with the workspace taken from
+ * a static device array of Q3OP_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends (its address is looked up
+ * once per device, on the first call with that device current).  The caller
+ * still passes inputs and outputs.  A call whose
+ * q3op_linear_workspace_bytes(kernel, epi, M, N, K) exceeds the scratch
+ * returns Q3_E_CAPACITY before anything is queued.  The call allocates
+ * nothing and clears what must start at zero (split counters) with a fill
+ * kernel on `stream`.  Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (different streams or threads without
+ * ordering) race; calls queued on one stream are ordered. */
+#define Q3OP_NOALLOC_SCRATCH_BYTES (16u << 20)
+q3_status q3op_linear_noalloc(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
+                              int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* stream);
+
 /* Pasos 3 + 5: a decode projection with RMSNorm fused into its prologue:
  * X = bf16(x * rsqrt(mean(x^2) + eps) * g) from float32 rows d_x [M][K] and
  * float32 weight d_gnorm [K], then epilogue `epi` as in q3op_linear.
