@@ -116,12 +116,20 @@ struct TileTable {
 // V(t) in sV[t & 1]; iteration j reads V(j-1) and K(j+1) and loads V(j) and
 // K(j+2) over the buffers of V(j-2) and K(j), used up in iteration j-1.
 template <int CB>
-__global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
+__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
     const bf16_t* __restrict__ kv, const uint16_t* __restrict__ vstage, int64_t vh_keys, int layer, int n_q,
     int n_kv, int qt, bf16_t* __restrict__ o, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * KT];  // fp16 bits
+  // One LDS array for both double buffers: [0], [1] = K tiles (bf16), [2],
+  // [3] = V^T tiles (fp16 bits).  With the key and value tiles in two arrays,
+  // the compiler could not tell which one a direct-to-LDS load writes and put
+  // a wait for every outstanding load (vmcnt(0)) before each LDS read -- right
+  // after the next tiles' loads were issued, which drained the pipeline; with
+  // one array it leaves the waits to the loop (wait_vm + barrier at the top
+  // of each iteration), checked in the compiled code.
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[4][KT * 128];
+  uint16_t (*sK)[KT * 128] = sKV;
+  uint16_t (*sV)[KT * 128] = sKV + 2;
 
   const int total = tt.tile_cu[sb.n];
   const int tile = total - 1 - (int)blockIdx.x;  // late (long) tiles first
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(256, CB <= 2 ? 2 : 1) void flash_prefill_kernel(
 
   // S^T of tile t: sacc[c][sb][cb], keys t*64 + c*32 + 8*fq + 4*sb + r.
   auto scores = [&](int t, f32x4 (&sacc)[2][2][CB]) {
-    const bf16_t* kb = sK[t & 1];
+    const bf16_t* kb = sK[t & 1];  // bf16 bits
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -613,17 +621,27 @@ struct KvRun {
   u32x4 v[8];
 };
 
+// Every address is formed before the first load is issued: when the address
+// arithmetic sat between the loads, the register allocator reused the
+// destination registers of loads still in flight for it, which forced waits
+// for those loads (and for the previous run's) in the middle of the issue.
 Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int end, int fr, int fq) {
+  const bf16_t* kp[2];
 #pragma unroll
   for (int sbk = 0; sbk < 2; ++sbk) {
     const int key = min(c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), end - 1);
-    const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16(kp + ks * 32);
+    kp[sbk] = Kc + (int64_t)key * 128 + fq * 8;
   }
-  const int vkey0 = c0 + fq * 8;
+  // value dim d * 16 + fr of the run's keys c0 + fq * 8 .. +7: vt_off steps
+  // by 16 * 32 elements per d
+  const bf16_t* vp = Vt + vt_off(c0 + fq * 8, fr);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) r.v[d] = ld16(Vt + vt_off(vkey0, d * 16 + fr));
+  for (int sbk = 0; sbk < 2; ++sbk)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16(kp[sbk] + ks * 32);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) r.v[d] = ld16(vp + d * 16 * 32);
 }
 
 template <int FW>
@@ -654,6 +672,8 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
   const int cend = min(w1, pos);
   const bool has_new = pos >= w0 && pos < w1;
   KvRun run[2];
+  // start of the wavefront's last 32-key run of cached keys
+  const int wlast = w0 + max(0, (cend - 1 - w0) >> 5) * 32;
   if (w0 < cend) load_run(run[0], Kc, Vt, w0, cend, fr, fq);
 
   // A: wavefront u handles unit u, u+FW, ...: the group's query heads, then
@@ -736,13 +756,20 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
       oacc[d] = mfma16_f16(vf, pf.lo, mfma16_f16(vf, pf.hi, oacc[d] * alpha));
     }
   };
-  // Two register buffers, used in turn: the next run loads while one is used.
-  for (int c0 = w0; c0 < cend; c0 += 64) {
-    if (c0 + 32 < cend) load_run(run[1], Kc, Vt, c0 + 32, cend, fr, fq);
-    attend(run[0], c0);
-    if (c0 + 32 >= cend) break;
-    if (c0 + 64 < cend) load_run(run[0], Kc, Vt, c0 + 64, cend, fr, fq);
-    attend(run[1], c0 + 32);
+  // Two register buffers, used in turn: the next run loads while one is
+  // used.  The next run is loaded on every path (past the end it re-reads the
+  // last run, which is not attended): with a conditional load the compiler
+  // counts outstanding loads by the path without it and waits for the
+  // just-issued run before using the current one.
+  if (w0 < cend) {
+    for (int c0 = w0;; c0 += 64) {
+      load_run(run[1], Kc, Vt, min(c0 + 32, wlast), cend, fr, fq);
+      attend(run[0], c0);
+      if (c0 + 32 >= cend) break;
+      load_run(run[0], Kc, Vt, min(c0 + 64, wlast), cend, fr, fq);
+      attend(run[1], c0 + 32);
+      if (c0 + 64 >= cend) break;
+    }
   }
   if (has_new) {
     // The new key: score q.k over 128 dims (bf16 operands, fp32 sums), then
@@ -908,8 +935,9 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   const int group = n_q / n_kv;
   if (group < 1 || group > 8 || 128 % group != 0) return hipErrorInvalidValue;
   // Rows per wavefront (16*CB).  CB = 2 halves the LDS reads per MFMA and still
-  // fits two blocks per CU (238 registers per lane); CB = 4 (one block per CU)
-  // measured slower on gfx950.  Short prefills keep CB = 1 for more blocks.
+  // fits two blocks per CU (248 registers per lane); 64 rows per wavefront (one
+  // block per CU, with register spills) measured slower on gfx950 and is not
+  // built.  Short prefills keep CB = 1 for more blocks.
   int CB = g_flash_cb;
   if (CB < 0) {
     // 32 rows per wavefront when that still gives every CU two blocks, else 16
@@ -931,10 +959,6 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const int64_t vh_keys = vstage_keys(sb);
   switch (CB) {
-    case 4:
-      flash_prefill_kernel<4><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
-                                                        scale_log2);
-      break;
     case 2:
       flash_prefill_kernel<2><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
                                                         scale_log2);

@@ -536,8 +536,8 @@ q3_status q3op_tune(int32_t key, int32_t value) {
     return Q3_OK;
   }
   if (key == Q3OP_TUNE_FLASH_ROWS) {
-    if (value != -1 && value != 1 && value != 2 && value != 4)
-      return op_fail(Q3_E_ARG, "rows per wavefront must be -1, 1, 2 or 4");
+    if (value != -1 && value != 1 && value != 2)
+      return op_fail(Q3_E_ARG, "rows per wavefront / 16 must be -1, 1 or 2");
     flash_set_rows(value);
     return Q3_OK;
   }

@@ -159,8 +159,9 @@ q3_status q3op_sample_top_p(const float* d_logits, int32_t n_rows, int32_t vocab
                             float top_p, const float* d_uniform, int32_t* d_next, uint32_t* d_err, void* d_ws,
                             size_t ws_bytes, void* stream);
 
-/* Weight-only affine group quantization (the page "Laya MLX performance
- * research", quantization section): groups of 64 along K, `bits` = 8 or 4.
+/* Weight-only affine group quantization (the page "Investigación de
+ * rendimiento de Laya MLX", quantization section): groups of 64 along K,
+ * `bits` = 8 or 4.
  * Codes [rows][K * bits / 8] bytes (4-bit: byte j holds k = 2j in its low
  * nibble and 2j + 1 in its high nibble); scale/offset words [rows][K / 64],
  * the float16 scale in the low 16 bits and the float16 offset in the high.
@@ -194,7 +195,7 @@ q3_status q3op_qlinear_rows(int32_t bits, int32_t epi, const void* d_x, int32_t 
  * Q3OP_TUNE_GEMM_TILES: prefill GEMM tile configuration, -1 = automatic,
  *   0..11 = fixed tile shapes (listed in k_gemm.hip).
  * Q3OP_TUNE_FLASH_ROWS: prefill attention query rows per wavefront / 16,
- *   -1 = automatic, or 1, 2, 4.
+ *   -1 = automatic, or 1, 2.
  * Q3OP_TUNE_ROWGEMV: single-row GEMV shape, -1 = automatic, else
  *   rows_per_wavefront (1, 2, 4, 8) + 256 * wavefronts_per_block (1..4);
  *   SwiGLU needs an even rows_per_wavefront.

@@ -165,6 +165,7 @@ def test_tune_rejects_bad_values():
     _, lib = ops()
     assert lib.q3op_tune(1, 12) != 0
     assert lib.q3op_tune(2, 3) != 0
+    assert lib.q3op_tune(2, 4) != 0
     assert lib.q3op_tune(3, 3 + 256) != 0
     assert lib.q3op_tune(3, 4 + 5 * 256) != 0
     assert lib.q3op_tune(4, 0) != 0
@@ -436,7 +437,7 @@ def test_flash_prefill_attention(lens):
     assert worst < 1.0, worst
 
 
-@pytest.mark.parametrize("rows", [1, 2, 4])
+@pytest.mark.parametrize("rows", [1, 2])
 def test_flash_prefill_rows_per_wavefront(rows):
     _, lib = ops()
     call(lib.q3op_tune(2, rows))
@@ -572,7 +573,8 @@ def test_rowdot_gemv(M, N, K):
 
 
 @pytest.mark.parametrize("prior,smax", [([0], 0), ([5, 700], 0), ([1500], 0), ([1500, 40], 3), ([32799], 0),
-                                        ([2047, 0, 4100], 0)])
+                                        ([2047, 0, 4100], 0), ([31, 32, 33, 63, 64, 65, 95, 127], 1),
+                                        ([126, 127, 128, 255, 256, 257], 2)])
 def test_decode_attention_fused_rope_append(prior, smax):
     """QK-Norm + RoPE of the new token, its cache append, and attention over the
     cache, in one kernel, against the oracle's functions."""
