@@ -22,7 +22,7 @@ EXPORTS = [
     "q3_bind_memory", "q3_load_weights", "q3_seq_alloc", "q3_seq_reset", "q3_kv_reset",
     "q3_seq_length", "q3_prefill", "q3_decode_step", "q3_set_option", "q3_error_flags",
     "q3_last_error", "q3_sample", "q3_checkpoint_validate", "q3_checkpoint_staging_bytes",
-    "q3_load_safetensors",
+    "q3_load_safetensors", "q3_check_tokens",
     "q3op_embed", "q3op_rmsnorm", "q3op_linear_workspace_bytes", "q3op_linear", "q3op_norm_linear",
     "q3op_rope_workspace_bytes", "q3op_rope_append", "q3op_attention_workspace_bytes",
     "q3op_attention", "q3op_decode_attn_fused_workspace_bytes", "q3op_decode_attn_fused", "q3op_tune",
@@ -115,6 +115,7 @@ def load() -> C.CDLL:
         "q3op_attention": (I32, [I32, VP, I32, i32p, I32, i64p, i32p, i32p, VP, I32, I32, I32, VP, VP,
                                  SZ, VP]),
         "q3op_model_decode_attention": (I32, [VP, I32, I32, i32p, VP]),
+        "q3_check_tokens": (I32, [VP, i32p, I64]),
         "q3op_linear_noalloc": (I32, [I32, I32, VP, I32, VP, I32, I32, VP, I64, VP, VP]),
     }
     for name, (res, args) in sig.items():

@@ -3,7 +3,7 @@
 // weights of a row (w ~ q * s + b), the quantizer, the dequantizer and the
 // single-row decode GEMV that reads the codes directly.
 //
-// Method source: "Laya MLX performance research" (reactapp.top), the
+// Method source: "Investigación de rendimiento de Laya MLX", its
 // quantization section (affine, grouped by 64, 8 or 4 bits, fp16 scales and
 // offsets, weight-only matrix products); "Dentro de un LLM: Inferencia en
 // Python puro para Qwen3-0.6B en MLX", Pasos 3, 5, 6, 7 for the projections

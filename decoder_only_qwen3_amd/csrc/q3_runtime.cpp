@@ -1066,6 +1066,17 @@ q3_status q3_decode_step(q3_model* m, int32_t n, const int32_t* h_slots, const i
   return Q3_OK;
 }
 
+q3_status q3_check_tokens(const q3_model* m, const int32_t* h_tokens, int64_t n) {
+  if (!m) return fail(Q3_E_ARG, "model is NULL");
+  if (n < 0 || (n > 0 && !h_tokens)) return fail(Q3_E_ARG, "bad token array");
+  for (int64_t i = 0; i < n; ++i)
+    if (h_tokens[i] < 0 || h_tokens[i] >= m->cfg.vocab)
+      return fail(Q3_E_ARG, "token " + std::to_string(i) + " has ID " + std::to_string(h_tokens[i]) +
+                                " outside [0, " + std::to_string(m->cfg.vocab) + ")");
+  g_err.clear();
+  return Q3_OK;
+}
+
 q3_status q3_sample(q3_model* m, int32_t n_rows, const float* d_logits, int64_t ld, float temperature,
                     float top_p, const float* d_uniform, int32_t* d_next, void* stream) {
   q3_status st;

@@ -145,7 +145,9 @@ class Q3Model:
         them); returns (logits, next) device tensors."""
         lens = [len(p) for p in prompts]
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        flat = np.concatenate([np.asarray(p, dtype=np.int32) for p in prompts])
+        flat = np.ascontiguousarray(np.concatenate([np.asarray(p, dtype=np.int32) for p in prompts]))
+        # the IDs are on the host here: check them before anything is queued
+        check(self.lib.q3_check_tokens(self.handle, flat.ctypes.data_as(C.POINTER(C.c_int32)), flat.size))
         V = self.dims.vocab
         with torch.cuda.stream(self.stream):
             tok = torch.from_numpy(flat).to(self.device)

@@ -178,9 +178,13 @@ q3_status q3_seq_length(const q3_model* m, int32_t slot, int64_t* out);
  * rounding (chunked prefill).  An empty slot starts at position 0.
  *   h_cu_seqlens: n_seqs+1 non-decreasing offsets, [0] = 0, each length >= 1,
  *                 total T <= max_prefill_tokens.
- *   d_tokens:     int32 [T].  IDs outside [0, vocab) are not checked on the
- *                 host; the kernel zeroes such a row and raises error bit 1
- *                 (see q3_error_flags).
+ *   d_tokens:     int32 [T] in device memory, so IDs are not checked on the
+ *                 host (a caller holding a host copy checks it first with
+ *                 q3_check_tokens).  An ID outside [0, vocab) reaching the
+ *                 kernels gives that row a zero embedding and raises error
+ *                 bit 1 (see q3_error_flags); the call still completes and
+ *                 advances its slots, so their caches then hold meaningless
+ *                 entries: reset them (q3_seq_reset) after bit 1 is seen.
  *   d_logits:     float [n_seqs, vocab] logits of each last position, or
  *                 [T, vocab] with Q3_PREFILL_ALL_LOGITS; may be NULL without
  *                 that flag.
@@ -198,7 +202,9 @@ q3_status q3_prefill(q3_model* m, int32_t n_seqs, const int32_t* h_slots,
 /* One greedy decode step for n_seqs sequences (Paso 9's loop body): token
  * d_tokens[b] goes to slot h_slots[b] at position = that slot's length; its
  * key and value are appended to the cache.
- *   d_tokens: int32 [n_seqs] (typically the previous call's d_next).
+ *   d_tokens: int32 [n_seqs] (typically the previous call's d_next); an ID
+ *             outside [0, vocab) is handled as in q3_prefill (error bit 1,
+ *             the slots still advance).
  *   d_logits: float [n_seqs, vocab] or NULL.
  *   d_next:   int32 [n_seqs].
  * Positions are read from device-resident slot state, so with graphs enabled
@@ -208,6 +214,12 @@ q3_status q3_prefill(q3_model* m, int32_t n_seqs, const int32_t* h_slots,
 q3_status q3_decode_step(q3_model* m, int32_t n_seqs, const int32_t* h_slots,
                          const int32_t* d_tokens, float* d_logits, int32_t* d_next,
                          void* stream);
+
+/* Host-side check of token IDs (Paso 1: IDs index the vocabulary): Q3_OK
+ * when every h_tokens[i], i < n, lies in [0, vocab); Q3_E_ARG naming the first
+ * that does not.  For callers that hold the IDs on the host before copying
+ * them to d_tokens; touches no device state. */
+q3_status q3_check_tokens(const q3_model* m, const int32_t* h_tokens, int64_t n);
 
 /* Temperature + top-p sampling (Paso 8) of n_rows logit rows, e.g. the
  * d_logits of q3_decode_step or q3_prefill; its d_next stays the greedy pick,

@@ -208,7 +208,7 @@ def sample_top_p(logits: np.ndarray, temperature: float, top_p: float, u: float)
 
 
 # ----------------------------------------------------------------------------
-# Weight-only affine group quantization (Laya MLX performance research,
+# Weight-only affine group quantization ("Investigación de rendimiento de Laya MLX",
 # "Cuantización" section: groups of 64 along the input dimension, 8 or 4 bits,
 # fp16 scale and offset per group)
 # ----------------------------------------------------------------------------

@@ -91,3 +91,20 @@ def test_create_and_destroy_without_gpu_and_state_errors():
     assert lib.q3_seq_length(h, 0, C.byref(n)) == mod.Q3_OK and n.value == 0
     assert lib.q3_seq_length(h, 9, C.byref(n)) == mod.Q3_E_ARG
     lib.q3_destroy(h)
+
+
+def test_check_tokens_on_the_host():
+    """q3_check_tokens: every ID in [0, vocab), else Q3_E_ARG naming the first
+    bad one (host only, no device)."""
+    mod, lib = _lib()
+    cfg = _cfg(mod)
+    h = C.c_void_p()
+    assert lib.q3_create(C.byref(cfg), C.byref(h)) == mod.Q3_OK
+    V = cfg.vocab
+    assert lib.q3_check_tokens(h, mod.i32_array([0, 1, V - 1]), 3) == mod.Q3_OK
+    assert lib.q3_check_tokens(h, None, 0) == mod.Q3_OK
+    assert lib.q3_check_tokens(h, mod.i32_array([5, V, 7]), 3) == mod.Q3_E_ARG
+    assert b"token 1" in lib.q3_last_error() and str(V).encode() in lib.q3_last_error()
+    assert lib.q3_check_tokens(h, mod.i32_array([-1]), 1) == mod.Q3_E_ARG
+    assert lib.q3_check_tokens(h, None, 2) == mod.Q3_E_ARG
+    lib.q3_destroy(h)
