@@ -253,7 +253,17 @@ CASES = {
                                                            ARGS.attn_smax),
     "fused_b1_640": lambda lib, r, s: fused_attn_case(lib, "fused_b1_640", [640], r, s, ARGS.attn_smax),
     "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax, pool=3),
+    # the headline workload's final decode state: the 64 ragged prompts of
+    # the benchmark plus 128 decoded keys each, two arenas cycled (cold reads)
+    "fused_ragged64_final": lambda lib, r, s: fused_attn_case(lib, "fused_ragged64_final", _ragged_final(), r, s,
+                                                              ARGS.attn_smax, pool=2),
 }
+
+
+def _ragged_final():
+    import q3synth
+    wl = q3synth.WORKLOADS["q06b_bf16_b64_ragged_d128"]
+    return [int(L) + wl.decode_steps for L in wl.prompt_lengths()]
 
 
 def main():
