@@ -26,6 +26,7 @@
 // its bf16 roundings; downstream of those flips the logits of a two-layer
 // random-init model moved by up to 3e-2 of their RMS.
 #include <algorithm>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -644,16 +645,21 @@ Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int e
   for (int d = 0; d < 8; ++d) r.v[d] = ld16(vp + d * 16 * 32);
 }
 
+// Sequence of each z-index of the grid: blocks are dispatched in z order.
+struct SeqOrder {
+  uint8_t v[Q3_MAX_BATCH];
+};
+
 template <int FW>
 __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
     const float* __restrict__ qkv, SeqBatch sb, const SeqState* __restrict__ st, bf16_t* __restrict__ kv,
     int layer, int n_q, int n_kv, RopeArgs ra, int smax, float* __restrict__ part, uint32_t* __restrict__ cnt,
-    bf16_t* __restrict__ o, float scale_log2) {
+    bf16_t* __restrict__ o, float scale_log2, SeqOrder ord) {
   __shared__ __attribute__((aligned(16))) uint16_t qs[8 * 128];
   __shared__ __attribute__((aligned(16))) uint16_t knew[128], vnew[128];
   __shared__ float wred[FW][8][PSTRIDE];
   __shared__ int last;
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.x, g = blockIdx.y, b = ord.v[blockIdx.z];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, fr = lane & 15, fq = lane >> 4;
   const int group = n_q / n_kv;
   const SeqState s = st[sb.slot[b]];
@@ -1013,36 +1019,63 @@ int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx) {
   return sm < 1 ? 1 : (int)sm;
 }
 
-int fused_attn_smax(int B, int n_kv, int64_t max_cap, bool ragged) {
+AttnPlan fused_attn_plan(int B, int n_kv, int64_t max_cap, const int64_t* ctx) {
+  AttnPlan p;
+  std::memset(&p, 0, sizeof(p));
   int64_t by_len = (max_cap + 127) / 128;
   int64_t want = (256 + (int64_t)B * n_kv - 1) / ((int64_t)B * n_kv);
   int64_t sm = by_len < want ? by_len : want;
+  int64_t maxctx = 1, sumctx = 0;
+  for (int b = 0; b < B; ++b) {
+    maxctx = std::max<int64_t>(maxctx, ctx[b]);
+    sumctx += std::max<int64_t>(1, ctx[b]);
+  }
   // A batch that fills the CUs with one block per (sequence, head) but has
-  // sequences of very different lengths ends on a tail of its longest
-  // blocks; splitting every sequence eight ways evens it out (64 ragged
-  // sequences of 128-8192 keys: 242 -> 211 us per layer on MI355X; equal
-  // lengths stay at one split, where more splits only add merge work).
-  if ((int64_t)B * n_kv >= 256 && ragged) sm = std::min<int64_t>(kRaggedSplits, by_len);
+  // sequences of different lengths ends on a tail of its longest blocks.
+  // Its blocks go longest first, and each sequence is split about
+  // max/mean ways, so that no block holds much more than a mean sequence
+  // (64 sequences of 128-8192 keys on MI355X: 214 us per layer at eight
+  // splits in batch order, 210 at one split longest first, 196 at two;
+  // equal lengths stay at one split, where more splits only add merge work).
+  if ((int64_t)B * n_kv >= 256 && B > 0) {
+    const int64_t r = (2 * maxctx * B + sumctx) / (2 * sumctx);  // max/mean, rounded
+    sm = std::min<int64_t>(by_len, std::min<int64_t>(kRaggedSplits, std::max<int64_t>(1, r)));
+  }
   if (sm > 64) sm = 64;
   if (sm < 1) sm = 1;
   if (g_attn_smax_cap > 0 && sm > g_attn_smax_cap) sm = g_attn_smax_cap;
-  return (int)sm;
+  p.smax = (int)sm;
+  int idx[Q3_MAX_BATCH];
+  for (int b = 0; b < B; ++b) idx[b] = b;
+  std::stable_sort(idx, idx + B, [&](int x, int y) { return ctx[x] > ctx[y]; });
+  for (int b = 0; b < B; ++b) p.order[b] = (uint8_t)idx[b];
+  return p;
 }
 
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
                              int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,
-                             const float* sin_t, int smax, float* part, uint32_t* counters, bf16_t* o,
-                             hipStream_t s) {
+                             const float* sin_t, const AttnPlan& plan, float* part, uint32_t* counters,
+                             bf16_t* o, hipStream_t s) {
   if (sb.n <= 0) return hipSuccess;
+  if (sb.n > Q3_MAX_BATCH || plan.smax < 1 || plan.smax > 64) return hipErrorInvalidValue;
   const int group = n_q / n_kv;
   if (group < 1 || group > 8) return hipErrorInvalidValue;
   const float scale_log2 = kLog2e / sqrtf(128.f);
   RopeArgs ra{qn, kn, cos_t, sin_t, eps};
-  dim3 grid(smax, n_kv, sb.n);
+  // the order must be a permutation: every output row written exactly once
+  static_assert(Q3_MAX_BATCH <= 64, "one bit per sequence below");
+  SeqOrder ord;
+  uint64_t seen = 0;
+  for (int b = 0; b < sb.n; ++b) {
+    if (plan.order[b] >= sb.n || (seen >> plan.order[b] & 1)) return hipErrorInvalidValue;
+    seen |= uint64_t(1) << plan.order[b];
+    ord.v[b] = plan.order[b];
+  }
+  dim3 grid(plan.smax, n_kv, sb.n);
   // Four wavefronts per block: eight measured slower at every batch and
   // context tried (one CU's stream does not grow with more wavefronts).
-  decode_attn_fused_kernel<4><<<grid, 256, 0, s>>>(qkv, sb, st, kv, layer, n_q, n_kv, ra, smax, part, counters, o,
-                                                   scale_log2);
+  decode_attn_fused_kernel<4><<<grid, 256, 0, s>>>(qkv, sb, st, kv, layer, n_q, n_kv, ra, plan.smax, part, counters,
+                                                   o, scale_log2, ord);
   return hipGetLastError();
 }
 

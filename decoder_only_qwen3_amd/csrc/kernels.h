@@ -142,18 +142,24 @@ hipError_t decode_attn(const bf16_t* q, const SeqBatch& sb, const SeqState* st, 
                        int layer, int n_q, int n_kv, int splits, float* part, bf16_t* o,
                        hipStream_t s);
 // Decode attention with QK-Norm + RoPE + cache append folded in; reads the
-// fused projection rows qkv [B][(n_q+2n_kv)*128] float32.  `smax` splits per
-// (sequence, kv head) at most (fused_attn_smax); partials need
+// fused projection rows qkv [B][(n_q+2n_kv)*128] float32.  The plan gives
+// `smax` splits per (sequence, kv head) at most, and the order in which the
+// sequences' blocks are launched (longest context first); partials need
 // B * n_q * smax * 130 floats and `counters` B * n_kv zeroed words (left
-// zeroed by the kernel).
-// ragged: the batch's longest context is at least twice its shortest.
-int fused_attn_smax(int B, int n_kv, int64_t max_cap, bool ragged);
+// zeroed by the kernel).  Results do not depend on the order.
+struct AttnPlan {
+  int smax;
+  uint8_t order[Q3_MAX_BATCH];  // a permutation of 0..B-1
+};
+// ctx[b]: sequence b's context (cached keys + the new one) at planning time;
+// max_cap: the largest slot capacity (bounds the contexts of later steps).
+AttnPlan fused_attn_plan(int B, int n_kv, int64_t max_cap, const int64_t* ctx);
 int fused_attn_smax_max(int B, int n_kv, int64_t max_ctx);  // ignoring the benchmark cap: for sizing
 void decode_attn_set_split_cap(int cap);  // -1 = no cap (benchmarks only)
 hipError_t decode_attn_fused(const float* qkv, const SeqBatch& sb, const SeqState* st, bf16_t* kv, int layer,
                              int n_q, int n_kv, const float* qn, const float* kn, float eps, const float* cos_t,
-                             const float* sin_t, int smax, float* part, uint32_t* counters, bf16_t* o,
-                             hipStream_t s);
+                             const float* sin_t, const AttnPlan& plan, float* part, uint32_t* counters,
+                             bf16_t* o, hipStream_t s);
 hipError_t attn_f32(const float* q, int T, const SeqBatch& sb, const SeqState* st,
                     const float* kv, int layer, int n_q, int n_kv, float* o, hipStream_t s);
 

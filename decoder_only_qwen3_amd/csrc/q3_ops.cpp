@@ -484,15 +484,18 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h
   if (!d_qkv || !d_kv || !d_qn || !d_kn || !d_out || !h_base || !h_cap || !h_len || max_pos <= 0)
     return op_fail(Q3_E_ARG, "bad argument");
   if (n_kv <= 0 || n_q % n_kv != 0 || n_q / n_kv > 8) return op_fail(Q3_E_UNSUPPORTED, "head grouping");
-  int64_t mc = 1, lmax = 1, lmin = INT64_MAX;
+  int64_t mc = 1;
+  int64_t ctx[Q3_MAX_BATCH];
   for (int b = 0; b < n; ++b) {
+    if (h_len[b] < 0) return op_fail(Q3_E_ARG, "negative length");
     if (h_len[b] + 1 > h_cap[b] || h_len[b] + 1 > max_pos) return op_fail(Q3_E_CAPACITY, "position beyond capacity");
     mc = std::max<int64_t>(mc, h_cap[b]);
-    lmax = std::max<int64_t>(lmax, h_len[b] + 1);
-    lmin = std::min<int64_t>(lmin, h_len[b] + 1);
+    ctx[b] = h_len[b] + 1;
   }
-  if (smax <= 0) smax = fused_attn_smax(n, n_kv, mc, lmax >= 2 * lmin);
+  AttnPlan plan = fused_attn_plan(n, n_kv, mc, ctx);
   if (smax > 64) return op_fail(Q3_E_ARG, "smax must be <= 64");
+  if (smax > 0) plan.smax = smax;
+  smax = plan.smax;
   if (!d_ws || ws_bytes < q3op_decode_attn_fused_workspace_bytes(n, n_q, smax, max_pos))
     return op_fail(Q3_E_ARG, "workspace too small");
   char* ws = (char*)d_ws;
@@ -513,7 +516,7 @@ q3_status q3op_decode_attn_fused(const float* d_qkv, int32_t n, const int64_t* h
   OP_TRY(hipMemcpy(cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
   OP_TRY(hipMemcpy(sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
   OP_TRY(decode_attn_fused(d_qkv, sb, (const SeqState*)ws, (bf16_t*)d_kv, 0, n_q, n_kv, d_qn, d_kn, eps, cos_t,
-                           sin_t, smax, part, cnt, (bf16_t*)d_out, s));
+                           sin_t, plan, part, cnt, (bf16_t*)d_out, s));
   return Q3_OK;
 }
 

@@ -258,19 +258,19 @@ q3_status check(hipError_t e, const char* what) {
     if (st_ != Q3_OK) return st_;                      \
   } while (0)
 
-// Key splits per (sequence, kv head) of bf16 decode attention, from the
-// contexts at this call (a recorded graph keeps the split count it was
-// recorded with, which only matters for speed).
-int decode_smax(const q3_model* m, const SeqBatch& sb) {
+// Key splits per (sequence, kv head) of bf16 decode attention and the launch
+// order of the sequences, from the contexts at this call (a recorded graph
+// keeps the plan it was recorded with, which only matters for speed).
+AttnPlan decode_plan(const q3_model* m, const SeqBatch& sb) {
   const q3_config& c = m->cfg;
-  int64_t maxcap = 1, maxctx = 1, minctx = INT64_MAX;
+  int64_t maxcap = 1;
+  int64_t ctx[Q3_MAX_BATCH];
   for (int b = 0; b < sb.n; ++b) {
     const auto& hs = m->slots[sb.slot[b]];
     maxcap = std::max<int64_t>(maxcap, std::min<int64_t>(hs.cap, c.max_positions));
-    maxctx = std::max<int64_t>(maxctx, hs.len + 1);
-    minctx = std::min<int64_t>(minctx, hs.len + 1);
+    ctx[b] = hs.len + 1;
   }
-  return fused_attn_smax(sb.n, c.n_kv_heads, maxcap, maxctx >= 2 * minctx);
+  return fused_attn_plan(sb.n, c.n_kv_heads, maxcap, ctx);
 }
 
 // The transformer blocks of Paso 7 over `T` rows already embedded in x.
@@ -289,7 +289,9 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   RowMap all;
   all.n = -1;
   const bool bf = c.dtype == Q3_BF16;
-  const int smax = decode && bf ? decode_smax(m, sb) : 1;
+  AttnPlan plan;
+  plan.smax = 1;
+  if (decode && bf) plan = decode_plan(m, sb);
   // Batch-1 decode: every projection on the single-row GEMV (RMSNorm fused
   // into q/k/v and gate/up).  Small batches: row GEMV for o and down.
   // Quantized weights: decode reads the codes directly (batch 1: the
@@ -348,7 +350,7 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     // all of it in one kernel; the other paths append first.
     if (bf && decode) {
       LAUNCH(decode_attn_fused(qkv, sb, m->state(), (bf16_t*)m->kv, l, c.n_q_heads, c.n_kv_heads,
-                               m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, smax,
+                               m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, plan,
                                m->WS<float>(L.attn_part), m->WS<uint32_t>(L.attn_cnt), (bf16_t*)ob, s));
     } else {
       LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
@@ -1121,7 +1123,7 @@ q3_status q3op_model_decode_attention(q3_model* m, int32_t layer, int32_t n, con
   const LayerW& lw = m->wl.layers[layer];
   LAUNCH(decode_attn_fused(m->WS<float>(L.qkv), sb, m->state(), (bf16_t*)m->kv, layer, c.n_q_heads, c.n_kv_heads,
                            m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, m->W<float>(m->wl.cos_t),
-                           m->W<float>(m->wl.sin_t), decode_smax(m, sb), m->WS<float>(L.attn_part),
+                           m->W<float>(m->wl.sin_t), decode_plan(m, sb), m->WS<float>(L.attn_part),
                            m->WS<uint32_t>(L.attn_cnt), (bf16_t*)m->WS(L.o), (hipStream_t)stream));
   g_err.clear();
   return Q3_OK;

@@ -574,7 +574,9 @@ def test_rowdot_gemv(M, N, K):
 
 @pytest.mark.parametrize("prior,smax", [([0], 0), ([5, 700], 0), ([1500], 0), ([1500, 40], 3), ([32799], 0),
                                         ([2047, 0, 4100], 0), ([31, 32, 33, 63, 64, 65, 95, 127], 1),
-                                        ([126, 127, 128, 255, 256, 257], 2)])
+                                        ([126, 127, 128, 255, 256, 257], 2),
+                                        # 32 ragged sequences: two splits each, launched longest first
+                                        ([int(x) for x in np.random.default_rng(5).integers(0, 700, 32)], 0)])
 def test_decode_attention_fused_rope_append(prior, smax):
     """QK-Norm + RoPE of the new token, its cache append, and attention over the
     cache, in one kernel, against the oracle's functions."""
