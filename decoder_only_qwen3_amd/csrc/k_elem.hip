@@ -38,6 +38,21 @@ hipError_t embed(int dtype, const int32_t* ids, int n, const void* E, int V, int
   return hipGetLastError();
 }
 
+// Four consecutive outputs as one store (16 bytes float32, 8 bytes bf16).
+template <typename T>
+Q3_DEV void store4(T* p, float a, float b, float c, float d);
+template <>
+Q3_DEV void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+}
+template <>
+Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  u32x2 w;
+  w[0] = pack_bf2(a, b);
+  w[1] = pack_bf2(c, d);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+
 // ---------------------------------------------------------------- Paso 3
 // One wavefront per row: out = x * rsqrt(mean(x^2) + eps) * w.  H % 256 == 0.
 template <typename Tout>
@@ -67,10 +82,56 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// The same with the row held in registers (NV float4 per lane, H = 256 NV):
+// x and w are loaded once, all loads issued before the reduction, and each
+// lane writes its four outputs with one store.  On MI355X a launch over 32-64
+// decode rows is one memory round trip plus the launch itself, which is what
+// this form keeps it to.
+template <typename Tout, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* __restrict__ x, int rows, RowMap map,
+                                                          const float* __restrict__ w, float eps,
+                                                          Tout* __restrict__ out) {
+  constexpr int H = 256 * NV;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = map.n >= 0 ? map.row[r] : r;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)src * H);
+  const float4* wr = reinterpret_cast<const float4*>(w);
+  float4 v[NV], g[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = xr[lane + 64 * i];
+    g[i] = wr[lane + 64 * i];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  Tout* o = out + (int64_t)r * H;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    store4<Tout>(o + 4 * (lane + 64 * i), v[i].x * inv * g[i].x, v[i].y * inv * g[i].y, v[i].z * inv * g[i].z,
+                 v[i].w * inv * g[i].w);
+}
+
 hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, const float* w,
                    int H, float eps, void* out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((rows + 3) / 4);
+#define Q3_RMS_REG(NV)                                                                                   \
+  do {                                                                                                   \
+    if (out_dtype == BF16)                                                                               \
+      rmsnorm_reg_kernel<bf16_t, NV><<<grid, 256, 0, s>>>(x, rows, map, w, eps, (bf16_t*)out);           \
+    else                                                                                                 \
+      rmsnorm_reg_kernel<float, NV><<<grid, 256, 0, s>>>(x, rows, map, w, eps, (float*)out);             \
+    return hipGetLastError();                                                                            \
+  } while (0)
+  if (H == 1024) Q3_RMS_REG(4);
+  if (H == 512) Q3_RMS_REG(2);
+  if (H == 2048) Q3_RMS_REG(8);
+#undef Q3_RMS_REG
   if (out_dtype == BF16)
     rmsnorm_kernel<bf16_t><<<grid, 256, 0, s>>>(x, rows, map, w, H, eps, (bf16_t*)out);
   else
@@ -87,19 +148,6 @@ hipError_t rmsnorm(int out_dtype, const float* x, int rows, const RowMap& map, c
 //              pair rotation by pos * theta^(-i/64) read from the cos/sin table;
 //              queries go to q_out [T][n_q][128], keys to the cache row `pos`.
 //   value:     (decode) stored unchanged into the cache's value block.
-template <typename T>
-Q3_DEV void store4(T* p, float a, float b, float c, float d);
-template <>
-Q3_DEV void store4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
-}
-template <>
-Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
-  u32x2 w;
-  w[0] = pack_bf2(a, b);
-  w[1] = pack_bf2(c, d);
-  *reinterpret_cast<u32x2*>(p) = w;
-}
 
 // Prefill values: block (64-position tile of one sequence, kv head g).  Tiles
 // are aligned to positions (tile i covers positions 64i .. 64i + 63), so a
