@@ -478,8 +478,8 @@ __global__ __launch_bounds__(1024) void argmax_finish_kernel(const float* __rest
     int ix[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      v[u] = pval[(int64_t)(j + u * blockDim.x) * M + m];
-      ix[u] = pidx[(int64_t)(j + u * blockDim.x) * M + m];
+      v[u] = pval[(int64_t)m * nblocks + j + u * blockDim.x];
+      ix[u] = pidx[(int64_t)m * nblocks + j + u * blockDim.x];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -488,8 +488,8 @@ __global__ __launch_bounds__(1024) void argmax_finish_kernel(const float* __rest
     }
   }
   for (; j < nblocks; j += blockDim.x) {
-    const float v = pval[(int64_t)j * M + m];
-    const int i = pidx[(int64_t)j * M + m];
+    const float v = pval[(int64_t)m * nblocks + j];
+    const int i = pidx[(int64_t)m * nblocks + j];
     finite &= __builtin_isfinite(v) || i < 0;
     if (i >= 0) better(bv, bi, v, i);
   }

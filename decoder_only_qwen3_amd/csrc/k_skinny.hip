@@ -238,8 +238,8 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
         if (bi < 0 || v > bv) { bv = v; bi = row0 + nl; }
         if (!__builtin_isfinite(v)) { bv = v; bi = row0 + nl; break; }
       }
-      amax_val[(int64_t)blockIdx.x * M + m] = bv;
-      amax_idx[(int64_t)blockIdx.x * M + m] = bi;
+      amax_val[(int64_t)m * gridDim.x + blockIdx.x] = bv;  // [M][blocks]: each row's partials contiguous
+      amax_idx[(int64_t)m * gridDim.x + blockIdx.x] = bi;
     }
   } else {
     for (int e = threadIdx.x; e < NE; e += blockDim.x) {

@@ -70,8 +70,8 @@ hipError_t sample_top_p(const float* logits, int64_t ld, int n, int V, float tem
                         const float* uniform, int32_t* next, uint32_t* err, void* ws, hipStream_t s);
 hipError_t argmax_rows(const float* logits, int64_t ld, const RowMap& rows, int V, int32_t* next,
                        uint32_t* err, hipStream_t s);
-// Reduce per-block (max, index) partials of EPI_ARGMAX into next[m], then
-// advance the lengths of the sequences of `sb` (decode: +1; prefill: = prior + length).
+// Reduce per-block (max, index) partials of EPI_ARGMAX ([M][nblocks]) into
+// next[m], then advance the lengths of the sequences of `sb` (decode: +1; prefill: = prior + length).
 hipError_t argmax_finish(const float* pval, const int32_t* pidx, int nblocks, int M, int32_t* next,
                          const SeqBatch& sb, SeqState* st, uint32_t* err, hipStream_t s);
 hipError_t seq_advance(const SeqBatch& sb, SeqState* st, hipStream_t s);
@@ -103,7 +103,7 @@ int skinny_argmax_blocks(int N);
 // M <= 64 rows times W[N,K]^T (bf16).  gnorm == nullptr: X is bf16 [M][K].
 // gnorm != nullptr (M <= 64): X is the float32 residual [M][K] and the kernel
 // applies RMSNorm with weight gnorm and eps first.  EPI_ARGMAX also writes
-// per-block (max, index) partials, N/16 blocks x M.
+// per-block (max, index) partials, [M][N/16] (each row's partials contiguous).
 hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
                        float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s,
                        float* split_part = nullptr, uint32_t* split_cnt = nullptr);
