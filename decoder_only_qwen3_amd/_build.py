@@ -16,7 +16,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libq3.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["k_elem.hip", "k_gemm.hip", "k_skinny.hip", "k_rowgemv.hip", "k_attn.hip", "k_sample.hip", "k_quant.hip", "checkpoint.cpp", "q3_runtime.cpp", "q3_ops.cpp"]
+SOURCES = ["k_elem.hip", "k_gemm.hip", "k_skinny.hip", "k_head.hip", "k_rowgemv.hip", "k_attn.hip", "k_sample.hip", "k_quant.hip", "checkpoint.cpp", "q3_runtime.cpp", "q3_ops.cpp"]
 
 # Packed fp32 VALU forms are kept out of the device code on purpose.
 # MFMA accumulators live in ordinary VGPRs: in the accumulation-register form

@@ -107,6 +107,14 @@ int skinny_argmax_blocks(int N);
 hipError_t skinny_bf16(int epi, const void* X, int M, const bf16_t* W, int N, int K, const float* gnorm,
                        float eps, void* out, int64_t ldo, float* amax_val, int32_t* amax_idx, hipStream_t s,
                        float* split_part = nullptr, uint32_t* split_cnt = nullptr);
+// Streaming lm_head (k_head.hip): M <= 64 rows of bf16 X [M][K] times W[N,K]^T,
+// float32 logits out [M][ldo], and per-block (max, index) partials
+// [M][headstream_blocks(N)] for argmax_finish.  Needs N % 16 == 0, K in
+// {512, 1024, 1536, 2048} and the rows of X (padded to 16) in LDS.
+bool headstream_ok(int M, int N, int K);
+int headstream_blocks(int N);
+hipError_t headstream_bf16(const bf16_t* X, int M, const bf16_t* W, int N, int K, float* out, int64_t ldo,
+                           float* amax_val, int32_t* amax_idx, hipStream_t s);
 // Split-K for RESADD with few row groups: K slices per row group (1 = none)
 // and the float workspace the slices' partial sums need (split_part); the
 // split_cnt array holds N/16 counters that must be zero before the first call

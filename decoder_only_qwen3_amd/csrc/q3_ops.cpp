@@ -93,6 +93,20 @@ q3_status skinny_op(int epi, const void* X, int M, const float* gnorm, float eps
   return Q3_OK;
 }
 
+// Partials of the streaming lm_head: [M][blocks] (max, index), an error word.
+struct HeadWs {
+  size_t err, amax_val, amax_idx, total;
+};
+HeadWs head_ws(int M, int N) {
+  HeadWs w;
+  const size_t parts = (size_t)std::max(M, 1) * headstream_blocks(N);
+  w.err = 0;
+  w.amax_val = al(16);
+  w.amax_idx = w.amax_val + al(parts * 4);
+  w.total = w.amax_idx + al(parts * 4);
+  return w;
+}
+
 struct RowWs {
   size_t err, amax_val, amax_idx, total;
 };
@@ -166,6 +180,7 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
 
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K) {
   if (kernel == Q3OP_SKINNY) return skinny_ws(M, N, K).total;
+  if (kernel == Q3OP_HEADSTREAM) return head_ws(M, N).total;
   if (kernel == Q3OP_ROWGEMV) return row_ws(N).total;
   if (kernel == Q3OP_GEMM && epi == EPI_RESADD) return gemm_ws(M, N, K).total;
   return 256;
@@ -178,7 +193,7 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   if (!d_x || !d_w || !d_out || M < 0 || N <= 0 || K <= 0) return op_fail(Q3_E_ARG, "bad argument");
   if (epi < 0 || epi > 3) return op_fail(Q3_E_ARG, "bad epilogue");
   if (epi == EPI_ARGMAX && M > Q3_MAX_BATCH) return op_fail(Q3_E_ARG, "logits epilogue needs M <= 64");
-  if (epi == EPI_ARGMAX && !d_next && kernel != Q3OP_SKINNY && kernel != Q3OP_ROWGEMV)
+  if (epi == EPI_ARGMAX && !d_next && kernel != Q3OP_SKINNY && kernel != Q3OP_ROWGEMV && kernel != Q3OP_HEADSTREAM)
     return op_fail(Q3_E_ARG, "logits epilogue needs d_next");
   RowMap rows;
   rows.n = M;
@@ -219,6 +234,24 @@ q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, c
   if (kernel == Q3OP_SKINNY) {
     if (M > Q3_MAX_BATCH) return op_fail(Q3_E_UNSUPPORTED, "the weight-streaming kernel takes M <= 64");
     return skinny_op(epi, d_x, M, nullptr, 0.f, d_w, N, K, d_out, ldo, d_next, d_ws, ws_bytes, s);
+  }
+  if (kernel == Q3OP_HEADSTREAM) {
+    if ((epi != EPI_STORE && epi != EPI_ARGMAX) || !headstream_ok(M, N, K))
+      return op_fail(Q3_E_UNSUPPORTED,
+                     "the streaming lm_head takes epilogue 0 or 3, M <= 64, N % 16 == 0, K in {512, 1024, 1536, "
+                     "2048} and 16 * ceil(M/16) rows of K bf16 within 156 KiB");
+    const HeadWs w = head_ws(M, N);
+    if (!d_ws || ws_bytes < w.total) return op_fail(Q3_E_ARG, "workspace smaller than q3op_linear_workspace_bytes");
+    char* ws = (char*)d_ws;
+    OP_TRY(headstream_bf16((const bf16_t*)d_x, M, (const bf16_t*)d_w, N, K, (float*)d_out, ldo,
+                           (float*)(ws + w.amax_val), (int32_t*)(ws + w.amax_idx), s));
+    if (epi == EPI_ARGMAX && d_next) {
+      SeqBatch none;
+      std::memset(&none, 0, sizeof(none));
+      OP_TRY(argmax_finish((const float*)(ws + w.amax_val), (const int32_t*)(ws + w.amax_idx), headstream_blocks(N),
+                           M, d_next, none, nullptr, (uint32_t*)(ws + w.err), s));
+    }
+    return Q3_OK;
   }
   if (kernel == Q3OP_ROWGEMV) {
     if (!rowgemv_ok(M, K)) return op_fail(Q3_E_UNSUPPORTED, "the single-row GEMV takes M = 1, K = 512 * {1,2,4,6,8}");

@@ -442,6 +442,14 @@ q3_status enqueue_head(q3_model* m, const RowMap& rows, int nrows, const SeqBatc
                         m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
     LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), rowgemv_argmax_blocks(c.vocab, c.hidden),
                          nrows, d_next, sb, m->state(), m->err(), s));
+  } else if (c.dtype == Q3_BF16 && nrows > 1 && headstream_ok(nrows, c.vocab, c.hidden)) {
+    // several rows: the rows stay on chip and the vocabulary streams past
+    // them once (the weight-streaming kernel would read all rows again for
+    // every 16 vocabulary rows)
+    LAUNCH(headstream_bf16((const bf16_t*)h, nrows, m->W<bf16_t>(m->wl.head), c.vocab, c.hidden, logits, c.vocab,
+                           m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), s));
+    LAUNCH(argmax_finish(m->WS<float>(L.amax_val), m->WS<int32_t>(L.amax_idx), headstream_blocks(c.vocab), nrows,
+                         d_next, sb, m->state(), m->err(), s));
   } else if (c.dtype == Q3_BF16) {
     LAUNCH(skinny_bf16(EPI_ARGMAX, fuse_norm ? (const void*)x : h, nrows, m->W<bf16_t>(m->wl.head), c.vocab,
                        c.hidden, fuse_norm ? m->W<float>(m->wl.final_norm) : nullptr, c.rms_eps, logits, c.vocab,

@@ -220,6 +220,12 @@ CASES = {
     "gate_up": lambda lib, r, s: linear_case(lib, "gate_up", 2, 1, 2 * I, H, r, s),
     "down": lambda lib, r, s: linear_case(lib, "down", 1, 1, H, I, r, s),
     "lm_head_b64": lambda lib, r, s: linear_case(lib, "lm_head_b64", 3, 64, V, H, r, s),
+    # batched lm_head on the streaming kernel (the decode step's choice for 2-64 rows)
+    "head_b64": lambda lib, r, s: linear_case(lib, "head_b64", 3, 64, V, H, r, s, kernel=5, pool=2),
+    "head_b32": lambda lib, r, s: linear_case(lib, "head_b32", 3, 32, V, H, r, s, kernel=5, pool=2),
+    "head_b8": lambda lib, r, s: linear_case(lib, "head_b8", 3, 8, V, H, r, s, kernel=5, pool=2),
+    "sk_head_b32": lambda lib, r, s: linear_case(lib, "sk_head_b32", 3, 32, V, H, r, s, kernel=1, pool=2),
+    "sk_head_b8": lambda lib, r, s: linear_case(lib, "sk_head_b8", 3, 8, V, H, r, s, kernel=1, pool=2),
     "gemm_qkv_32k": lambda lib, r, s: linear_case(lib, "gemm_qkv_32k", 0, 32768, Q + 2 * KVW, H, r, s, kernel=0),
     "gemm_gate_up_32k": lambda lib, r, s: linear_case(lib, "gemm_gate_up_32k", 2, 32768, 2 * I, H, r, s, kernel=0),
     "gemm_down_32k": lambda lib, r, s: linear_case(lib, "gemm_down_32k", 1, 32768, H, I, r, s, kernel=0),

@@ -52,13 +52,17 @@ q3_status q3op_rmsnorm(int32_t out_dtype, const float* d_x, int32_t rows, const 
  * kernel 3 = bf16 row-per-wavefront GEMV (decode with M <= 4, epi 0 or 1,
  * K a multiple of 512);
  * kernel 4 = bf16 single-row GEMV (M = 1, epi 0-3, K = 512 * {1,2,4,6,8};
- * SwiGLU needs N % 32 == 0; out is dense, ldo is ignored).
+ * SwiGLU needs N % 32 == 0; out is dense, ldo is ignored);
+ * kernel 5 = bf16 streaming lm_head (epi 0 or 3, M <= 64, N % 16 == 0, K in
+ * {512, 1024, 1536, 2048}, 16 * ceil(M/16) rows of K bf16 within 156 KiB; the
+ * rows of X stay on chip while the weight rows stream past them once).
  * bf16 kernels take bf16 X and W. */
 #define Q3OP_GEMM 0
 #define Q3OP_SKINNY 1
 #define Q3OP_GEMV_F32 2
 #define Q3OP_ROWDOT 3  /* bf16 row-per-wavefront GEMV (decode, M <= 4, epi 0-1) */
 #define Q3OP_ROWGEMV 4 /* bf16 single-row GEMV (decode batch 1, epi 0-3) */
+#define Q3OP_HEADSTREAM 5 /* bf16 streaming lm_head (decode batches, epi 0 or 3) */
 size_t q3op_linear_workspace_bytes(int32_t kernel, int32_t epi, int32_t M, int32_t N, int32_t K);
 q3_status q3op_linear(int32_t kernel, int32_t epi, const void* d_x, int32_t M, const void* d_w, int32_t N,
                       int32_t K, void* d_out, int64_t ldo, int32_t* d_next, void* d_ws, size_t ws_bytes,

@@ -14,7 +14,7 @@ from oracle import attention_rows, rms_norm, rope_cos_sin, rope_rotate, silu, to
 pytestmark = pytest.mark.gpu
 
 EPI_STORE, EPI_RESADD, EPI_SWIGLU, EPI_ARGMAX = 0, 1, 2, 3
-GEMM, SKINNY, GEMV_F32, ROWDOT, ROWGEMV = 0, 1, 2, 3, 4
+GEMM, SKINNY, GEMV_F32, ROWDOT, ROWGEMV, HEADSTREAM = 0, 1, 2, 3, 4, 5
 BF16, F32 = 1, 0
 
 
@@ -83,7 +83,7 @@ def _linear(kernel, epi, X, W, out_init=None, ldo=None, want_next=False):
     mod, lib = ops()
     M, K = X.shape
     N = W.shape[0]
-    bf = kernel in (GEMM, SKINNY, ROWDOT, ROWGEMV)
+    bf = kernel in (GEMM, SKINNY, ROWDOT, ROWGEMV, HEADSTREAM)
     dx = dev_bf16(X) if bf else dev_f32(X)
     dw = dev_bf16(W) if bf else dev_f32(W)
     if epi == EPI_SWIGLU:
@@ -248,7 +248,7 @@ def test_gemv_f32_store_and_residual(M):
 
 
 @pytest.mark.parametrize("kernel,M", [(SKINNY, 1), (SKINNY, 7), (SKINNY, 64), (GEMM, 3), (GEMV_F32, 2),
-                                      (ROWGEMV, 1)])
+                                      (ROWGEMV, 1), (HEADSTREAM, 2), (HEADSTREAM, 17), (HEADSTREAM, 64)])
 def test_logits_and_argmax(kernel, M):
     rng = np.random.default_rng(300 + M)
     V, H = 8192, 1024
@@ -268,6 +268,40 @@ def test_logits_and_argmax(kernel, M):
         assert nxt[m] == int(np.argmax(got[m]))
         top = int(np.argmax(ref[m]))
         assert ref[m][top] - ref[m][nxt[m]] <= 1e-5 * np.sqrt(np.mean(ref[m] ** 2))
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_headstream_full_vocabulary(M):
+    """The streaming lm_head at the model's vocabulary (151,936 rows, several
+    16-row groups per wavefront): logits against the float64 product, and the
+    greedy pick with copies of each row's winner planted at higher and lower
+    indices in other blocks (the lowest index must win)."""
+    rng = np.random.default_rng(900 + M)
+    V, H = 151936, 1024
+    X = rand_bf16(rng, (M, H))
+    E = rand_bf16(rng, (V, H), 0.02)
+    ref = X.astype(np.float64) @ E.astype(np.float64).T
+    win = int(np.argmax(ref[0]))
+    E[(win + 77777) % V] = E[win]
+    E[(win + 4096) % V] = E[win]
+    ref = X.astype(np.float64) @ E.astype(np.float64).T
+    got, nxt = _linear(HEADSTREAM, EPI_ARGMAX, X, E, want_next=True)
+    assert _rel(got, ref) < 2e-5
+    for m in range(M):
+        assert nxt[m] == int(np.argmax(got[m])), m
+    assert nxt[0] == min(win, (win + 77777) % V, (win + 4096) % V)
+
+
+def test_headstream_rejects_unsupported_shapes():
+    _, lib = ops()
+    dummy = torch.zeros(16, dtype=torch.int32, device="cuda:0")
+    ws = _ws(1 << 16)
+    p = dummy.data_ptr()
+    assert lib.q3op_linear(HEADSTREAM, EPI_STORE, p, 65, p, 4096, 1024, p, 4096, None, ws.data_ptr(), ws.numel(), None) != 0
+    assert lib.q3op_linear(HEADSTREAM, EPI_STORE, p, 8, p, 4100, 1024, p, 4100, None, ws.data_ptr(), ws.numel(), None) != 0
+    assert lib.q3op_linear(HEADSTREAM, EPI_STORE, p, 8, p, 4096, 1000, p, 4096, None, ws.data_ptr(), ws.numel(), None) != 0
+    assert lib.q3op_linear(HEADSTREAM, EPI_STORE, p, 8, p, 4096, 768, p, 4096, None, ws.data_ptr(), ws.numel(), None) != 0
+    assert lib.q3op_linear(HEADSTREAM, EPI_RESADD, p, 8, p, 4096, 1024, p, 4096, None, ws.data_ptr(), ws.numel(), None) != 0
 
 
 # ---------------------------------------------------------------- Pasos 4-5: QK-Norm, RoPE, cache append
