@@ -174,6 +174,60 @@ Q3_DEV int seq_of_token(const SeqBatch& sb, int t) {
   return lo;
 }
 
+// Four consecutive outputs as one store (16 bytes float32, 8 bytes bf16).
+template <typename T>
+Q3_DEV void store4(T* p, float a, float b, float c, float d);
+template <>
+Q3_DEV void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+}
+template <>
+Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  u32x2 w;
+  w[0] = pack_bf2(a, b);
+  w[1] = pack_bf2(c, d);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+
+// QK-Norm + rotate-half RoPE of one 128-wide query or key head, spread over
+// 16 lanes (lane j holds dims 4j..4j+3 in x and 64+4j..64+4j+3 in y, i.e.
+// four whole RoPE pairs): RMSNorm over the head with weight w, then the pair
+// rotation by the position's angles (cos_t/sin_t rows of 64), stored at dst.
+// Every kernel that does this step calls these functions, so the paths round
+// identically.
+struct RopeIn {
+  float4 wa, wc, cs, sn;
+};
+Q3_DEV RopeIn rope_inputs(const float* __restrict__ w, const float* __restrict__ cos_t,
+                          const float* __restrict__ sin_t, int pos, int j) {
+  RopeIn in;
+  in.wa = *reinterpret_cast<const float4*>(w + 4 * j);
+  in.wc = *reinterpret_cast<const float4*>(w + 64 + 4 * j);
+  in.cs = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * 64 + 4 * j);
+  in.sn = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * 64 + 4 * j);
+  return in;
+}
+template <typename T>
+Q3_DEV void qk_norm_rope_apply(float4 x, float4 y, const RopeIn& in, float eps, int j, T* __restrict__ dst) {
+  float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+  const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
+  const float4 wa = in.wa, wc = in.wc, cs = in.cs, sn = in.sn;
+  x = float4{x.x * inv * wa.x, x.y * inv * wa.y, x.z * inv * wa.z, x.w * inv * wa.w};
+  y = float4{y.x * inv * wc.x, y.y * inv * wc.y, y.z * inv * wc.z, y.w * inv * wc.w};
+  store4<T>(dst + 4 * j, x.x * cs.x - y.x * sn.x, x.y * cs.y - y.y * sn.y, x.z * cs.z - y.z * sn.z,
+            x.w * cs.w - y.w * sn.w);
+  store4<T>(dst + 64 + 4 * j, x.x * sn.x + y.x * cs.x, x.y * sn.y + y.y * cs.y, x.z * sn.z + y.z * cs.z,
+            x.w * sn.w + y.w * cs.w);
+}
+template <typename T>
+Q3_DEV void qk_norm_rope_store(float4 x, float4 y, const float* __restrict__ w, float eps,
+                               const float* __restrict__ cos_t, const float* __restrict__ sin_t, int pos, int j,
+                               T* __restrict__ dst) {
+  qk_norm_rope_apply<T>(x, y, rope_inputs(w, cos_t, sin_t, pos, j), eps, j, dst);
+}
+
 // Error bits raised by kernels (read back by q3_error_flags).
 #define Q3_ERRBIT_TOKEN 1u
 #define Q3_ERRBIT_NONFINITE 2u

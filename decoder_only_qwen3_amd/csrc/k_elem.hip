@@ -38,20 +38,6 @@ hipError_t embed(int dtype, const int32_t* ids, int n, const void* E, int V, int
   return hipGetLastError();
 }
 
-// Four consecutive outputs as one store (16 bytes float32, 8 bytes bf16).
-template <typename T>
-Q3_DEV void store4(T* p, float a, float b, float c, float d);
-template <>
-Q3_DEV void store4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
-}
-template <>
-Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
-  u32x2 w;
-  w[0] = pack_bf2(a, b);
-  w[1] = pack_bf2(c, d);
-  *reinterpret_cast<u32x2*>(p) = w;
-}
 
 // ---------------------------------------------------------------- Paso 3
 // One wavefront per row: out = x * rsqrt(mean(x^2) + eps) * w.  H % 256 == 0.
@@ -172,9 +158,20 @@ Q3_DEV int vt_seq(const VtTiles& tt, int n, int tix) {
   return lo;
 }
 
-template <typename T>
-Q3_DEV void vt_append_tile(const float* __restrict__ qkv, const SeqBatch& sb, const VtTiles& tt,
-                           const SeqState* __restrict__ st, T* __restrict__ kv, int layer, int n_q, int n_kv,
+// Four values of a value row as float32 (bf16 sources widen exactly).
+Q3_DEV float4 load4v(const float* p) { return *reinterpret_cast<const float4*>(p); }
+Q3_DEV float4 load4v(const bf16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return float4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+// Value rows of the call's tokens: token t's value head g at
+// vsrc + t * vstride + g * 128 (float32 projection rows, or the bf16 values
+// the fused projection epilogue writes).
+template <typename T, typename S>
+Q3_DEV void vt_append_tile(const S* __restrict__ vsrc, int64_t vstride, const SeqBatch& sb, const VtTiles& tt,
+                           const SeqState* __restrict__ st, T* __restrict__ kv, int layer, int n_kv,
                            uint16_t* __restrict__ vh, int64_t vh_keys, int tix, int g) {
   __shared__ T tile[Q3_HEAD_DIM][VT_TILE + 16 / sizeof(T)];
   const int b = vt_seq(tt, sb.n, tix);
@@ -182,8 +179,7 @@ Q3_DEV void vt_append_tile(const float* __restrict__ qkv, const SeqBatch& sb, co
   const int p0 = (tt.first[b] + tix - tt.tile_cu[b]) * VT_TILE;  // first position of the tile
   // new positions in the tile: p0 + lo .. p0 + n - 1
   const int lo = max(P - p0, 0), n = min(VT_TILE, P + L - p0);
-  const int units = n_q + 2 * n_kv;
-  const float* src = qkv + (int64_t)(sb.cu[b] + p0 - P) * units * Q3_HEAD_DIM + (int64_t)(n_q + n_kv + g) * Q3_HEAD_DIM;
+  const S* src = vsrc + (int64_t)(sb.cu[b] + p0 - P) * vstride + (int64_t)g * Q3_HEAD_DIM;
   // read: thread -> (token r0 + 8i, 4 dims); 256 threads cover 8 tokens per
   // pass, and all eight passes' loads are issued before the first LDS store
   const int c4 = (threadIdx.x & 31) * 4, r0 = threadIdx.x >> 5;
@@ -191,7 +187,7 @@ Q3_DEV void vt_append_tile(const float* __restrict__ qkv, const SeqBatch& sb, co
 #pragma unroll
   for (int i = 0; i < VT_TILE / 8; ++i) {
     const int r = r0 + 8 * i;
-    if (r >= lo && r < n) v[i] = *reinterpret_cast<const float4*>(src + (int64_t)r * units * Q3_HEAD_DIM + c4);
+    if (r >= lo && r < n) v[i] = load4v(src + (int64_t)r * vstride + c4);
   }
 #pragma unroll
   for (int i = 0; i < VT_TILE / 8; ++i) {
@@ -252,7 +248,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
   // block.
   if ((int)blockIdx.x >= rope_blocks) {
     const int i = (int)blockIdx.x - rope_blocks;
-    vt_append_tile<T>(qkv, sb, tt, st, kv, layer, n_q, n_kv, vh, vh_keys, i / n_kv, i % n_kv);
+    vt_append_tile<T, float>(qkv + (int64_t)(n_q + n_kv) * Q3_HEAD_DIM, (int64_t)(n_q + 2 * n_kv) * Q3_HEAD_DIM, sb,
+                             tt, st, kv, layer, n_kv, vh, vh_keys, i / n_kv, i % n_kv);
     return;
   }
   // Each 16-lane group takes ROPE_UPG heads (16 apart), loading all of them
@@ -285,28 +282,14 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
       if (j == 0) atomicOr(err, 4u);
       continue;
     }
-    float4 x = a[k], y = c[k];
+    const float4 x = a[k], y = c[k];
     if (u < n_q + n_kv) {
-      const float* w = u < n_q ? qn : kn;
-      float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
-      const float inv = rsqrtf(ss * (1.f / Q3_HEAD_DIM) + eps);
-      const float4 wa = *reinterpret_cast<const float4*>(w + 4 * j);
-      const float4 wc = *reinterpret_cast<const float4*>(w + 64 + 4 * j);
-      x = float4{x.x * inv * wa.x, x.y * inv * wa.y, x.z * inv * wa.z, x.w * inv * wa.w};
-      y = float4{y.x * inv * wc.x, y.y * inv * wc.y, y.z * inv * wc.z, y.w * inv * wc.w};
-      const float4 cs = *reinterpret_cast<const float4*>(cos_t + (int64_t)pos * 64 + 4 * j);
-      const float4 sn = *reinterpret_cast<const float4*>(sin_t + (int64_t)pos * 64 + 4 * j);
       T* dst;
       if (u < n_q)
         dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
       else
         dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
-      store4<T>(dst + 4 * j, x.x * cs.x - y.x * sn.x, x.y * cs.y - y.y * sn.y, x.z * cs.z - y.z * sn.z,
-                x.w * cs.w - y.w * sn.w);
-      store4<T>(dst + 64 + 4 * j, x.x * sn.x + y.x * cs.x, x.y * sn.y + y.y * cs.y, x.z * sn.z + y.z * cs.z,
-                x.w * sn.w + y.w * cs.w);
+      qk_norm_rope_store<T>(x, y, u < n_q ? qn : kn, eps, cos_t, sin_t, pos, j, dst);
     } else {
       T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
       const float av[4] = {x.x, x.y, x.z, x.w}, cv[4] = {y.x, y.y, y.z, y.w};
@@ -408,6 +391,37 @@ hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, cons
   dim3 grid((unsigned)tt.tile_cu[sb.n], n_kv);
   vstage_kernel<<<grid, 256, 0, s>>>(sb, tt, st, kv, layer, n_kv, vstage, vstage_keys(sb));
   return hipGetLastError();
+}
+
+// The value half of Pasos 4-5 for a prefill whose projection epilogue has
+// already normalised, rotated and stored the queries and keys: the bf16 value
+// rows v [T][n_kv][128] go into the cache's transposed value blocks (and the
+// fp16 staging of the flash kernel), as the trailing blocks of
+// rope_append_kernel do from the float32 rows.
+__global__ __launch_bounds__(256) void vt_append_kernel(const bf16_t* __restrict__ v, SeqBatch sb, VtTiles tt,
+                                                        const SeqState* __restrict__ st, bf16_t* __restrict__ kv,
+                                                        int layer, int n_kv, uint16_t* __restrict__ vh,
+                                                        int64_t vh_keys) {
+  const int i = blockIdx.x;
+  vt_append_tile<bf16_t, bf16_t>(v, (int64_t)n_kv * Q3_HEAD_DIM, sb, tt, st, kv, layer, n_kv, vh, vh_keys, i / n_kv,
+                                 i % n_kv);
+}
+
+hipError_t vt_append_bf16(const bf16_t* v, int T, const SeqBatch& sb, SeqState* st, bf16_t* kv, int layer, int n_kv,
+                          uint16_t* vstage, hipStream_t s) {
+  if (T <= 0 || sb.decode) return hipSuccess;
+  const VtTiles tt = vt_tiles(sb, false);
+  const bool cont = has_prior(sb);
+  const int64_t blocks = (int64_t)tt.tile_cu[sb.n] * n_kv;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks > 0) {
+    vt_append_kernel<<<(unsigned)blocks, 256, 0, s>>>(v, sb, tt, st, kv, layer, n_kv, cont ? nullptr : vstage,
+                                                      vstage_keys(sb));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!cont || !vstage) return hipSuccess;
+  return vstage_from_cache(T, sb, st, kv, layer, n_kv, vstage, s);
 }
 
 // ---------------------------------------------------------------- Paso 8

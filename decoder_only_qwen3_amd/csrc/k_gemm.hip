@@ -17,6 +17,8 @@
 // Large problems use 256x256 tiles on 16 wavefronts with the pipeline,
 // small ones 64x64 tiles on 4 wavefronts.  The products run as C^T = W . A^T
 // so that each lane writes four consecutive outputs (one 16-byte store).
+#include <cstring>
+
 #include "kernels.h"
 
 namespace q3k {
@@ -279,17 +281,26 @@ Q3_DEV void xcd_tile(int TM, int TN, int& tm, int& tn) {
   tn = r / rows;
 }
 
+// Epilogue of the fused prefill q/k/v projection (gemm_qkv_rope), beside the
+// public EPI_* values.
+constexpr int EPI_QKROPE = 16;
+constexpr int kRopeStageStride = 256 + 4;  // floats per staged row (padded against LDS bank conflicts)
+
 template <int EPI, int WM, int WN, int GM, int GN, int NS, bool DB>
 __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __restrict__ A, int M,
                                                                const bf16_t* __restrict__ W, int N, int K,
-                                                               void* __restrict__ out, int64_t ldo) {
+                                                               void* __restrict__ out, int64_t ldo,
+                                                               QkvRopeArgs ra) {
   constexpr int NW = GM * GN;
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN;
   constexpr int GA = BM / 16, GB = BN / 16;  // 1 KiB load groups per slice
   static_assert((GA + GB) % NW == 0, "load groups must split evenly over the wavefronts");
   constexpr int LPW = (GA + GB) / NW;        // load instructions per wavefront per slice
   constexpr int STAGE = (BM + BN) * DBK;     // bf16 elements per slice
-  __shared__ __attribute__((aligned(16))) bf16_t lds[NS * STAGE];
+  // the fused epilogue stages 128 rows of float32 outputs in the same LDS
+  constexpr int LDS_N = (EPI == EPI_QKROPE && 128 * kRopeStageStride * 2 > NS * STAGE) ? 128 * kRopeStageStride * 2
+                                                                                       : NS * STAGE;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_N];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / GN, wn = wid % GN;
   int tm, tn;
@@ -391,7 +402,62 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
       if (++kt >= nk) break;
     }
   }
-  gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
+  if constexpr (EPI == EPI_QKROPE) {
+    // Pasos 4-5 per token on the tile's two heads (columns bn0 .. bn0 + 255),
+    // 128 rows at a time: the float32 outputs are staged in LDS (padded rows),
+    // then 16 lanes take one (token, head): a query or key head is normalised,
+    // rotated and stored by the same function as rope_append, a value head is
+    // rounded to bf16 for the value pass.
+    static_assert(BM == 256 && BN == 256 && WM == 4 && WN == 4 && !DB, "written for the 256 x 256 tiles");
+    wait_vm<0>();
+    __syncthreads();  // every wavefront is done with the pipeline's LDS
+    float* stg = reinterpret_cast<float*>(lds);
+    constexpr int SP = kRopeStageStride;
+    const int units = ra.n_q + 2 * ra.n_kv;
+    const int unit0 = bn0 / Q3_HEAD_DIM;
+    const KvGeom geo{ra.n_kv, ra.layer};
+    const int j16 = threadIdx.x & 15;
+    for (int half = 0; half < 2; ++half) {
+      if ((wm >> 1) == half) {
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int tl = (wm & 1) * 64 + i * 16 + (lane & 15);
+            const int col = wn * 64 + j * 16 + (lane >> 4) * 4;
+            *reinterpret_cast<f32x4*>(&stg[tl * SP + col]) = acc[i][j];
+          }
+      }
+      __syncthreads();
+      for (int uu = (int)threadIdx.x >> 4; uu < 256; uu += 64 * NW / 16) {
+        const int tl = uu >> 1, hl = uu & 1;
+        const int t = bm0 + half * 128 + tl;
+        const int u = unit0 + hl;
+        if (t >= M || u >= units) continue;  // uniform over the 16 lanes
+        const float4 x = *reinterpret_cast<const float4*>(&stg[tl * SP + hl * Q3_HEAD_DIM + 4 * j16]);
+        const float4 y = *reinterpret_cast<const float4*>(&stg[tl * SP + hl * Q3_HEAD_DIM + 64 + 4 * j16]);
+        if (u >= ra.n_q + ra.n_kv) {
+          bf16_t* dst = ra.v_out + ((int64_t)t * ra.n_kv + (u - ra.n_q - ra.n_kv)) * Q3_HEAD_DIM;
+          store4<bf16_t>(dst + 4 * j16, x.x, x.y, x.z, x.w);
+          store4<bf16_t>(dst + 64 + 4 * j16, y.x, y.y, y.z, y.w);
+          continue;
+        }
+        const int b = seq_of_token(ra.sb, t);
+        const SeqState sst = ra.st[ra.sb.slot[b]];
+        const int pos = ra.sb.prior[b] + t - ra.sb.cu[b];
+        if (pos < 0 || pos >= sst.cap) {  // host validation makes this unreachable
+          if (j16 == 0) atomicOr(ra.err, 4u);
+          continue;
+        }
+        bf16_t* dst = u < ra.n_q ? ra.q_out + ((int64_t)t * ra.n_q + u) * Q3_HEAD_DIM
+                                 : kv_k(ra.kv, sst, geo, u - ra.n_q) + (int64_t)pos * Q3_HEAD_DIM;
+        qk_norm_rope_store<bf16_t>(x, y, u < ra.n_q ? ra.qn : ra.kn, ra.eps, ra.cos_t, ra.sin_t, pos, j16, dst);
+      }
+      __syncthreads();  // the staging is rewritten by the next half
+    }
+  } else {
+    gemm_epilogue<EPI, WM, WN>(acc, bm0 + wm * 16 * WM, bn0 + wn * 16 * WN, M, N, out, ldo);
+  }
 }
 
 template <int WM, int WN, int GM, int GN, int NS, bool DB>
@@ -400,16 +466,18 @@ hipError_t gemm_dma_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int
   constexpr int BM = 16 * WM * GM, BN = 16 * WN * GN, NT = 64 * GM * GN;
   if (K % DBK != 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM)));
+  QkvRopeArgs none;
+  std::memset(&none, 0, sizeof(none));
   switch (epi) {
     case EPI_STORE:
     case EPI_ARGMAX:
-      gemm_dma_kernel<EPI_STORE, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_STORE, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, none);
       break;
     case EPI_RESADD:
-      gemm_dma_kernel<EPI_RESADD, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_RESADD, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, none);
       break;
     case EPI_SWIGLU:
-      gemm_dma_kernel<EPI_SWIGLU, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo);
+      gemm_dma_kernel<EPI_SWIGLU, WM, WN, GM, GN, NS, DB><<<grid, NT, 0, s>>>(A, M, W, N, K, out, ldo, none);
       break;
     default:
       return hipErrorInvalidValue;
@@ -418,9 +486,37 @@ hipError_t gemm_dma_launch(int epi, const bf16_t* A, int M, const bf16_t* W, int
 }
 
 int g_gemm_cfg = -1;  // tile configuration override (q3op_tune); -1 = automatic
+int g_qkv_rope = -1;  // fused q/k/v epilogue: -1 automatic, 0 never
+
+// The automatic tile configuration (see gemm_bf16).
+int auto_config(int M, int N) {
+  const int64_t g256 = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
+  const int64_t g128 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
+  return g256 >= 256 ? 7 : (g128 >= 256 ? 8 : 0);
+}
 }  // namespace
 
 void gemm_set_config(int cfg) { g_gemm_cfg = cfg; }
+void gemm_set_qkv_rope(int mode) { g_qkv_rope = mode; }
+
+// Fused only where the unfused call would run the 256 x 256 pipeline (large
+// prefills), so both paths multiply in the same order.
+bool gemm_qkv_rope_ok(int M, int N, int K) {
+  if (g_qkv_rope == 0 || M <= 0 || N % 256 != 0 || K % BK != 0) return false;
+  const int cfg = g_gemm_cfg >= 0 ? g_gemm_cfg : auto_config(M, N);
+  return cfg == 7;
+}
+
+hipError_t gemm_qkv_rope(const bf16_t* A, int M, const bf16_t* W, int N, int K, const QkvRopeArgs& ra,
+                         hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!gemm_qkv_rope_ok(M, N, K) || N != (ra.n_q + 2 * ra.n_kv) * Q3_HEAD_DIM || !ra.q_out || !ra.v_out ||
+      !ra.kv || !ra.st || ra.sb.decode)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((N + 255) / 256) * ((M + 255) / 256)));
+  gemm_dma_kernel<EPI_QKROPE, 4, 4, 4, 4, 4, false><<<grid, 1024, 0, s>>>(A, M, W, N, K, nullptr, 0, ra);
+  return hipGetLastError();
+}
 
 int gemm_splits(int epi, int M, int N, int K) {
   // residual GEMMs whose 64 x 64 grid leaves CUs idle: up to 4 K slices of at
@@ -461,9 +557,7 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, in
     // double-buffering) measured 5-25 % below it.  At M = 4096 the 128 x 128
     // pipeline runs the o and down shapes (256 tiles) at 445 and 516 TFLOP/s,
     // 15 % above the 128 x 128 tile without it.
-    const int64_t g256 = (int64_t)((N + 255) / 256) * ((M + 255) / 256);
-    const int64_t g128 = (int64_t)((N + 127) / 128) * ((M + 127) / 128);
-    cfg = g256 >= 256 ? 7 : (g128 >= 256 ? 8 : 0);
+    cfg = auto_config(M, N);
   }
   switch (cfg) {
     case 0: return gemm_launch<2, 2, 2, 2, 1>(epi, A, M, W, N, K, out, ldo, s);   //  64 x  64, 4 waves

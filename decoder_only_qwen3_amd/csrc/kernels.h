@@ -37,6 +37,11 @@ hipError_t rope_append(int dtype, const float* qkv, int T, const SeqBatch& sb, S
 // rope_append writes the same staging when given one.
 hipError_t vstage_from_cache(int T, const SeqBatch& sb, const SeqState* st, const bf16_t* kv, int layer, int n_kv,
                              uint16_t* vstage, hipStream_t s);
+// The value half of rope_append for a bf16 prefill whose q/k/v projection ran
+// with the fused QK-Norm/RoPE epilogue (gemm_qkv_rope): bf16 value rows
+// v [T][n_kv][128] into the cache and the fp16 staging.
+hipError_t vt_append_bf16(const bf16_t* v, int T, const SeqBatch& sb, SeqState* st, bf16_t* kv, int layer, int n_kv,
+                          uint16_t* vstage, hipStream_t s);
 // ---------------------------------------------------------------- k_quant.hip
 // Weight-only affine group quantization (groups of 64 along K, 8 or 4 bits,
 // fp16 scale and offset per group packed in one 32-bit word).
@@ -83,6 +88,30 @@ hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 // C[M,N] = A[M,K] . W[N,K]^T with bf16 operands on MFMA; K % 64 == 0.
 hipError_t gemm_bf16(int epi, const bf16_t* A, int M, const bf16_t* W, int N, int K, void* out,
                      int64_t ldo, hipStream_t s, float* split_part = nullptr, uint32_t* split_cnt = nullptr);
+// The prefill q/k/v projection with Pasos 4-5's per-token work in its
+// epilogue: query heads normalised and rotated into q_out [T][n_q][128]
+// (bf16), key heads into the cache at each token's position, value heads
+// rounded to bf16 into v_out [T][n_kv][128] (for vt_append_bf16).  Results
+// equal gemm_bf16(EPI_STORE) followed by rope_append's query/key work.  Only
+// for the tile configuration of large calls (gemm_qkv_rope_ok).
+struct QkvRopeArgs {
+  SeqBatch sb;
+  const SeqState* st;
+  bf16_t* kv;
+  int layer, n_q, n_kv;
+  const float* qn;
+  const float* kn;
+  float eps;
+  const float* cos_t;
+  const float* sin_t;
+  bf16_t* q_out;
+  bf16_t* v_out;
+  uint32_t* err;
+};
+bool gemm_qkv_rope_ok(int M, int N, int K);
+hipError_t gemm_qkv_rope(const bf16_t* A, int M, const bf16_t* W, int N, int K, const QkvRopeArgs& ra,
+                         hipStream_t s);
+void gemm_set_qkv_rope(int mode);  // -1 automatic, 0 never (timing and parity tests)
 // Split-K of residual GEMMs on small grids: slices (1 = none) and the float
 // workspace their partial tiles need; split_cnt holds one zeroed counter per
 // 64 x 64 output tile (every call leaves them zero).

@@ -306,6 +306,9 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
   const bool one_i = !bits && bf && decode && rowgemv_ok(T, I);
   const bool rows_o = !bits && bf && decode && rowdot_ok(T, Q);
   const bool rows_d = !bits && bf && decode && rowdot_ok(T, I);
+  // bf16 prefill on the large-tile GEMM: the q/k/v projection's epilogue does
+  // the query/key half of Pasos 4-5 (the float32 q/k/v rows never reach HBM)
+  const bool qkv_rope = bf && !decode && gemm_qkv_rope_ok(T, NQKV, H);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& lw = m->wl.layers[l];
     const bf16_t *Wqkv = nullptr, *Wo = nullptr, *Wgu = nullptr, *Wd = nullptr;
@@ -343,6 +346,26 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
     } else if (decode) {
       LAUNCH(skinny_bf16(EPI_STORE, fuse_norm ? (const void*)x : h, T, Wqkv, NQKV, H,
                          fuse_norm ? m->W<float>(lw.in_norm) : nullptr, c.rms_eps, qkv, NQKV, nullptr, nullptr, s));
+    } else if (qkv_rope) {
+      // large prefills: QK-Norm, RoPE and the key append in the projection's
+      // epilogue, the values out as bf16 rows (in the q/k/v buffer)
+      QkvRopeArgs ra;
+      std::memset(&ra, 0, sizeof(ra));
+      ra.sb = sb;
+      ra.st = m->state();
+      ra.kv = (bf16_t*)m->kv;
+      ra.layer = l;
+      ra.n_q = c.n_q_heads;
+      ra.n_kv = c.n_kv_heads;
+      ra.qn = m->W<float>(lw.qn);
+      ra.kn = m->W<float>(lw.kn);
+      ra.eps = c.rms_eps;
+      ra.cos_t = cos_t;
+      ra.sin_t = sin_t;
+      ra.q_out = (bf16_t*)qb;
+      ra.v_out = (bf16_t*)qkv;
+      ra.err = m->err();
+      LAUNCH(gemm_qkv_rope((const bf16_t*)h, T, Wqkv, NQKV, H, ra, s));
     } else {
       LAUNCH(gemm_bf16(EPI_STORE, (const bf16_t*)h, T, Wqkv, NQKV, H, qkv, NQKV, s));
     }
@@ -352,6 +375,9 @@ q3_status enqueue_layers(q3_model* m, int T, const SeqBatch& sb, bool decode, hi
       LAUNCH(decode_attn_fused(qkv, sb, m->state(), (bf16_t*)m->kv, l, c.n_q_heads, c.n_kv_heads,
                                m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, plan,
                                m->WS<float>(L.attn_part), m->WS<uint32_t>(L.attn_cnt), (bf16_t*)ob, s));
+    } else if (qkv_rope) {
+      LAUNCH(vt_append_bf16((const bf16_t*)qkv, T, sb, m->state(), (bf16_t*)m->kv, l, c.n_kv_heads,
+                            m->WS<uint16_t>(L.vstage), s));
     } else {
       LAUNCH(rope_append(c.dtype, qkv, T, sb, m->state(), m->kv, l, c.n_q_heads, c.n_kv_heads,
                          m->W<float>(lw.qn), m->W<float>(lw.kn), c.rms_eps, cos_t, sin_t, qb, m->err(), s,

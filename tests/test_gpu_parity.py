@@ -302,3 +302,38 @@ def test_bf16_decode_then_top_p_sample(bf16_two_layer):
         assert ok, r
     np.testing.assert_array_equal(greedy.cpu().numpy(), nx.cpu().numpy())
     assert m.error_flags() == 0
+
+
+def test_bf16_fused_qkv_epilogue_equals_separate_kernels(bf16_two_layer):
+    """Large prefills fold QK-Norm, RoPE and the key append into the q/k/v
+    projection's epilogue.  The same calls with the fold switched off (float32
+    projection rows, then the separate kernel) must give the same bits: the
+    last rows' logits, the next tokens and the whole KV cache, after a packed
+    call of three prompts (4,877 tokens: the 256 x 256 tile path) and a
+    continuation of one of them by 4,000 tokens."""
+    from decoder_only_qwen3_amd import _lib
+    d, w = bf16_two_layer
+    lib = _lib.load()
+    lens = [1500, 2600, 777]
+    prompts = [q3synth.make_tokens(L, d.vocab, 300 + i).tolist() for i, L in enumerate(lens)]
+    more = q3synth.make_tokens(4000, d.vocab, 310).tolist()
+    runs = []
+    for mode in (-1, 0):
+        _lib.check(lib.q3op_tune(5, mode))
+        try:
+            m = _model(d, max_slots=4, max_positions=5568, max_prefill_tokens=4992, kv_tokens=9152)
+            m.load_weights(w)
+            with torch.cuda.stream(m.stream):
+                m.bufs[1].zero_()  # unused cache rows compare equal too
+            for s, cap in zip([0, 1, 2], [5568, 2624, 832]):
+                m.seq_alloc(s, cap)
+            lg1, nx1 = m.prefill([0, 1, 2], prompts)
+            lg2, nx2 = m.prefill([0], [more])
+            m.synchronize()
+            assert m.error_flags() == 0
+            runs.append([t.cpu() for t in (lg1, nx1, lg2, nx2, m.bufs[1])])
+            m.close()
+        finally:
+            _lib.check(lib.q3op_tune(5, -1))
+    for name, a, b in zip(["logits 1", "next 1", "logits 2", "next 2", "kv cache"], runs[0], runs[1]):
+        assert torch.equal(a, b), name
