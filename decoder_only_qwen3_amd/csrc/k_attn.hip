@@ -27,6 +27,7 @@
 // random-init model moved by up to 3e-2 of their RMS.
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "kernels.h"
 
@@ -101,6 +102,7 @@ Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ vswz(dim))
 struct TileTable {
   int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
   int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
+  int32_t xbnd[9];                    // work items of XCD x: xbnd[x] .. xbnd[x+1] - 1
 };
 
 // Block: one kv head and one query tile of `qt` tokens of one sequence; its
@@ -132,18 +134,28 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
   uint16_t (*sK)[KT * 128] = sKV;
   uint16_t (*sV)[KT * 128] = sKV + 2;
 
-  const int total = tt.tile_cu[sb.n];
-  const int tile = total - 1 - (int)blockIdx.x;  // late (long) tiles first
-  const int g = blockIdx.y;
+  // Work item = (sequence b, kv head g, query tile), ordered by b, then g,
+  // then tile from the last (longest) down.  Blocks are dealt to the eight
+  // XCDs round robin (block i runs on XCD i % 8), each with an L2 of its own;
+  // XCD x takes the contiguous run of items xbnd[x] .. xbnd[x+1]-1 (balanced
+  // by key tiles on the host), so the query tiles of one (sequence, head)
+  // read its keys and values through one L2 instead of all eight.
+  const int xcd = blockIdx.x & 7;
+  const int item = tt.xbnd[xcd] + (int)(blockIdx.x >> 3);
+  if (item >= tt.xbnd[xcd + 1]) return;  // the grid covers the longest run
   int b = 0;
   {
     int lo = 0, hi = sb.n - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (tt.tile_cu[mid] <= tile) lo = mid; else hi = mid - 1;
+      if (tt.tile_cu[mid] * n_kv <= item) lo = mid; else hi = mid - 1;
     }
     b = lo;
   }
+  const int ntb = tt.tile_cu[b + 1] - tt.tile_cu[b];
+  const int rr = item - tt.tile_cu[b] * n_kv;
+  const int g = rr / ntb;
+  const int tile = tt.tile_cu[b] + (ntb - 1 - (rr - g * ntb));
   const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
   const int q0 = (tile - tt.tile_cu[b]) * qt;
   const SeqState s = st[sb.slot[b]];
@@ -961,7 +973,39 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   }
   const int total = tt.tile_cu[sb.n];
   if (total <= 0) return hipSuccess;
-  dim3 grid(total, n_kv);
+  // XCD runs of work items, balanced by the key tiles each item reads
+  // (items in the kernel's order: sequence, head, query tile descending)
+  {
+    std::vector<int64_t> wb(sb.n);
+    int64_t wsum = 0;
+    for (int b = 0; b < sb.n; ++b) {
+      const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
+      int64_t w = 0;
+      for (int t = 0; t * qt < L; ++t) w += (P + std::min(L, (t + 1) * qt) + 63) / 64;
+      wb[b] = w;
+      wsum += w * n_kv;
+    }
+    // walk the items in order, cutting at each eighth of the work
+    int x = 1;
+    int64_t acc = 0;
+    int idx = 0;
+    tt.xbnd[0] = 0;
+    for (int b = 0; b < sb.n && x < 8; ++b) {
+      const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
+      const int ntb = (L + qt - 1) / qt;
+      for (int g = 0; g < n_kv && x < 8; ++g)
+        for (int t = ntb - 1; t >= 0 && x < 8; --t, ++idx) {
+          while (x < 8 && acc * 8 >= wsum * x) tt.xbnd[x++] = idx;
+          acc += (P + std::min(L, (t + 1) * qt) + 63) / 64;
+        }
+    }
+    while (x < 8) tt.xbnd[x++] = total * n_kv;
+    tt.xbnd[8] = total * n_kv;
+  }
+  int longest = 0;
+  for (int x = 0; x < 8; ++x) longest = std::max(longest, tt.xbnd[x + 1] - tt.xbnd[x]);
+  if ((int64_t)longest * 8 > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)longest * 8);
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const int64_t vh_keys = vstage_keys(sb);
   switch (CB) {
