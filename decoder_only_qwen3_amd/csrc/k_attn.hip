@@ -101,6 +101,7 @@ Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ vswz(dim))
 
 struct TileTable {
   int32_t tile_cu[Q3_MAX_BATCH + 1];  // prefix sums of query tiles per sequence
+  int32_t item_cu[Q3_MAX_BATCH + 1];  // prefix sums of work items (groups of TPB tiles) per sequence and head
   int32_t vstart[Q3_MAX_BATCH];       // vstage_start of each sequence
   int32_t xbnd[9];                    // work items of XCD x: xbnd[x] .. xbnd[x+1] - 1
 };
@@ -118,8 +119,14 @@ struct TileTable {
 // S(j+1) = K(j+1).Q^T while exponentiating S(j).  LDS: K(t) in sK[t & 1],
 // V(t) in sV[t & 1]; iteration j reads V(j-1) and K(j+1) and loads V(j) and
 // K(j+2) over the buffers of V(j-2) and K(j), used up in iteration j-1.
-template <int CB>
-__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
+//
+// TPB = 2: a block of 8 wavefronts takes two consecutive query tiles of one
+// (sequence, head) -- wavefronts 0-3 the later tile, 4-7 the one before it --
+// and both halves share every K/V tile it loads; the loop runs over the later
+// tile's keys (the earlier tile's rows mask the extra ones).  Half the
+// blocks, each with twice the work, halve the per-block start and finish.
+template <int CB, int TPB>
+__global__ __launch_bounds__(256 * TPB, 2 / TPB) void flash_prefill_kernel(
     const bf16_t* __restrict__ q, SeqBatch sb, TileTable tt, const SeqState* __restrict__ st,
     const bf16_t* __restrict__ kv, const uint16_t* __restrict__ vstage, int64_t vh_keys, int layer, int n_q,
     int n_kv, int qt, bf16_t* __restrict__ o, float scale_log2) {
@@ -140,6 +147,8 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
   // XCD x takes the contiguous run of items xbnd[x] .. xbnd[x+1]-1 (balanced
   // by key tiles on the host), so the query tiles of one (sequence, head)
   // read its keys and values through one L2 instead of all eight.
+  constexpr int NWV = 4 * TPB;   // wavefronts per block
+  constexpr int LPW = 4 / TPB;   // 1 KiB loads per wavefront per K or V tile
   const int xcd = blockIdx.x & 7;
   const int item = tt.xbnd[xcd] + (int)(blockIdx.x >> 3);
   if (item >= tt.xbnd[xcd + 1]) return;  // the grid covers the longest run
@@ -148,35 +157,39 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
     int lo = 0, hi = sb.n - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (tt.tile_cu[mid] * n_kv <= item) lo = mid; else hi = mid - 1;
+      if (tt.item_cu[mid] * n_kv <= item) lo = mid; else hi = mid - 1;
     }
     b = lo;
   }
   const int ntb = tt.tile_cu[b + 1] - tt.tile_cu[b];
-  const int rr = item - tt.tile_cu[b] * n_kv;
-  const int g = rr / ntb;
-  const int tile = tt.tile_cu[b] + (ntb - 1 - (rr - g * ntb));
+  const int nib = tt.item_cu[b + 1] - tt.item_cu[b];  // items per head: ceil(ntb / TPB)
+  const int rr = item - tt.item_cu[b] * n_kv;
+  const int g = rr / nib;
+  const int k = rr - g * nib;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wq = wid & 3, tsel = wid >> 2;  // wavefront within its tile, tile of the item
+  const int tlocA = ntb - 1 - TPB * k;      // the item's last (longest) tile
+  const int tloc = tlocA - tsel;            // this wavefront's tile (< 0: none, it only helps load)
   const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
-  const int q0 = (tile - tt.tile_cu[b]) * qt;
+  const int q0 = tloc * qt;
   const SeqState s = st[sb.slot[b]];
   const KvGeom geo{n_kv, layer};
   const bf16_t* Kc = kv_k(kv, s, geo, g);
   const uint16_t* Vh = vstage + ((int64_t)g * vh_keys + tt.vstart[b]) * Q3_HEAD_DIM;  // fp16, zero-padded
   const int group = n_q / n_kv;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
 
   // V(-1) is all zeros (the first iteration's P.V adds nothing).
-  for (int i = tid; i < 128 * KT / 8; i += 256) reinterpret_cast<u32x4*>(sV[1])[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < 128 * KT / 8; i += 64 * NWV) reinterpret_cast<u32x4*>(sV[1])[i] = u32x4{0u, 0u, 0u, 0u};
 
   // Query fragments (B operand of S^T) for this wavefront's 16-row blocks.
   bf16x8 qf[CB][4];
   int qpos[CB], qhead[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int r = wid * 16 * CB + cb * 16 + fr;
+    const int r = wq * 16 * CB + cb * 16 + fr;
     const int hh = r / qt, tq = r - hh * qt;
-    qpos[cb] = q0 + tq;
+    qpos[cb] = tloc >= 0 ? q0 + tq : L;  // no tile: rows past the end (never stored)
     qhead[cb] = g * group + hh;
     const bool ok = qpos[cb] < L;
     const bf16_t* qp = q + ((int64_t)(sb.cu[b] + (ok ? qpos[cb] : 0)) * n_q + qhead[cb]) * 128 + fq * 8;
@@ -188,31 +201,31 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
     }
   }
 
-  const int kend = P + min(L, q0 + qt);  // keys of the tile's last row, + 1
+  const int kend = P + min(L, tlocA * qt + qt);  // keys of the item's last row, + 1
   const int ntiles = (kend + KT - 1) / KT;
 
-  // Load i of wavefront w fills LDS chunks (4i + w)*64 + lane of a tile: the
-  // K chunk (key, j) holds global chunk j ^ kswz(key) of that key's row; the
-  // V^T chunk (dim, j) holds keys 8 (j ^ vswz(dim)) .. +7 of that dim.
-  int ksrc[4], vsrc[4];
+  // Load i of wavefront w fills LDS chunks (NWV*i + w)*64 + lane of a tile:
+  // the K chunk (key, j) holds global chunk j ^ kswz(key) of that key's row;
+  // the V^T chunk (dim, j) holds keys 8 (j ^ vswz(dim)) .. +7 of that dim.
+  int ksrc[LPW], vsrc[LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + wid) * 64 + lane;
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (NWV * i + wid) * 64 + lane;
     const int key = p >> 4, dim = p >> 3;
     ksrc[i] = key * 128 + (((p & 15) ^ kswz(key)) << 3);
     vsrc[i] = (int)vt_off(((p & 7) ^ vswz(dim)) << 3, dim);
   }
   auto issue_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)  // (non-const pointers: with a const source the host pass drops the kernel stub)
+    for (int i = 0; i < LPW; ++i)  // (non-const pointers: with a const source the host pass drops the kernel stub)
       __builtin_amdgcn_global_load_lds((void*)(Kc + (int64_t)t * KT * 128 + ksrc[i]),
-                                       (void*)(&sK[t & 1][(4 * i + wid) * 512]), 16, 0, 0);
+                                       (void*)(&sK[t & 1][(NWV * i + wid) * 512]), 16, 0, 0);
   };
   auto issue_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)  // a 64-key tile is two 32-key value blocks: 64 * 128 elements
+    for (int i = 0; i < LPW; ++i)  // a 64-key tile is two 32-key value blocks: 64 * 128 elements
       __builtin_amdgcn_global_load_lds((void*)(Vh + (int64_t)t * KT * 128 + vsrc[i]),
-                                       (void*)(&sV[t & 1][(4 * i + wid) * 512]), 16, 0, 0);
+                                       (void*)(&sV[t & 1][(NWV * i + wid) * 512]), 16, 0, 0);
   };
 
   // S^T of tile t: sacc[c][sb][cb], keys t*64 + c*32 + 8*fq + 4*sb + r.
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(
   issue_k(0);
   if (ntiles > 1) {
     issue_k(1);
-    wait_vm<4>();
+    wait_vm<LPW>();
   } else {
     wait_vm<0>();
   }
@@ -942,9 +955,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
 }  // namespace
 
 namespace {
-int g_flash_cb = -1;  // rows-per-wavefront override (q3op_tune); -1 = automatic
+int g_flash_cb = -1;   // rows-per-wavefront override (q3op_tune); -1 = automatic
+int g_flash_tpb = -1;  // query tiles per block override (q3op_tune); -1 = automatic
 }
 void flash_set_rows(int cb) { g_flash_cb = cb; }
+void flash_set_tiles_per_block(int tpb) { g_flash_tpb = tpb; }
 
 hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqState* st,
                          const bf16_t* kv, const uint16_t* vstage, int layer, int n_q, int n_kv, bf16_t* o,
@@ -964,26 +979,40 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
     CB = tiles2 * n_kv >= 512 ? 2 : 1;
   }
   const int qt = 64 * CB / group;
+  // Two query tiles per block when the call's tiles read 64 key tiles or
+  // more on average (MI355X: 32K keys 5.32 -> 5.12 ms, 8K 1.43 -> 1.41 ms;
+  // shorter prompts lose: 512 keys 263 -> 299 us, 2K 989 -> 1002 us).
+  int TPB = g_flash_tpb;
+  if (TPB < 0) {
+    int64_t kt = 0, nt = 0;
+    for (int b = 0; b < sb.n; ++b) {
+      const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
+      for (int t = 0; t * qt < L; ++t, ++nt) kt += (P + std::min(L, (t + 1) * qt) + 63) / 64;
+    }
+    TPB = (nt > 0 && kt >= 64 * nt) ? 2 : 1;
+  }
   TileTable tt;
   tt.tile_cu[0] = 0;
+  tt.item_cu[0] = 0;
   for (int b = 0; b < sb.n; ++b) {
     const int L = sb.cu[b + 1] - sb.cu[b];
-    tt.tile_cu[b + 1] = tt.tile_cu[b] + (L + qt - 1) / qt;
+    const int ntb = (L + qt - 1) / qt;
+    tt.tile_cu[b + 1] = tt.tile_cu[b] + ntb;
+    tt.item_cu[b + 1] = tt.item_cu[b] + (ntb + TPB - 1) / TPB;
     tt.vstart[b] = vstage_start(sb, b);
   }
   const int total = tt.tile_cu[sb.n];
   if (total <= 0) return hipSuccess;
-  // XCD runs of work items, balanced by the key tiles each item reads
-  // (items in the kernel's order: sequence, head, query tile descending)
+  const int items = tt.item_cu[sb.n] * n_kv;
+  // XCD runs of work items, balanced by the key tiles each item's loop reads
+  // (items in the kernel's order: sequence, head, last query tile descending)
   {
-    std::vector<int64_t> wb(sb.n);
+    auto item_work = [&](int L, int P, int tA) { return (int64_t)(P + std::min(L, (tA + 1) * qt) + 63) / 64; };
     int64_t wsum = 0;
     for (int b = 0; b < sb.n; ++b) {
       const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
-      int64_t w = 0;
-      for (int t = 0; t * qt < L; ++t) w += (P + std::min(L, (t + 1) * qt) + 63) / 64;
-      wb[b] = w;
-      wsum += w * n_kv;
+      const int ntb = (L + qt - 1) / qt;
+      for (int tA = ntb - 1; tA >= 0; tA -= TPB) wsum += item_work(L, P, tA) * n_kv;
     }
     // walk the items in order, cutting at each eighth of the work
     int x = 1;
@@ -994,13 +1023,13 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
       const int L = sb.cu[b + 1] - sb.cu[b], P = sb.prior[b];
       const int ntb = (L + qt - 1) / qt;
       for (int g = 0; g < n_kv && x < 8; ++g)
-        for (int t = ntb - 1; t >= 0 && x < 8; --t, ++idx) {
+        for (int tA = ntb - 1; tA >= 0 && x < 8; tA -= TPB, ++idx) {
           while (x < 8 && acc * 8 >= wsum * x) tt.xbnd[x++] = idx;
-          acc += (P + std::min(L, (t + 1) * qt) + 63) / 64;
+          acc += item_work(L, P, tA);
         }
     }
-    while (x < 8) tt.xbnd[x++] = total * n_kv;
-    tt.xbnd[8] = total * n_kv;
+    while (x < 8) tt.xbnd[x++] = items;
+    tt.xbnd[8] = items;
   }
   int longest = 0;
   for (int x = 0; x < 8; ++x) longest = std::max(longest, tt.xbnd[x + 1] - tt.xbnd[x]);
@@ -1008,18 +1037,15 @@ hipError_t flash_prefill(const bf16_t* q, int T, const SeqBatch& sb, const SeqSt
   dim3 grid((unsigned)longest * 8);
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const int64_t vh_keys = vstage_keys(sb);
-  switch (CB) {
-    case 2:
-      flash_prefill_kernel<2><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
-                                                        scale_log2);
-      break;
-    case 1:
-      flash_prefill_kernel<1><<<grid, 256, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, n_kv, qt, o,
-                                                        scale_log2);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+#define Q3_FLASH(CBV, TPBV)                                                                                \
+  flash_prefill_kernel<CBV, TPBV><<<grid, 256 * TPBV, 0, s>>>(q, sb, tt, st, kv, vstage, vh_keys, layer, n_q, \
+                                                              n_kv, qt, o, scale_log2)
+  if (CB == 2 && TPB == 1) Q3_FLASH(2, 1);
+  else if (CB == 2 && TPB == 2) Q3_FLASH(2, 2);
+  else if (CB == 1 && TPB == 1) Q3_FLASH(1, 1);
+  else if (CB == 1 && TPB == 2) Q3_FLASH(1, 2);
+  else return hipErrorInvalidValue;
+#undef Q3_FLASH
   return hipGetLastError();
 }
 

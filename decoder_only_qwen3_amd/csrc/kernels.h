@@ -119,6 +119,7 @@ int gemm_splits(int epi, int M, int N, int K);
 size_t gemm_split_floats(int M, int N, int K);
 void gemm_set_config(int cfg);  // tile configuration override; -1 = automatic
 void flash_set_rows(int cb);    // prefill attention rows per wavefront / 16 (1, 2, 4); -1 = automatic
+void flash_set_tiles_per_block(int tpb);  // -1 automatic, 1 or 2 query tiles per block
 
 // ---------------------------------------------------------------- k_skinny.hip
 struct SkinnyPlan {

@@ -571,6 +571,11 @@ q3_status q3op_tune(int32_t key, int32_t value) {
     decode_attn_set_split_cap(value);
     return Q3_OK;
   }
+  if (key == Q3OP_TUNE_FLASH_TILES) {
+    if (value != -1 && value != 1 && value != 2) return op_fail(Q3_E_ARG, "query tiles per block must be -1, 1 or 2");
+    flash_set_tiles_per_block(value);
+    return Q3_OK;
+  }
   if (key == Q3OP_TUNE_QKV_ROPE) {
     if (value != -1 && value != 0) return op_fail(Q3_E_ARG, "fused q/k/v epilogue mode must be -1 or 0");
     gemm_set_qkv_rope(value);

@@ -210,12 +210,15 @@ q3_status q3op_qlinear_rows(int32_t bits, int32_t epi, const void* d_x, int32_t 
  * Q3OP_TUNE_QKV_ROPE: large bf16 prefills fold QK-Norm, RoPE and the key
  *   append into the q/k/v projection's epilogue; -1 = automatic, 0 = never
  *   (the projection writes float32 rows and a separate kernel does the rest;
- *   both give the same bits). */
+ *   both give the same bits).
+ * Q3OP_TUNE_FLASH_TILES: query tiles per prefill attention block, -1 =
+ *   automatic, 1, or 2 (eight wavefronts sharing each key/value tile). */
 #define Q3OP_TUNE_GEMM_TILES 1
 #define Q3OP_TUNE_FLASH_ROWS 2
 #define Q3OP_TUNE_ROWGEMV 3
 #define Q3OP_TUNE_ATTN_SPLITS 4
 #define Q3OP_TUNE_QKV_ROPE 5
+#define Q3OP_TUNE_FLASH_TILES 6
 q3_status q3op_tune(int32_t key, int32_t value);
 
 #ifdef __cplusplus

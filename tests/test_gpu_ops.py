@@ -667,3 +667,26 @@ def test_decode_attention_fused_rope_append(prior, smax):
         bound = 2.0 ** -8 * np.abs(ref) + 2e-3 * rms
         # the kernel's own new key may differ from the oracle's by one bf16 ulp
         assert float(np.max(np.abs(got[b] - ref) / (bound + 4e-3 * rms))) < 1.0, b
+
+
+@pytest.mark.parametrize("rows", [1, 2])
+def test_flash_prefill_two_tiles_per_block(rows):
+    """Blocks of two query tiles (eight wavefronts sharing the key/value
+    tiles): odd and even tile counts, ragged tails, continued caches and the
+    GQA groupings, against the oracle."""
+    _, lib = ops()
+    call(lib.q3op_tune(2, rows))
+    call(lib.q3op_tune(6, 2))
+    try:
+        for n_q, n_kv in [(16, 8), (16, 2), (8, 1)]:
+            lens = [600, 3, 130, 257, 64, 65]
+            caps = [((L + 63) // 64) * 64 for L in lens]
+            worst = _attention_case(0, lens, None, caps, n_q=n_q, n_kv=n_kv, seed=rows * 10 + n_kv + 7)
+            assert worst < 1.0, (rows, n_q, n_kv, worst)
+        lens, cached = [300, 3, 130], [70, 1000, 0]
+        caps = [((c + L + 63) // 64) * 64 for L, c in zip(lens, cached)]
+        worst = _attention_case(0, lens, None, caps, seed=rows + 70, cached=cached)
+        assert worst < 1.0, (rows, worst)
+    finally:
+        call(lib.q3op_tune(6, -1))
+        call(lib.q3op_tune(2, -1))
