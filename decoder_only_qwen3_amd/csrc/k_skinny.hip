@@ -38,6 +38,7 @@ Q3_DEV uint32_t pack_bf2_hw(float lo, float hi) {
 
 constexpr int kMaxWaves = 16;
 constexpr int kNormMaxM = 64;
+constexpr int kMaxSplit = 4;  // K slices of a split residual projection
 
 // BITS = 8 or 4: W holds affine group codes of the weights (groups of 64
 // along K, a 32-bit fp16 scale/offset word per group in sbw); each lane
@@ -87,6 +88,10 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
       }
     }
   }
+  // Keep the weight loads ahead of everything else (the compiler would
+  // otherwise issue the activation loads first and wait on one of them
+  // before the weight stream starts).
+  __builtin_amdgcn_sched_barrier(0);
 
   float* red = smem;                                  // [nw][RG][MT][256]
   float* inv = smem + nw * RG * MT * 256;             // [kNormMaxM] (NORM only)
@@ -159,6 +164,20 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[g][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // bf16 activations: every fragment of the wavefront's slice is loaded (from
+  // L2) before the first product, so they take one round trip; rows past M
+  // read row 0 (their results are never stored).
+  u32x4 xf[NORM ? 1 : MT][NORM ? 1 : NST];
+  if constexpr (!NORM) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + (lane & 15);
+      const bf16_t* xp = reinterpret_cast<const bf16_t*>(Xin) + (int64_t)(m < M ? m : 0) * K + k0;
+#pragma unroll
+      for (int s = 0; s < NST; ++s) xf[mt][s] = ld16(xp + s * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + (lane & 15);
@@ -186,9 +205,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
           xv[3] = pack_bf2(b.z * r * gb.z, b.w * r * gb.w);
         }
       } else {
-        const bf16_t* xp = reinterpret_cast<const bf16_t*>(Xin) + (int64_t)(live ? m : 0) * K + k0;
-        xv = ld16(xp + s * 32);
-        if (!live) xv = u32x4{0u, 0u, 0u, 0u};
+        xv = xf[mt][s];
       }
 #pragma unroll
       for (int g = 0; g < RG; ++g) acc[g][mt] = mfma16(as_bf16x8(xv), as_bf16x8(wf[g][s]), acc[g][mt]);
@@ -280,17 +297,37 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const void* __restrict__ X
                  (uint32_t)(nsplit - 1);
         __syncthreads();
         if (last) {
+          // Every load of the merge (up to kMaxSplit partials and the
+          // residual for each of this thread's entries) is issued before the
+          // first add; the sums still run in slice order.  Entries of rows
+          // past M read row 0 and are not stored.  blockDim >= 256, so a
+          // thread has at most MT entries.
           const float* grp = part + (int64_t)blockIdx.x * nsplit * NE;
           float* o = reinterpret_cast<float*>(out);
-          for (int e = threadIdx.x; e < NE; e += blockDim.x) {
+          float pv[MT][kMaxSplit], rv[MT];
+          int64_t oi[MT];
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int e = min((int)threadIdx.x + i * (int)blockDim.x, NE - 1);
             const int mt = e >> 8, le = e & 255;
             const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
-            const int nl = (le >> 2) & 15;
-            if (m >= M) continue;
+            oi[i] = (int64_t)(m < M ? m : 0) * ldo + row0 + ((le >> 2) & 15);
+#pragma unroll
+            for (int j = 0; j < kMaxSplit; ++j)
+              pv[i][j] = __hip_atomic_load(grp + (int64_t)min(j, nsplit - 1) * NE + e, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            rv[i] = o[oi[i]];
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int e = (int)threadIdx.x + i * (int)blockDim.x;
+            const int mt = e >> 8, le = e & 255;
+            const int m = mt * 16 + ((le >> 2) >> 4) * 4 + (le & 3);
             float v = 0.f;
-            for (int j = 0; j < nsplit; ++j)
-              v += __hip_atomic_load(grp + (int64_t)j * NE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            o[(int64_t)m * ldo + row0 + nl] += v;
+#pragma unroll
+            for (int j = 0; j < kMaxSplit; ++j)
+              if (j < nsplit) v += pv[i][j];
+            if (e < NE && m < M) o[oi[i]] = rv[i] + v;
           }
           if (threadIdx.x == 0) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -364,7 +401,7 @@ bool skinny_norm_fuse(int M) { return M <= 16; }
 int skinny_splits(int epi, int M, int N, int K) {
   (void)M;
   if (epi != EPI_RESADD || N / 16 >= 128) return 1;
-  for (int sp = 4; sp >= 2; sp >>= 1)
+  for (int sp = kMaxSplit; sp >= 2; sp >>= 1)
     if (K % (sp * 128) == 0 && K / sp >= 512) return sp;
   return 1;
 }

@@ -137,6 +137,24 @@ def test_gemm_split_k_residual(M, N, K):
     assert np.array_equal(got1, got2)
 
 
+@pytest.mark.parametrize("M", [5, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(1024, 2048), (1024, 3072)])
+def test_skinny_split_k_residual(M, N, K):
+    """The decode residual projections (1024 outputs) split K over block
+    slices; the last slice adds the partials in slice order, then the
+    residual, so repeated calls agree bit for bit and every row matches the
+    float64 product, including the rows of a partly filled 16-row tile."""
+    rng = np.random.default_rng(7 * M + N + K)
+    X = rand_bf16(rng, (M, K))
+    W = rand_bf16(rng, (N, K), 0.02)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    base = rng.standard_normal((M, N)).astype(np.float32)
+    got1, _ = _linear(SKINNY, EPI_RESADD, X, W, out_init=base)
+    got2, _ = _linear(SKINNY, EPI_RESADD, X, W, out_init=base)
+    assert _rel(got1 - base, ref) < 2e-5
+    assert np.array_equal(got1, got2)
+
+
 @pytest.mark.parametrize("cfg", list(range(12)))
 def test_gemm_tile_configurations(cfg):
     """Every prefill GEMM tile shape, with ragged row and column tails."""
