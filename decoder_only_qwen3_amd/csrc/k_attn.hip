@@ -488,13 +488,13 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restric
       key = min(key, k_end - 1);
       const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16(kp + ks * 32)), qf[ks], sacc[sbk]);
+      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16_nt(kp + ks * 32)), qf[ks], sacc[sbk]);
     }
     u32x4 vraw[8];
     const int vkey0 = c0 + fq * 8;
 #pragma unroll
     for (int d = 0; d < 8; ++d)
-      vraw[d] = mask_keys(ld16(Vt + vt_off(vkey0, d * 16 + fr)), vkey0, k_end);
+      vraw[d] = mask_keys(ld16_nt(Vt + vt_off(vkey0, d * 16 + fr)), vkey0, k_end);
 
     float mx = -INFINITY;
 #pragma unroll
@@ -665,9 +665,9 @@ Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int e
 #pragma unroll
   for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16(kp[sbk] + ks * 32);
+    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16_nt(kp[sbk] + ks * 32);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) r.v[d] = ld16(vp + d * 16 * 32);
+  for (int d = 0; d < 8; ++d) r.v[d] = ld16_nt(vp + d * 16 * 32);
 }
 
 // Sequence of each z-index of the grid: blocks are dispatched in z order.
