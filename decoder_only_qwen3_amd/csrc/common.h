@@ -135,9 +135,10 @@ struct SeqState {
   int32_t len;    // tokens currently cached
 };
 
-// KV arena addressing.  A slot's region holds, for each layer, the keys as
-// [kv_head][cap][128] followed by the values as [kv_head][cap/32][128][32]
-// (transposed within blocks of 32 keys).
+// KV arena addressing.  A slot's region holds, for each layer, the keys of
+// each kv head (cap * 128 elements per head, laid out by kk_off) followed by
+// the values as [kv_head][cap/32][128][32] (transposed within blocks of 32
+// keys).
 struct KvGeom {
   int32_t n_kv;
   int32_t layer;
@@ -145,6 +146,25 @@ struct KvGeom {
 template <typename T>
 Q3_DEV T* kv_k(T* arena, const SeqState& s, KvGeom g, int head) {
   return arena + s.base + ((int64_t)(g.layer * 2) * g.n_kv + head) * (int64_t)s.cap * Q3_HEAD_DIM;
+}
+// Element of (key, dim) from a head's key base.  float32 caches: rows
+// [cap][128].  bf16 caches: blocks of 32 keys (8 KiB), each stored in the
+// order the attention kernels take its keys as MFMA operands: 16-byte chunk
+// c = (sbk * 4 + ks) * 64 + fq * 16 + fr of a block holds dims
+// ks * 32 + fq * 8 .. +7 of its key 8 * (fr / 4) + 4 * sbk + fr % 4.  A
+// wavefront's operand load (one chunk per lane, lane = fq * 16 + fr) is then
+// 1 KiB of consecutive bytes; with rows, each load took 64 bytes from each of
+// 16 rows, and streamed about 8 % slower on MI355X.
+template <typename T>
+Q3_DEV int64_t kk_off(int key, int dim);
+template <>
+Q3_DEV int64_t kk_off<float>(int key, int dim) { return (int64_t)key * Q3_HEAD_DIM + dim; }
+template <>
+Q3_DEV int64_t kk_off<bf16_t>(int key, int dim) {
+  const int k = key & 31;
+  const int sbk = (k >> 2) & 1, fr = ((k >> 3) << 2) | (k & 3);
+  const int ks = dim >> 5, fq = (dim >> 3) & 3;
+  return ((int64_t)(key >> 5) << 12) + ((((sbk * 4 + ks) * 4 + fq) * 16 + fr) << 3) + (dim & 7);
 }
 // Values are stored in blocks of 32 keys, each block [128 dims][32 keys]: a
 // 32-key run of every dim is one contiguous 8 KiB read, and a dim's 8-key
@@ -196,9 +216,9 @@ Q3_DEV void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
 // QK-Norm + rotate-half RoPE of one 128-wide query or key head, spread over
 // 16 lanes (lane j holds dims 4j..4j+3 in x and 64+4j..64+4j+3 in y, i.e.
 // four whole RoPE pairs): RMSNorm over the head with weight w, then the pair
-// rotation by the position's angles (cos_t/sin_t rows of 64), stored at dst.
-// Every kernel that does this step calls these functions, so the paths round
-// identically.
+// rotation by the position's angles (cos_t/sin_t rows of 64); dims 4j..4j+3
+// are stored at lo, dims 64+4j..64+4j+3 at hi.  Every kernel that does this
+// step calls these functions, so the paths round identically.
 struct RopeIn {
   float4 wa, wc, cs, sn;
 };
@@ -212,7 +232,8 @@ Q3_DEV RopeIn rope_inputs(const float* __restrict__ w, const float* __restrict__
   return in;
 }
 template <typename T>
-Q3_DEV void qk_norm_rope_apply(float4 x, float4 y, const RopeIn& in, float eps, int j, T* __restrict__ dst) {
+Q3_DEV void qk_norm_rope_apply(float4 x, float4 y, const RopeIn& in, float eps, T* __restrict__ lo,
+                               T* __restrict__ hi) {
   float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
@@ -220,16 +241,16 @@ Q3_DEV void qk_norm_rope_apply(float4 x, float4 y, const RopeIn& in, float eps, 
   const float4 wa = in.wa, wc = in.wc, cs = in.cs, sn = in.sn;
   x = float4{x.x * inv * wa.x, x.y * inv * wa.y, x.z * inv * wa.z, x.w * inv * wa.w};
   y = float4{y.x * inv * wc.x, y.y * inv * wc.y, y.z * inv * wc.z, y.w * inv * wc.w};
-  store4<T>(dst + 4 * j, x.x * cs.x - y.x * sn.x, x.y * cs.y - y.y * sn.y, x.z * cs.z - y.z * sn.z,
+  store4<T>(lo, x.x * cs.x - y.x * sn.x, x.y * cs.y - y.y * sn.y, x.z * cs.z - y.z * sn.z,
             x.w * cs.w - y.w * sn.w);
-  store4<T>(dst + 64 + 4 * j, x.x * sn.x + y.x * cs.x, x.y * sn.y + y.y * cs.y, x.z * sn.z + y.z * cs.z,
+  store4<T>(hi, x.x * sn.x + y.x * cs.x, x.y * sn.y + y.y * cs.y, x.z * sn.z + y.z * cs.z,
             x.w * sn.w + y.w * cs.w);
 }
 template <typename T>
 Q3_DEV void qk_norm_rope_store(float4 x, float4 y, const float* __restrict__ w, float eps,
                                const float* __restrict__ cos_t, const float* __restrict__ sin_t, int pos, int j,
-                               T* __restrict__ dst) {
-  qk_norm_rope_apply<T>(x, y, rope_inputs(w, cos_t, sin_t, pos, j), eps, j, dst);
+                               T* __restrict__ lo, T* __restrict__ hi) {
+  qk_norm_rope_apply<T>(x, y, rope_inputs(w, cos_t, sin_t, pos, j), eps, lo, hi);
 }
 
 // Error bits raised by kernels (read back by q3_error_flags).

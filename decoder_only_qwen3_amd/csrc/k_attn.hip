@@ -6,11 +6,13 @@
 // keys is the same softmax); softmax over the visible keys weights the values;
 // query head h reads key/value head h / (n_q / n_kv).
 //
-// Cache layout (per slot and layer): keys [kv_head][cap][128] row-major,
-// values [kv_head][cap/32][128][32] (transposed within 32-key blocks).  With
-// that layout both MFMA products read 16-byte runs, and a 32-key run of keys
-// or of values is one contiguous 8 KiB stretch (strided value rows read about
-// 30 % slower on MI355X):
+// Cache layout (per slot and layer, bf16): keys in blocks of 32, each block
+// stored in the order its keys are taken as MFMA operands (kk_off), values
+// [kv_head][cap/32][128][32] (transposed within 32-key blocks).  With that
+// layout both MFMA products read 16-byte runs, every operand load of a
+// wavefront is 1 KiB of consecutive bytes, and a 32-key run of keys or of
+// values is one contiguous 8 KiB stretch (strided value rows read about 30 %
+// slower on MI355X):
 //   S^T[key][row] = K[key][:] . Q[row][:]   A = K rows,    B = Q rows
 //   O^T[dim][row] = V^T[dim][keys] . P^T     A = V^T rows,  B = P from registers
 // The key order inside each 32-key chunk is permuted for the S^T product so
@@ -86,17 +88,14 @@ Q3_DEV u32x4 mask_keys(u32x4 v, int key0, int limit) {
 // ---------------------------------------------------------------- prefill
 constexpr int KT = 64;          // keys per tile
 constexpr float kLazyLog2 = 8.f;  // headroom of the stale reference maximum (log2 units)
-// LDS tiles are stored unpadded with the 16-byte chunk index of each row
-// XOR-swizzled by the row (keys: 16 chunks per row, values^T: 8), so the
-// MFMA fragment reads (16 rows, one chunk) do not collide in LDS banks.  The
-// key fragment's 16 rows differ in key bits 0, 1, 3 and 4 (the permuted key
-// order below), and the key swizzle takes exactly those bits.  Both choices
-// were checked with the LDS bank-conflict counter on gfx950 (zero conflict
-// cycles; swizzling keys by their low four bits instead cost one conflict
-// cycle per read).
-Q3_DEV int kswz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
+// LDS tiles are stored unpadded.  A key tile is the cache's two 32-key
+// blocks copied as they are (the MFMA operand order of kk_off), so a key
+// fragment read is 1 KiB of consecutive LDS per wavefront.  Value^T tiles
+// have the 16-byte chunk index of each row XOR-swizzled by the row (8 chunks
+// per row), so the fragment reads (16 rows, one chunk) do not collide in LDS
+// banks (checked with the bank-conflict counter on gfx950: zero conflict
+// cycles).
 Q3_DEV int vswz(int dim) { return dim & 7; }
-Q3_DEV int koff(int key, int col) { return key * 128 + ((((col >> 3) ^ kswz(key)) << 3) | (col & 7)); }
 Q3_DEV int voff(int dim, int key) { return dim * KT + ((((key >> 3) ^ vswz(dim)) << 3) | (key & 7)); }
 
 struct TileTable {
@@ -205,14 +204,14 @@ __global__ __launch_bounds__(256 * TPB, 2 / TPB) void flash_prefill_kernel(
   const int ntiles = (kend + KT - 1) / KT;
 
   // Load i of wavefront w fills LDS chunks (NWV*i + w)*64 + lane of a tile:
-  // the K chunk (key, j) holds global chunk j ^ kswz(key) of that key's row;
-  // the V^T chunk (dim, j) holds keys 8 (j ^ vswz(dim)) .. +7 of that dim.
+  // the K chunk p is chunk p of the tile's two cache blocks; the V^T chunk
+  // (dim, j) holds keys 8 (j ^ vswz(dim)) .. +7 of that dim.
   int ksrc[LPW], vsrc[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int p = (NWV * i + wid) * 64 + lane;
-    const int key = p >> 4, dim = p >> 3;
-    ksrc[i] = key * 128 + (((p & 15) ^ kswz(key)) << 3);
+    const int dim = p >> 3;
+    ksrc[i] = p * 8;
     vsrc[i] = (int)vt_off(((p & 7) ^ vswz(dim)) << 3, dim);
   }
   auto issue_k = [&](int t) {
@@ -243,9 +242,8 @@ __global__ __launch_bounds__(256 * TPB, 2 / TPB) void flash_prefill_kernel(
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int sbk = 0; sbk < 2; ++sbk)
-          kf[c][sbk] = *reinterpret_cast<const bf16x8*>(
-              &kb[koff(c * 32 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), ks * 32 + fq * 8)]);
+        for (int sbk = 0; sbk < 2; ++sbk)  // keys c*32 + 8*(fr/4) + 4*sbk + fr%4, dims ks*32 + fq*8 ..
+          kf[c][sbk] = *reinterpret_cast<const bf16x8*>(&kb[((c * 8 + sbk * 4 + ks) * 64 + lane) * 8]);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -483,12 +481,13 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const bf16_t* __restric
     f32x4 sacc[2];
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk) {
+      // keys c0 + 8*(fr/4) + 4*sbk + fr%4 of the 32-key block (the ones at or
+      // past k_end are read but masked below)
       sacc[sbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int key = c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3);
-      key = min(key, k_end - 1);
-      const bf16_t* kp = Kc + (int64_t)key * 128 + fq * 8;
+      const bf16_t* kp = Kc + (int64_t)(c0 >> 5) * 4096 + lane * 8;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(ld16_nt(kp + ks * 32)), qf[ks], sacc[sbk]);
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[sbk] = mfma16(as_bf16x8(ld16_nt(kp + (sbk * 4 + ks) * 512)), qf[ks], sacc[sbk]);
     }
     u32x4 vraw[8];
     const int vkey0 = c0 + fq * 8;
@@ -639,9 +638,10 @@ Q3_DEV void norm_rope_pair(float& a, float& c, const float* w, float eps, float 
 
 
 // One 32-key run of the cache in registers, in the MFMA operand layouts:
-// k[sbk][ks] = K[key(sbk)][ks*32 + fq*8 ..], key(sbk) = c0 + 8*(fr/4) + 4*sbk + fr%4
-// (clamped to the last valid key); v[d] = V^T[d*16 + fr][c0 + fq*8 ..] (the
-// caller zeroes keys at or beyond its end).  c0 is a multiple of 32.
+// k[sbk][ks] = K[key(sbk)][ks*32 + fq*8 ..], key(sbk) = c0 + 8*(fr/4) + 4*sbk + fr%4;
+// v[d] = V^T[d*16 + fr][c0 + fq*8 ..].  Keys at or beyond the caller's end
+// are read too (the caller masks their scores and zeroes their values).  c0
+// is a multiple of 32.
 struct KvRun {
   u32x4 k[2][4];
   u32x4 v[8];
@@ -651,13 +651,10 @@ struct KvRun {
 // arithmetic sat between the loads, the register allocator reused the
 // destination registers of loads still in flight for it, which forced waits
 // for those loads (and for the previous run's) in the middle of the issue.
-Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int end, int fr, int fq) {
-  const bf16_t* kp[2];
-#pragma unroll
-  for (int sbk = 0; sbk < 2; ++sbk) {
-    const int key = min(c0 + 8 * (fr >> 2) + 4 * sbk + (fr & 3), end - 1);
-    kp[sbk] = Kc + (int64_t)key * 128 + fq * 8;
-  }
+Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int lane) {
+  const int fr = lane & 15, fq = lane >> 4;
+  // the block's chunk (sbk * 4 + ks) * 64 + lane (kk_off)
+  const bf16_t* kp = Kc + (int64_t)(c0 >> 5) * 4096 + lane * 8;
   // value dim d * 16 + fr of the run's keys c0 + fq * 8 .. +7: vt_off steps
   // by 16 * 32 elements per d
   const bf16_t* vp = Vt + vt_off(c0 + fq * 8, fr);
@@ -665,7 +662,7 @@ Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int e
 #pragma unroll
   for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16_nt(kp[sbk] + ks * 32);
+    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16_nt(kp + (sbk * 4 + ks) * 512);
 #pragma unroll
   for (int d = 0; d < 8; ++d) r.v[d] = ld16_nt(vp + d * 16 * 32);
 }
@@ -705,7 +702,7 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
   KvRun run[2];
   // start of the wavefront's last 32-key run of cached keys
   const int wlast = w0 + max(0, (cend - 1 - w0) >> 5) * 32;
-  if (w0 < cend) load_run(run[0], Kc, Vt, w0, cend, fr, fq);
+  if (w0 < cend) load_run(run[0], Kc, Vt, w0, lane);
 
   // A: wavefront u handles unit u, u+FW, ...: the group's query heads, then
   // (in the block holding the new position) the new key and value.
@@ -726,8 +723,8 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
       const bf16_t ka = f2bf(a), kc = f2bf(c);
       const bf16_t va = f2bf(row[(n_q + n_kv + g) * 128 + lane]);
       const bf16_t vc = f2bf(row[(n_q + n_kv + g) * 128 + lane + 64]);
-      Kc[(int64_t)pos * 128 + lane] = ka;
-      Kc[(int64_t)pos * 128 + lane + 64] = kc;
+      Kc[kk_off<bf16_t>(pos, lane)] = ka;
+      Kc[kk_off<bf16_t>(pos, lane + 64)] = kc;
       Vt[vt_off(pos, lane)] = va;
       Vt[vt_off(pos, lane + 64)] = vc;
       knew[lane] = ka;
@@ -794,10 +791,10 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
   // just-issued run before using the current one.
   if (w0 < cend) {
     for (int c0 = w0;; c0 += 64) {
-      load_run(run[1], Kc, Vt, min(c0 + 32, wlast), cend, fr, fq);
+      load_run(run[1], Kc, Vt, min(c0 + 32, wlast), lane);
       attend(run[0], c0);
       if (c0 + 32 >= cend) break;
-      load_run(run[0], Kc, Vt, min(c0 + 64, wlast), cend, fr, fq);
+      load_run(run[0], Kc, Vt, min(c0 + 64, wlast), lane);
       attend(run[1], c0 + 32);
       if (c0 + 64 >= cend) break;
     }

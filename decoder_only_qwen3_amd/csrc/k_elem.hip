@@ -284,12 +284,17 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     }
     const float4 x = a[k], y = c[k];
     if (u < n_q + n_kv) {
-      T* dst;
-      if (u < n_q)
-        dst = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
-      else
-        dst = kv_k(kv, s, g, u - n_q) + (int64_t)pos * Q3_HEAD_DIM;
-      qk_norm_rope_store<T>(x, y, u < n_q ? qn : kn, eps, cos_t, sin_t, pos, j, dst);
+      T *lo, *hi;
+      if (u < n_q) {
+        T* row = q_out + ((int64_t)t * n_q + u) * Q3_HEAD_DIM;
+        lo = row + 4 * j;
+        hi = row + 64 + 4 * j;
+      } else {
+        T* kh = kv_k(kv, s, g, u - n_q);
+        lo = kh + kk_off<T>(pos, 4 * j);
+        hi = kh + kk_off<T>(pos, 64 + 4 * j);
+      }
+      qk_norm_rope_store<T>(x, y, u < n_q ? qn : kn, eps, cos_t, sin_t, pos, j, lo, hi);
     } else {
       T* dst = kv_vt(kv, s, g, u - n_q - n_kv);
       const float av[4] = {x.x, x.y, x.z, x.w}, cv[4] = {y.x, y.y, y.z, y.w};

@@ -449,9 +449,17 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
           if (j16 == 0) atomicOr(ra.err, 4u);
           continue;
         }
-        bf16_t* dst = u < ra.n_q ? ra.q_out + ((int64_t)t * ra.n_q + u) * Q3_HEAD_DIM
-                                 : kv_k(ra.kv, sst, geo, u - ra.n_q) + (int64_t)pos * Q3_HEAD_DIM;
-        qk_norm_rope_store<bf16_t>(x, y, u < ra.n_q ? ra.qn : ra.kn, ra.eps, ra.cos_t, ra.sin_t, pos, j16, dst);
+        bf16_t *lo, *hi;
+        if (u < ra.n_q) {
+          bf16_t* row = ra.q_out + ((int64_t)t * ra.n_q + u) * Q3_HEAD_DIM;
+          lo = row + 4 * j16;
+          hi = row + 64 + 4 * j16;
+        } else {
+          bf16_t* kh = kv_k(ra.kv, sst, geo, u - ra.n_q);
+          lo = kh + kk_off<bf16_t>(pos, 4 * j16);
+          hi = kh + kk_off<bf16_t>(pos, 64 + 4 * j16);
+        }
+        qk_norm_rope_store<bf16_t>(x, y, u < ra.n_q ? ra.qn : ra.kn, ra.eps, ra.cos_t, ra.sin_t, pos, j16, lo, hi);
       }
       __syncthreads();  // the staging is rewritten by the next half
     }

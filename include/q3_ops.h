@@ -96,9 +96,14 @@ q3_status q3op_norm_linear(int32_t kernel, int32_t epi, const float* d_x, int32_
 
 /* A one-layer KV arena for the attention ops: sequence b owns the elements
  * [h_base[b], h_base[b] + 2*n_kv*h_cap[b]*128) of d_kv (dtype elements):
- * keys [n_kv][cap][128] then values [n_kv][cap/32][128][32] (32-key blocks,
- * each transposed: value dim d of key t at ((t/32)*128 + d)*32 + t%32); h_cap[b] and
- * h_base[b] are multiples of 64 and d_kv is 16-byte aligned.  h_len[b] = tokens already cached before the call.
+ * keys (cap*128 elements per kv head) then values [n_kv][cap/32][128][32]
+ * (32-key blocks, each transposed: value dim d of key t at
+ * ((t/32)*128 + d)*32 + t%32).  float32 keys are rows [cap][128].  bf16 keys
+ * come in 32-key blocks of 4096 elements in MFMA operand order: with
+ * k = t%32, dim d of key t sits at (t/32)*4096 + (((sbk*4 + d/32)*4 + (d/8)%4)*16
+ * + fr)*8 + d%8, where sbk = (k/4)%2 and fr = (k/8)*4 + k%4.  h_cap[b] and
+ * h_base[b] are multiples of 64 and d_kv is 16-byte aligned.  h_len[b] = tokens
+ * already cached before the call.
  *
  * Pasos 4-5: per-head RMSNorm (q_norm / k_norm) then rotate-half RoPE at each
  * token's position, queries to d_q_out [T][n_q][128], keys and values into the

@@ -41,6 +41,33 @@ def vt_logical(flat: np.ndarray, n_kv: int, cap: int) -> np.ndarray:
     return flat.reshape(n_kv, cap // 32, 128, 32).transpose(0, 2, 1, 3).reshape(n_kv, 128, cap)
 
 
+# ---------------------------------------------------------------- KV cache key layout (bf16)
+def k_perm(cap: int) -> np.ndarray:
+    """Element index of (key, dim) within one head's key region of a bf16
+    cache: blocks of 32 keys, each stored in the order the attention kernels
+    take it as MFMA operands -- 16-byte chunk (sbk*4 + ks)*64 + fq*16 + fr of a
+    block holds dims ks*32 + fq*8 .. +7 of its key 8*(fr//4) + 4*sbk + fr%4."""
+    key = np.arange(cap)[:, None]
+    dim = np.arange(128)[None, :]
+    k = key & 31
+    sbk, fr = (k >> 2) & 1, ((k >> 3) << 2) | (k & 3)
+    ks, fq = dim >> 5, (dim >> 3) & 3
+    return (key >> 5) * 4096 + (((sbk * 4 + ks) * 4 + fq) * 16 + fr) * 8 + (dim & 7)
+
+
+def k_blocks(k: np.ndarray) -> np.ndarray:
+    """Keys as a bf16 cache stores them, from the logical k [n_kv][cap][128]."""
+    n_kv, cap, _ = k.shape
+    out = np.empty((n_kv, cap * 128), k.dtype)
+    out[:, k_perm(cap).reshape(-1)] = k.reshape(n_kv, -1)
+    return out.reshape(-1)
+
+
+def k_logical(flat: np.ndarray, n_kv: int, cap: int) -> np.ndarray:
+    """Inverse of k_blocks: [n_kv][cap][128] copy of a stored key region."""
+    return flat.reshape(n_kv, cap * 128)[:, k_perm(cap).reshape(-1)].reshape(n_kv, cap, 128)
+
+
 # ---------------------------------------------------------------- device marshalling
 def dev_bf16(a: np.ndarray):
     """bf16-valued float32 array -> torch int16 tensor of its bit patterns on cuda:0."""

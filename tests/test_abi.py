@@ -108,3 +108,23 @@ def test_check_tokens_on_the_host():
     assert lib.q3_check_tokens(h, mod.i32_array([-1]), 1) == mod.Q3_E_ARG
     assert lib.q3_check_tokens(h, None, 2) == mod.Q3_E_ARG
     lib.q3_destroy(h)
+
+
+def test_bf16_key_layout_helper():
+    """The tests' model of the bf16 key cache layout (include/q3_ops.h, arena
+    description) is a bijection of each head's cap x 128 elements, and each
+    32-key block holds, as 16-byte chunk (sbk*4 + ks)*64 + fq*16 + fr, dims
+    ks*32 + fq*8 .. +7 of key 8*(fr//4) + 4*sbk + fr%4."""
+    import numpy as np
+    from gpu_helpers import k_blocks, k_logical, k_perm
+    for cap in (64, 192):
+        p = k_perm(cap)
+        assert np.array_equal(np.sort(p.reshape(-1)), np.arange(cap * 128))
+        for key in (0, 5, 31, 32, 63, cap - 1):
+            for dim in (0, 7, 8, 33, 64, 127):
+                t, k = key, key % 32
+                sbk, fr = (k // 4) % 2, (k // 8) * 4 + k % 4
+                want = (t // 32) * 4096 + (((sbk * 4 + dim // 32) * 4 + (dim // 8) % 4) * 16 + fr) * 8 + dim % 8
+                assert p[key, dim] == want
+    K = np.arange(2 * 64 * 128, dtype=np.float32).reshape(2, 64, 128)
+    assert np.array_equal(k_logical(k_blocks(K), 2, 64), K)

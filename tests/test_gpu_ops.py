@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import q3synth
-from gpu_helpers import call, dev_bf16, dev_f32, host_bf16, ops, rand_bf16, vt_blocks, vt_logical
+from gpu_helpers import (call, dev_bf16, dev_f32, host_bf16, k_blocks, k_logical, ops, rand_bf16, vt_blocks,
+                         vt_logical)
 from oracle import attention_rows, rms_norm, rope_cos_sin, rope_rotate, silu, to_bf16
 
 pytestmark = pytest.mark.gpu
@@ -383,7 +384,10 @@ def test_rope_append(dtype, mode):
         np.testing.assert_allclose(q_got[rows], q_ref, **tol)
         cap = caps[b]
         region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
-        K = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        if dtype == BF16:
+            K = k_logical(region[:n_kv * cap * 128], n_kv, cap)
+        else:
+            K = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
         Vt = vt_logical(region[n_kv * cap * 128:], n_kv, cap)
         for i, p in enumerate(pos):
             np.testing.assert_allclose(K[:, p, :], k_ref[i], **tol)
@@ -427,10 +431,11 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0,
         Vs.append(V)
         cap = caps[b]
         region = np.zeros(2 * n_kv * cap * 128, np.float32)
-        Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        Kc = np.zeros((n_kv, cap, 128), np.float32)
         Vt = np.zeros((n_kv, 128, cap), np.float32)
         Kc[:, :ctx[b], :] = K.transpose(1, 0, 2)
         Vt[:, :, :ctx[b]] = V.transpose(1, 2, 0)
+        region[:n_kv * cap * 128] = k_blocks(Kc) if bf else Kc.reshape(-1)
         region[n_kv * cap * 128:] = vt_blocks(Vt)
         arena[bases[b]:bases[b] + region.size] = region
     if bf:
@@ -439,10 +444,11 @@ def _attention_case(kernel, lens, prior, caps, n_q=16, n_kv=8, seed=0, splits=0,
         for b in range(n):
             cap = caps[b]
             reg = bits[bases[b]:bases[b] + 2 * n_kv * cap * 128]
-            Kc = reg[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+            Kc = k_logical(reg[:n_kv * cap * 128], n_kv, cap)
             Vt = vt_logical(reg[n_kv * cap * 128:], n_kv, cap).copy()
             Kc[:, ctx[b]:, :] = 0x7FC0
             Vt[:, :, ctx[b]:] = 0x7FC0
+            reg[:n_kv * cap * 128] = k_blocks(Kc)
             reg[n_kv * cap * 128:] = vt_blocks(Vt)
         dkv = torch.from_numpy(bits.view(np.int16)).to("cuda:0")
         dq = dev_bf16(q)
@@ -647,7 +653,9 @@ def test_decode_attention_fused_rope_append(prior, smax):
         old_v.append(V)
         cap = caps[b]
         region = np.zeros(2 * n_kv * cap * 128, np.float32)
-        region[:n_kv * cap * 128].reshape(n_kv, cap, 128)[:, :prior[b], :] = K.transpose(1, 0, 2)
+        kc = np.zeros((n_kv, cap, 128), np.float32)
+        kc[:, :prior[b], :] = K.transpose(1, 0, 2)
+        region[:n_kv * cap * 128] = k_blocks(kc)
         vt = np.zeros((n_kv, 128, cap), np.float32)
         vt[:, :, :prior[b]] = V.transpose(1, 2, 0)
         region[n_kv * cap * 128:] = vt_blocks(vt)
@@ -674,7 +682,7 @@ def test_decode_attention_fused_rope_append(prior, smax):
         v_new = to_bf16(x[:, n_q + n_kv:])
         cap = caps[b]
         region = kv_got[bases[b]:bases[b] + 2 * n_kv * cap * 128]
-        Kc = region[:n_kv * cap * 128].reshape(n_kv, cap, 128)
+        Kc = k_logical(region[:n_kv * cap * 128], n_kv, cap)
         Vt = vt_logical(region[n_kv * cap * 128:], n_kv, cap)
         np.testing.assert_allclose(Kc[:, prior[b], :], k_new[0], rtol=2 ** -7, atol=1e-6)
         np.testing.assert_array_equal(Vt[:, :, prior[b]], v_new[0].astype(np.float32))
