@@ -258,6 +258,8 @@ CASES = {
     "fused_b64_uniform": lambda lib, r, s: fused_attn_case(lib, "fused_b64_uniform", [4160] * 64, r, s,
                                                            ARGS.attn_smax),
     "fused_b1_640": lambda lib, r, s: fused_attn_case(lib, "fused_b1_640", [640], r, s, ARGS.attn_smax),
+    # one 32K-token sequence (the long-context workload's decode), three cache copies cycled (cold reads)
+    "fused_b1_32k": lambda lib, r, s: fused_attn_case(lib, "fused_b1_32k", [32799], r, s, ARGS.attn_smax, pool=3),
     "fused_b32_2k": lambda lib, r, s: fused_attn_case(lib, "fused_b32_2k", [2112] * 32, r, s, ARGS.attn_smax, pool=3),
     # the headline workload's final decode state: the 64 ragged prompts of
     # the benchmark plus 128 decoded keys each, two arenas cycled (cold reads)
