@@ -647,24 +647,44 @@ struct KvRun {
   u32x4 v[8];
 };
 
-// Every address is formed before the first load is issued: when the address
-// arithmetic sat between the loads, the register allocator reused the
-// destination registers of loads still in flight for it, which forced waits
-// for those loads (and for the previous run's) in the middle of the issue.
-Q3_DEV void load_run(KvRun& r, const bf16_t* Kc, const bf16_t* Vt, int c0, int lane) {
-  const int fr = lane & 15, fq = lane >> 4;
-  // the block's chunk (sbk * 4 + ks) * 64 + lane (kk_off)
-  const bf16_t* kp = Kc + (int64_t)(c0 >> 5) * 4096 + lane * 8;
-  // value dim d * 16 + fr of the run's keys c0 + fq * 8 .. +7: vt_off steps
-  // by 16 * 32 elements per d
-  const bf16_t* vp = Vt + vt_off(c0 + fq * 8, fr);
+// A head's key or value blocks (8 KiB per 32 keys) as a buffer resource
+// whose range ends with the last block a wavefront attends: a run past it
+// loads zeros and moves no bytes, so runs can be requested ahead without a
+// bounds test (which would make the loads conditional).  gfx9 raw buffer:
+// stride 0, the range in bytes, untyped 32-bit data.  Loads are
+// nontemporal (the cache is read once per layer).
+Q3_DEV __amdgpu_buffer_rsrc_t kv_rsrc(const bf16_t* base, int nblocks) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane(nblocks * 8192), 0x00020000);
+}
+Q3_DEV u32x4 ld16_rs(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 2));
+}
+// Byte offsets within a head's blocks of the run at key c0 (a multiple of
+// 32): key chunk (sbk * 4 + ks) * 64 + lane at kro + (sbk * 4 + ks) * 1024
+// (kk_off); value dim d * 16 + fr of keys c0 + fq * 8 .. +7 at
+// vro + d * 1024 (vt_off).
+Q3_DEV int run_koff(int c0, int lane) { return (c0 >> 5) * 8192 + lane * 16; }
+Q3_DEV int run_voff(int c0, int lane) { return ((c0 >> 5) * 128 + (lane & 15)) * 64 + (lane >> 4) * 16; }
+
+// Loads of one half of a run at the given byte offset.  Every address is
+// formed before the first load is issued: when the address arithmetic sat
+// between the loads, the register allocator reused the destination registers
+// of loads still in flight for it, which forced waits for those loads (and
+// for the previous run's) in the middle of the issue.
+Q3_DEV void load_k(KvRun& r, __amdgpu_buffer_rsrc_t krs, int ko) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int sbk = 0; sbk < 2; ++sbk)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16_nt(kp + (sbk * 4 + ks) * 512);
+    for (int ks = 0; ks < 4; ++ks) r.k[sbk][ks] = ld16_rs(krs, ko + (sbk * 4 + ks) * 1024);
+  __builtin_amdgcn_sched_barrier(0);
+}
+Q3_DEV void load_v(KvRun& r, __amdgpu_buffer_rsrc_t vrs, int vo) {
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) r.v[d] = ld16_nt(vp + d * 16 * 32);
+  for (int d = 0; d < 8; ++d) r.v[d] = ld16_rs(vrs, vo + d * 1024);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Sequence of each z-index of the grid: blocks are dispatched in z order.
@@ -682,7 +702,10 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
   __shared__ float wred[FW][8][PSTRIDE];
   __shared__ int last;
   const int j = blockIdx.x, g = blockIdx.y, b = ord.v[blockIdx.z];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, fr = lane & 15, fq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, fr = lane & 15, fq = lane >> 4;
+  // the wavefront index is uniform: held in a scalar register, the key-run
+  // loop below is scalar control flow (no lane masks around its loads)
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = n_q / n_kv;
   const SeqState s = st[sb.slot[b]];
   const int pos = s.len, ctx = pos + 1;
@@ -700,9 +723,19 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
   const int cend = min(w1, pos);
   const bool has_new = pos >= w0 && pos < w1;
   KvRun run[2];
-  // start of the wavefront's last 32-key run of cached keys
-  const int wlast = w0 + max(0, (cend - 1 - w0) >> 5) * 32;
-  if (w0 < cend) load_run(run[0], Kc, Vt, w0, lane);
+  // the blocks up to this wavefront's last cached key
+  const int nblk = (cend + 31) >> 5;
+  const __amdgpu_buffer_rsrc_t krs = kv_rsrc(Kc, nblk), vrs = kv_rsrc(Vt, nblk);
+  // The first two runs go out before the query work, whose loads are all
+  // waited for before the loop (so a condition here costs no later wait).
+  if (w0 < cend) {
+    load_k(run[0], krs, run_koff(w0, lane));
+    load_v(run[0], vrs, run_voff(w0, lane));
+    if (w0 + 32 < cend) {
+      load_k(run[1], krs, run_koff(w0 + 32, lane));
+      load_v(run[1], vrs, run_voff(w0 + 32, lane));
+    }
+  }
 
   // A: wavefront u handles unit u, u+FW, ...: the group's query heads, then
   // (in the block holding the new position) the new key and value.
@@ -747,7 +780,10 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
 #pragma unroll
   for (int d = 0; d < 8; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
-  auto attend = [&](const KvRun& r, int c0) {
+  // Attend to the run in r (keys c0 ..), then refill r with the run at nc0:
+  // its keys as soon as the score products have used r's, its values after
+  // the P.V products.
+  auto attend = [&](KvRun& r, int c0, int kro, int vro) {
     f32x4 sacc[2];
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk) {
@@ -755,6 +791,7 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sacc[sbk] = mfma16(as_bf16x8(r.k[sbk][ks]), qf[ks], sacc[sbk]);
     }
+    load_k(r, krs, kro);
     float mx = -INFINITY;
 #pragma unroll
     for (int sbk = 0; sbk < 2; ++sbk)
@@ -783,20 +820,23 @@ __global__ __launch_bounds__(64 * FW, 8 / FW) void decode_attn_fused_kernel(
       const f16x8 vf = as_f16x8(bf16x8_to_f16x8(mask_keys(r.v[d], vkey0, cend)));
       oacc[d] = mfma16_f16(vf, pf.lo, mfma16_f16(vf, pf.hi, oacc[d] * alpha));
     }
+    load_v(r, vrs, vro);
   };
-  // Two register buffers, used in turn: the next run loads while one is
-  // used.  The next run is loaded on every path (past the end it re-reads the
-  // last run, which is not attended): with a conditional load the compiler
-  // counts outstanding loads by the path without it and waits for the
-  // just-issued run before using the current one.
+  // Two register buffers, used in turn, each refilled with the run two ahead
+  // (past the wavefront's last run: zeros, no bytes moved).  Every path loads
+  // the same runs: with a conditional load the compiler counts outstanding
+  // loads by the path without it and waits for the just-issued run before
+  // using the current one.
   if (w0 < cend) {
+    // byte offsets of the runs two ahead, advanced by two blocks per step
+    int ko0 = run_koff(w0 + 64, lane), vo0 = run_voff(w0 + 64, lane);
     for (int c0 = w0;; c0 += 64) {
-      load_run(run[1], Kc, Vt, min(c0 + 32, wlast), lane);
-      attend(run[0], c0);
+      attend(run[0], c0, ko0, vo0);
       if (c0 + 32 >= cend) break;
-      load_run(run[0], Kc, Vt, min(c0 + 64, wlast), lane);
-      attend(run[1], c0 + 32);
+      attend(run[1], c0 + 32, ko0 + 8192, vo0 + 8192);
       if (c0 + 64 >= cend) break;
+      ko0 += 16384;
+      vo0 += 16384;
     }
   }
   if (has_new) {
