@@ -334,7 +334,7 @@ def run_workload(name, args, steps, warmup, roofline=False, keep_weights=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only (each GPU box has one); --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import q3synth
