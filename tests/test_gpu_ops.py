@@ -633,7 +633,7 @@ def test_rowdot_gemv(M, N, K):
 @pytest.mark.parametrize("prior,smax", [([0], 0), ([5, 700], 0), ([1500], 0), ([1500, 40], 3), ([32799], 0),
                                         ([2047, 0, 4100], 0), ([31, 32, 33, 63, 64, 65, 95, 127], 1),
                                         ([126, 127, 128, 255, 256, 257], 2),
-                                        # 32 ragged sequences: two splits each, launched longest first
+                                        # 32 ragged sequences: several splits each, launched longest first
                                         ([int(x) for x in np.random.default_rng(5).integers(0, 700, 32)], 0)])
 def test_decode_attention_fused_rope_append(prior, smax):
     """QK-Norm + RoPE of the new token, its cache append, and attention over the
@@ -652,13 +652,15 @@ def test_decode_attention_fused_rope_append(prior, smax):
         old_k.append(K)
         old_v.append(V)
         cap = caps[b]
-        region = np.zeros(2 * n_kv * cap * 128, np.float32)
-        kc = np.zeros((n_kv, cap, 128), np.float32)
+        # every slot past the new position holds NaN: the kernel reads whole
+        # 32-key blocks, and what lies past a sequence's end must not leak
+        kc = np.full((n_kv, cap, 128), np.nan, np.float32)
+        kc[:, :prior[b] + 1, :] = 0.0
         kc[:, :prior[b], :] = K.transpose(1, 0, 2)
-        region[:n_kv * cap * 128] = k_blocks(kc)
-        vt = np.zeros((n_kv, 128, cap), np.float32)
+        vt = np.full((n_kv, 128, cap), np.nan, np.float32)
+        vt[:, :, :prior[b] + 1] = 0.0
         vt[:, :, :prior[b]] = V.transpose(1, 2, 0)
-        region[n_kv * cap * 128:] = vt_blocks(vt)
+        region = np.concatenate([k_blocks(kc), vt_blocks(vt)])
         arena[bases[b]:bases[b] + region.size] = region
     qkv = rng.standard_normal((n, units * 128)).astype(np.float32)
     qn = q3synth.round_to_bf16((1 + 0.1 * rng.standard_normal(128)).astype(np.float32))
