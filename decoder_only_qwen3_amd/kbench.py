@@ -211,6 +211,11 @@ CASES = {
     "row_lm_head": lambda lib, r, s: linear_case(lib, "row_lm_head", 3, 1, V, H, r, s, kernel=4, pool=2),
     "sk_qkv": lambda lib, r, s: linear_case(lib, "sk_qkv", 0, 1, Q + 2 * KVW, H, r, s, kernel=1, norm=True, pool=32),
     "sk_gate_up": lambda lib, r, s: linear_case(lib, "sk_gate_up", 2, 1, 2 * I, H, r, s, kernel=1, norm=True, pool=32),
+    # the batched decode projections at 64 rows (weight-streaming kernel, cold weights)
+    "sk64_qkv": lambda lib, r, s: linear_case(lib, "sk64_qkv", 0, 64, Q + 2 * KVW, H, r, s, kernel=1, pool=32),
+    "sk64_o": lambda lib, r, s: linear_case(lib, "sk64_o", 1, 64, H, Q, r, s, kernel=1, pool=32),
+    "sk64_gate_up": lambda lib, r, s: linear_case(lib, "sk64_gate_up", 2, 64, 2 * I, H, r, s, kernel=1, pool=32),
+    "sk64_down": lambda lib, r, s: linear_case(lib, "sk64_down", 1, 64, H, I, r, s, kernel=1, pool=32),
     "rd_o": lambda lib, r, s: linear_case(lib, "rd_o", 1, 1, H, Q, r, s, kernel=3, pool=32),
     "rd_down": lambda lib, r, s: linear_case(lib, "rd_down", 1, 1, H, I, r, s, kernel=3, pool=32),
     "sk_lm_head": lambda lib, r, s: linear_case(lib, "sk_lm_head", 3, 1, V, H, r, s, kernel=1, pool=2),
