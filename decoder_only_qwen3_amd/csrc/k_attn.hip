@@ -578,17 +578,18 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 // Decode attention with the QK-Norm + RoPE + cache append of Pasos 4-5 folded
 // in.  Block (split j, kv head g, sequence b), FW wavefronts:
 //   0. read the sequence's length; every wavefront issues the loads of its
-//      first 32 cached keys and values at once, so the cache stream starts
-//      before any of the steps below;
+//      first two 32-key runs of cached keys and values at once, so the cache
+//      stream starts before any of the steps below;
 //   A. normalise and rotate the group's query heads from the fused projection
 //      row (into LDS, bf16).  The block whose key range holds the new
 //      position also normalises/rotates the new key, stores it and the new
 //      value into the cache for later steps, and keeps both in LDS: this
 //      step takes the new key from LDS, never from the cache, so nothing
 //      waits on those stores;
-//   B. attend over the wavefront's cached keys (MFMA, next 32-key run loaded
-//      while the current one is used), then the wavefront that holds the new
-//      position adds the new key as one more online-softmax term;
+//   B. attend over the wavefront's cached keys (MFMA; two register buffers,
+//      each refilled with the run two ahead as soon as its keys, then its
+//      values, are used), then the wavefront that holds the new position
+//      adds the new key as one more online-softmax term;
 //   C. merge the block's wavefronts in order.  One split: write the output.
 //      Several splits: publish a (max, sum, output) partial with agent-scope
 //      stores, count the finished splits of this (b, g) on an agent-scope
