@@ -417,6 +417,15 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
     const int unit0 = bn0 / Q3_HEAD_DIM;
     const KvGeom geo{ra.n_kv, ra.layer};
     const int j16 = threadIdx.x & 15;
+    // Thread: head hl of the tile's two, tokens tl0 + 32 p (p = 0..3) of each
+    // 128-token half.  The sequence of each token is found by walking the
+    // sequence starts inside the half from the sequence of the tile's first
+    // token; every load of that walk has a wave-uniform address (scalar
+    // loads), so a pass waits on two memory round trips (slot state, then the
+    // rope rows) instead of a per-lane binary search before them.
+    const int hl = (threadIdx.x >> 4) & 1, tl0 = threadIdx.x >> 5;
+    const int u = unit0 + hl;
+    const int b0 = seq_of_token(ra.sb, min(bm0, M - 1));
     for (int half = 0; half < 2; ++half) {
       if ((wm >> 1) == half) {
 #pragma unroll
@@ -429,10 +438,12 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
           }
       }
       __syncthreads();
-      for (int uu = (int)threadIdx.x >> 4; uu < 256; uu += 64 * NW / 16) {
-        const int tl = uu >> 1, hl = uu & 1;
-        const int t = bm0 + half * 128 + tl;
-        const int u = unit0 + hl;
+      const int h0 = bm0 + half * 128;  // the half's first token
+      if (h0 >= M) break;
+      static_assert(64 * NW == 1024, "32 token rows per pass");
+      for (int p = 0; p < 4; ++p) {
+        const int tl = tl0 + 32 * p;
+        const int t = h0 + tl;
         if (t >= M || u >= units) continue;  // uniform over the 16 lanes
         const float4 x = *reinterpret_cast<const float4*>(&stg[tl * SP + hl * Q3_HEAD_DIM + 4 * j16]);
         const float4 y = *reinterpret_cast<const float4*>(&stg[tl * SP + hl * Q3_HEAD_DIM + 64 + 4 * j16]);
@@ -442,9 +453,18 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_dma_kernel(const bf16_t* __
           store4<bf16_t>(dst + 64 + 4 * j16, y.x, y.y, y.z, y.w);
           continue;
         }
-        const int b = seq_of_token(ra.sb, t);
-        const SeqState sst = ra.st[ra.sb.slot[b]];
-        const int pos = ra.sb.prior[b] + t - ra.sb.cu[b];
+        int slot = ra.sb.slot[b0], cub = ra.sb.cu[b0], prb = ra.sb.prior[b0];
+        for (int nb = b0 + 1; nb < ra.sb.n; ++nb) {
+          const int c = ra.sb.cu[nb];
+          if (c > h0 + 127) break;  // starts after the half
+          if (t >= c) {
+            slot = ra.sb.slot[nb];
+            cub = c;
+            prb = ra.sb.prior[nb];
+          }
+        }
+        const SeqState sst = ra.st[slot];
+        const int pos = prb + t - cub;
         if (pos < 0 || pos >= sst.cap) {  // host validation makes this unreachable
           if (j16 == 0) atomicOr(ra.err, 4u);
           continue;
