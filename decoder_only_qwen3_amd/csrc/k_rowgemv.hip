@@ -75,6 +75,16 @@ __global__ __launch_bounds__(256) void rowgemv_kernel(const void* __restrict__ X
 #pragma unroll
     for (int i = 0; i < KS; ++i) xv[i] = ld16(x + koff + 512 * i);
   }
+  // RESADD: lane r < RW fetches the residual of row r now, so that the
+  // read-modify-write at the end costs no extra round trip.
+  float resv = 0.f;
+  if constexpr (EPI == EPI_RESADD) {
+    int rr = N;
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      if (lane == r) rr = rows[r];
+    if (rr < N) resv = reinterpret_cast<const float*>(out)[rr];
+  }
   u32x4 wv[RW][KS];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(256) void rowgemv_kernel(const void* __restrict__ X
     for (int r = 0; r < RW; ++r) {
       if (lane == r && rows[r] < N) {
         if constexpr (EPI == EPI_RESADD)
-          o[rows[r]] += acc[r];
+          o[rows[r]] = resv + acc[r];
         else
           o[rows[r]] = acc[r];
       }
