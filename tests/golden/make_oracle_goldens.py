@@ -9,7 +9,7 @@ their 16-bit patterns, so nothing is lost).  A test rebuilds every logit of
 every step with the oracle's own head.
 
 Only `oracle/` and `q3synth` are called; this runs on the CPU (the 32,768-token
-prompt takes about 1.5 hours on 8 cores).
+prompt took 1.9 hours with 7 BLAS threads).
 
     python tests/golden/make_oracle_goldens.py [workload ...]
 """

@@ -173,7 +173,8 @@ def _whole_run(name):
     _say(f"{name}: worst error {worst:.2e} of the logit RMS; near-ties {ties} of {len(seqs) * (n + 1)} picks")
 
 
-@pytest.mark.parametrize("name", ["q06b_bf16_p512_d256", "q06b_bf16_b32_p2048_d128", "q06b_bf16_b64_ragged_d128"])
+@pytest.mark.parametrize("name", ["q06b_bf16_p512_d256", "q06b_bf16_b32_p2048_d128", "q06b_bf16_b64_ragged_d128",
+                                  "q06b_bf16_p32768_d32"])
 def test_whole_run_matches_oracle(name):
     _whole_run(name)
 
